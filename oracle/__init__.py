@@ -1,0 +1,246 @@
+"""CPU oracle for the FP8/BF16-weight GEMM path (ctypes binding of oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The HIP library never
+loads it, and it never loads the HIP library; the two share only the seeded
+input generators in ``synthetic``.
+
+Each wrapper takes and returns numpy arrays.  The arithmetic lives in
+``oracle.c`` (scalar, fp64 where the pages leave precision open); see that
+file's header for the passages each function follows.
+
+Parity status: every function here is pinned by a ``-m "not gpu"`` test that
+does not re-type its formula (torch float8 decoders, brute-force nearest
+search, numpy matmul, the CDNA3 packing expression printed on the pages,
+closed forms and invariants), except the end-to-end chain, whose composed
+output beyond the per-stage pins is "parity unpinned" (the pages print no
+worked chain value); its per-stage pins are one-hot and zero-weight cases.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+OCP = 1
+FNUZ = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+          "-std=c11", "-D_GNU_SOURCE", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc into liboracle.so next to it."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I64 = ctypes.c_int64
+            INT = ctypes.c_int
+            sig = {
+                "orc_fp8_decode": (ctypes.c_double, [ctypes.c_uint8, INT]),
+                "orc_fp8_decode_table": (None, [INT, P]),
+                "orc_fp8_encode": (ctypes.c_uint8, [ctypes.c_float, INT]),
+                "orc_fp8_encode_array": (None, [P, I64, INT, P]),
+                "orc_bf16_round_array": (None, [P, I64, P]),
+                "orc_bf16_round_f32_array": (None, [P, I64, P]),
+                "orc_bf16_to_f64": (None, [P, I64, P]),
+                "orc_quantize_rows": (None, [P, I64, I64, INT, P, P]),
+                "orc_quantize_act": (None, [P, I64, I64, P, P]),
+                "orc_reencode_fnuz_to_ocp": (None, [P, P, I64, I64, P, P]),
+                "orc_pack": (None, [P, P, I64, I64, INT, INT]),
+                "orc_unpack": (None, [P, P, I64, I64, INT, INT]),
+                "orc_dequant_rows": (None, [P, P, I64, I64, INT, P]),
+                "orc_gemm": (None, [P, P, P, I64, I64, I64, P, P]),
+                "orc_gelu_tanh": (ctypes.c_double, [ctypes.c_double]),
+                "orc_gelu_mul": (None, [P, P, I64, P]),
+                "orc_mlp_chain": (None, [P, P, P, P, P, INT, I64, I64, I64, P, P, P, P]),
+            }
+            for name, (res, args) in sig.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------- codec
+
+def decode_table(dialect: int) -> np.ndarray:
+    """The 256 decoded values of a dialect, fp64 (NaN where the code is NaN)."""
+    out = np.empty(256, np.float64)
+    _load().orc_fp8_decode_table(dialect, _p(out))
+    return out
+
+
+def decode(codes, dialect: int) -> np.ndarray:
+    return decode_table(dialect)[np.asarray(codes, np.uint8)]
+
+
+def encode(x, dialect: int) -> np.ndarray:
+    """fp32 -> E4M3 codes, nearest-even with saturation."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_fp8_encode_array(_p(x), x.size, dialect, _p(out))
+    return out
+
+
+def bf16_round(x) -> np.ndarray:
+    """fp64 values -> bf16 bit patterns (uint16), nearest-even."""
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint16)
+    _load().orc_bf16_round_array(_p(x), x.size, _p(out))
+    return out
+
+
+def bf16_value(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float64)
+    _load().orc_bf16_to_f64(_p(h), h.size, _p(out))
+    return out
+
+
+# ------------------------------------------------------------ quantizers
+
+def quantize_rows(W, dialect: int):
+    """Per-output-channel quantization of fp32 W (N x K). Returns (q, s)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.uint8)
+    s = np.empty(N, np.float32)
+    _load().orc_quantize_rows(_p(W), N, K, dialect, _p(q), _p(s))
+    return q, s
+
+
+def quantize_act(A_bits):
+    """Per-tensor OCP quantization of bf16 A (uint16 bits, M x K). Returns (qa, s_a)."""
+    A = _c(A_bits, np.uint16)
+    M, K = A.shape
+    qa = np.empty((M, K), np.uint8)
+    s = np.empty(1, np.float32)
+    _load().orc_quantize_act(_p(A), M, K, _p(qa), _p(s))
+    return qa, np.float32(s[0])
+
+
+def reencode_fnuz_to_ocp(q, s):
+    """Row-major FNUZ codes + scales -> OCP codes + scales (per-row j rule)."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    N, K = q.shape
+    q2 = np.empty_like(q)
+    s2 = np.empty_like(s)
+    _load().orc_reencode_fnuz_to_ocp(_p(q), _p(s), N, K, _p(q2), _p(s2))
+    return q2, s2
+
+
+# ---------------------------------------------------------------- packer
+
+def pack(W, KL: int = 8) -> np.ndarray:
+    """MFMA lane packing of an N x K matrix (any 1/2/4/8-byte dtype) -> flat array."""
+    W = np.ascontiguousarray(W)
+    N, K = W.shape
+    out = np.empty(N * K, W.dtype)
+    _load().orc_pack(_p(W), _p(out), N, K, KL, W.itemsize)
+    return out
+
+
+def unpack(flat, N: int, K: int, KL: int = 8) -> np.ndarray:
+    flat = np.ascontiguousarray(flat)
+    out = np.empty((N, K), flat.dtype)
+    _load().orc_unpack(_p(flat), _p(out), N, K, KL, flat.itemsize)
+    return out
+
+
+# ------------------------------------------------------ dequant and GEMM
+
+def dequant_rows(q, s, dialect: int = OCP) -> np.ndarray:
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    N, K = q.shape
+    w = np.empty((N, K), np.float64)
+    _load().orc_dequant_rows(_p(q), _p(s), N, K, dialect, _p(w))
+    return w
+
+
+def gemm(a, w, bias=None):
+    """fp64 y = a @ w.T (+ bias) and yabs = |a| @ |w|.T (+ |bias|)."""
+    a = _c(a, np.float64)
+    w = _c(w, np.float64)
+    M, K = a.shape
+    N, K2 = w.shape
+    assert K == K2
+    b = None if bias is None else _c(bias, np.float64)
+    y = np.empty((M, N), np.float64)
+    yabs = np.empty((M, N), np.float64)
+    _load().orc_gemm(_p(a), _p(w), _p(b), M, N, K, _p(y), _p(yabs))
+    return y, yabs
+
+
+def gelu_tanh(g: float) -> float:
+    return _load().orc_gelu_tanh(float(g))
+
+
+def gelu_mul(g_bits, u_bits) -> np.ndarray:
+    g = _c(g_bits, np.uint16)
+    u = _c(u_bits, np.uint16)
+    assert g.shape == u.shape
+    out = np.empty(g.shape, np.uint16)
+    _load().orc_gelu_mul(_p(g), _p(u), g.size, _p(out))
+    return out
+
+
+def mlp_chain(x_in_bits, wgu, sgu, wd, sd, stages: bool = False):
+    """Gated-MLP chain on row-major OCP codes.  wgu[l]: 2I x H, wd[l]: H x I.
+
+    Returns x_out bits (M x H), or (x_out, gu, act, x_layers) with stages=True.
+    """
+    x = _c(x_in_bits, np.uint16)
+    M, H = x.shape
+    L = len(wgu)
+    I = wgu[0].shape[0] // 2
+    keep = [_c(w, np.uint8) for w in wgu] + [_c(w, np.uint8) for w in wd]
+    keep_s = [_c(v, np.float32) for v in sgu] + [_c(v, np.float32) for v in sd]
+    for w in keep[:L]:
+        assert w.shape == (2 * I, H)
+    for w in keep[L:]:
+        assert w.shape == (H, I)
+    arr = lambda xs: (ctypes.c_void_p * len(xs))(*[x.ctypes.data for x in xs])
+    pgu, pd = arr(keep[:L]), arr(keep[L:])
+    psg, psd = arr(keep_s[:L]), arr(keep_s[L:])
+    out = np.empty((M, H), np.uint16)
+    gu = act = xl = None
+    if stages:
+        gu = np.empty((L, M, 2 * I), np.uint16)
+        act = np.empty((L, M, I), np.uint16)
+        xl = np.empty((L, M, H), np.uint16)
+    _load().orc_mlp_chain(_p(x), pgu, psg, pd, psd, L, M, H, I, _p(out), _p(gu), _p(act),
+                          _p(xl))
+    return (out, gu, act, xl) if stages else out

@@ -1,0 +1,369 @@
+/*
+ * CPU oracle for the FP8/BF16-weight GEMM path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or constant
+ * generator with the HIP library; the two meet only through seeded inputs.
+ *
+ * Everything here is scalar, obviously-correct, and computed in fp64 where
+ * the pages leave the precision open.  Build flags: -O2 -ffp-contract=off,
+ * never -ffast-math, so every float operation written below is one IEEE
+ * operation in the type it is written in.
+ *
+ * Sources (the pages these functions follow):
+ *  [P1] "Real-time VLA inference on AMD hardware" (cyberneticphysics.com):
+ *       intro (FNUZ decodes the same byte to half the value; CDNA4 MFMA
+ *       16x16x32 takes 8 BF16 per lane), section "Different FP8
+ *       representation", section "Packing around the instruction" (the
+ *       view/permute packing expression and its axis labels), section
+ *       "Merging gate and up", section "Fusing the BF16 decoder boundary".
+ *  [P3] "Deploying DeepSeek-V4-Flash on AMD MI300X" (lehuy.net), section
+ *       "The FP8 dialect problem": the dialects share the bit layout, the
+ *       exponent bias differs by one, FNUZ = finite, NaN, unsigned zero
+ *       (no -0, no inf).
+ *  Format limits the pages leave open (OCP: bias 7, max 448, NaN S.1111.111;
+ *  FNUZ: bias 8, max 240, NaN 0x80) are the ones the project statement
+ *  fixes; the subnormal exponent 1-bias is the reading under which the
+ *  halving identity of [P1]/[P3] holds for every non-special code.
+ *
+ * Every function has a pin in tests/test_oracle_*.py that does not re-type
+ * its formula: torch's float8 decoders, brute-force nearest search, numpy
+ * matmul, the page's packing expression, closed forms and invariants.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+
+#define ORC_OCP 1
+#define ORC_FNUZ 2
+
+/* ---------------------------------------------------------------- formats */
+
+static int fmt_bias(int dialect) { return dialect == ORC_OCP ? 7 : 8; }
+static double fmt_max(int dialect) { return dialect == ORC_OCP ? 448.0 : 240.0; }
+
+/* Decode one E4M3 byte (plain definition; [P1] intro, [P3] FP8 dialect).
+ * Bits s eeee mmm.  e == 0 is subnormal with exponent 1 - bias. */
+double orc_fp8_decode(uint8_t b, int dialect)
+{
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    int bias = fmt_bias(dialect);
+    if (dialect == ORC_OCP && e == 15 && m == 7) return NAN;   /* 0x7F, 0xFF */
+    if (dialect == ORC_FNUZ && b == 0x80) return NAN;          /* the one NaN */
+    double v = (e == 0) ? ldexp(m / 8.0, 1 - bias) : ldexp(1.0 + m / 8.0, e - bias);
+    return s ? -v : v;   /* OCP 0x80 is -0.0; FNUZ has no -0 (0x80 is NaN) */
+}
+
+void orc_fp8_decode_table(int dialect, double *out256)
+{
+    for (int b = 0; b < 256; ++b) out256[b] = orc_fp8_decode((uint8_t)b, dialect);
+}
+
+/* Round a >= 0 to the nearest value of a binary format with `mbits` fraction
+ * bits and smallest normal exponent `emin` (below it, subnormals share the
+ * quantum 2^(emin - mbits)).  Ties go to an even number of quanta, which is
+ * the even code (mantissa LSB 0).  a / q and n * q are exact (power-of-two
+ * scalings of doubles that stay in range); nearbyint rounds ties to even in
+ * the default rounding mode. */
+static double round_nearest_even(double a, int mbits, int emin)
+{
+    if (a == 0.0) return 0.0;
+    int e2;
+    frexp(a, &e2);            /* a = f * 2^e2, f in [0.5, 1) */
+    int ex = e2 - 1;          /* floor(log2(a)) */
+    if (ex < emin) ex = emin;
+    double q = ldexp(1.0, ex - mbits);
+    return nearbyint(a / q) * q;
+}
+
+/* Encode fp32 -> E4M3 with round-to-nearest-even and saturation.
+ * NaN -> OCP 0x7F|sign, FNUZ 0x80.  |x| >= max (incl. inf) -> +-max code.
+ * Zero: OCP keeps the sign (-0 and negative underflow give 0x80); FNUZ has
+ * only +0 (0x00). */
+uint8_t orc_fp8_encode(float x, int dialect)
+{
+    int ocp = dialect == ORC_OCP;
+    int bias = fmt_bias(dialect);
+    int sgn = signbit(x) ? 1 : 0;
+    if (isnan(x)) return ocp ? (uint8_t)(0x7F | (sgn << 7)) : 0x80;
+    double a = fabs((double)x);
+    uint8_t maxcode = ocp ? 0x7E : 0x7F;
+    if (a >= fmt_max(dialect)) return (uint8_t)(maxcode | (sgn << 7));
+    double r = round_nearest_even(a, 3, 1 - bias);
+    if (r == 0.0) return ocp ? (uint8_t)(sgn << 7) : 0x00;
+    int e, m;
+    int e2;
+    frexp(r, &e2);
+    int ex = e2 - 1;
+    if (ex < 1 - bias) {                  /* subnormal */
+        e = 0;
+        m = (int)(r / ldexp(1.0, 1 - bias - 3));
+    } else {
+        e = ex + bias;
+        m = (int)(ldexp(r, -ex) * 8.0) - 8;
+    }
+    return (uint8_t)((sgn << 7) | (e << 3) | m);
+}
+
+void orc_fp8_encode_array(const float *x, int64_t n, int dialect, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8_encode(x[i], dialect);
+}
+
+/* ------------------------------------------------------------------ bf16 */
+
+double orc_bf16_value(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round a double to bf16 (8 significant bits, fp32 exponent range), nearest
+ * even; overflow past the largest finite value's rounding boundary -> inf. */
+uint16_t orc_bf16_round(double x)
+{
+    if (isnan(x)) return 0x7FC0;
+    int sgn = signbit(x) ? 1 : 0;
+    double a = fabs(x);
+    double r = round_nearest_even(a, 7, -126);
+    uint16_t mag;
+    if (r == 0.0) {
+        mag = 0;
+    } else if (r >= ldexp(1.0, 128)) {
+        mag = 0x7F80;
+    } else {
+        float f = (float)r;    /* r has <= 8 significant bits: exact */
+        uint32_t u;
+        memcpy(&u, &f, 4);
+        mag = (uint16_t)((u >> 16) & 0x7FFF);
+    }
+    return (uint16_t)(mag | (sgn << 15));
+}
+
+void orc_bf16_round_array(const double *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(x[i]);
+}
+
+void orc_bf16_round_f32_array(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round((double)x[i]);
+}
+
+/* ------------------------------------------------------- weight quantizer */
+
+/* Per-output-channel quantization of W (N x K row-major fp32):
+ *   s[n] = fp32(absmax_k |W[n,k]| / max)   (one IEEE fp32 division)
+ *   q[n,k] = enc(fp32(W[n,k] / s[n]))      (division, not reciprocal-multiply)
+ * An all-zero row gets s = 1.  [P1] "Packing around the instruction": the
+ * weights are quantized and packed once at load time. */
+void orc_quantize_rows(const float *W, int64_t N, int64_t K, int dialect,
+                       uint8_t *q, float *s)
+{
+    const float maxv = (float)fmt_max(dialect);
+    for (int64_t n = 0; n < N; ++n) {
+        const float *row = W + n * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(row[k]);
+            if (a > amax) amax = a;
+        }
+        float sc = (amax == 0.0f) ? 1.0f : amax / maxv;
+        s[n] = sc;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = row[k] / sc;
+            q[n * K + k] = orc_fp8_encode(v, dialect);
+        }
+    }
+}
+
+/* Per-tensor activation quantization to OCP E4M3 (bf16 A, M x K):
+ *   s_a = fp32(absmax |A| / 448); qa = enc_ocp(fp32(A / s_a)). */
+void orc_quantize_act(const uint16_t *A, int64_t M, int64_t K, uint8_t *qa, float *s_a)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < M * K; ++i) {
+        float a = fabsf((float)orc_bf16_value(A[i]));
+        if (a > amax) amax = a;
+    }
+    float sc = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    *s_a = sc;
+    for (int64_t i = 0; i < M * K; ++i) {
+        float v = (float)orc_bf16_value(A[i]) / sc;
+        qa[i] = orc_fp8_encode(v, ORC_OCP);
+    }
+}
+
+/* ------------------------------------------------------------ re-encoder */
+
+/* FNUZ -> OCP re-encode of a row-major N x K code matrix with scales.
+ * [P1] intro and [P3] FP8 dialect: the same byte reads as exactly half the
+ * OCP value under FNUZ.  Per row n: j = 1 when the row holds no FNUZ +-240
+ * code (0x7F / 0xFF), else 0; new byte = enc_ocp(2^j * dec_fnuz(b)), the
+ * FNUZ NaN becomes OCP NaN 0x7F; new scale = s * 2^-j (exact).  With j = 1
+ * this is the pages' "same byte, half the scale" identity; j = 0 keeps
+ * +-240 representable. */
+void orc_reencode_fnuz_to_ocp(const uint8_t *q, const float *s, int64_t N, int64_t K,
+                              uint8_t *q2, float *s2)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *row = q + n * K;
+        int j = 1;
+        for (int64_t k = 0; k < K; ++k)
+            if (row[k] == 0x7F || row[k] == 0xFF) { j = 0; break; }
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t b = row[k];
+            if (b == 0x80) { q2[n * K + k] = 0x7F; continue; }
+            double v = ldexp(orc_fp8_decode(b, ORC_FNUZ), j);
+            q2[n * K + k] = orc_fp8_encode((float)v, ORC_OCP);   /* v exact in fp32 */
+        }
+        s2[n] = ldexpf(s[n], -j);
+    }
+}
+
+/* ----------------------------------------------------------------- packer */
+
+/* MFMA lane packing of an N x K row-major matrix of `esize`-byte elements.
+ * KL = values per lane (4 on CDNA3's 16x16x16, 8 on CDNA4's 16x16x32;
+ * [P1] intro), KS = 4 * KL = K per MFMA step.  Element (n, k) with
+ * n = 16 n0 + n1, k = KS k0 + KL k1 + k2 goes to
+ *   ((n0 * (K / KS) + k0) * 64 + 16 k1 + n1) * KL + k2,
+ * i.e. axes [output tile][MFMA K step][lane = 16 k1 + n1][KL contiguous
+ * values], the axis order of [P1] "Packing around the instruction". */
+void orc_pack(const void *src, void *dst, int64_t N, int64_t K, int KL, int esize)
+{
+    const int KS = 4 * KL;
+    const uint8_t *s = (const uint8_t *)src;
+    uint8_t *d = (uint8_t *)dst;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t n0 = n / 16, n1 = n % 16, k0 = k / KS, r = k % KS, k1 = r / KL, k2 = r % KL;
+            int64_t off = ((n0 * (K / KS) + k0) * 64 + 16 * k1 + n1) * KL + k2;
+            memcpy(d + off * esize, s + (n * K + k) * esize, (size_t)esize);
+        }
+}
+
+void orc_unpack(const void *src, void *dst, int64_t N, int64_t K, int KL, int esize)
+{
+    const int KS = 4 * KL;
+    const uint8_t *s = (const uint8_t *)src;
+    uint8_t *d = (uint8_t *)dst;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t n0 = n / 16, n1 = n % 16, k0 = k / KS, r = k % KS, k1 = r / KL, k2 = r % KL;
+            int64_t off = ((n0 * (K / KS) + k0) * 64 + 16 * k1 + n1) * KL + k2;
+            memcpy(d + (n * K + k) * esize, s + off * esize, (size_t)esize);
+        }
+}
+
+/* ------------------------------------------------------- dequantization */
+
+/* w[n,k] = dec(q[n,k]) * s[n] in fp64 (exact: 4 x 24 significant bits). */
+void orc_dequant_rows(const uint8_t *q, const float *s, int64_t N, int64_t K, int dialect,
+                      double *w)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            w[n * K + k] = orc_fp8_decode(q[n * K + k], dialect) * (double)s[n];
+}
+
+void orc_bf16_to_f64(const uint16_t *h, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_value(h[i]);
+}
+
+/* ------------------------------------------------------------------ GEMM */
+
+/* y[m,n] = sum_k a[m,k] * w[n,k] (+ bias[n]), fp64, ascending k, one
+ * accumulator per output.  yabs[m,n] = sum_k |a[m,k] * w[n,k]| (+ |bias[n]|),
+ * the scale of the tolerance bound.  w is N x K (one row per output
+ * channel).  Either bias or yabs may be NULL. */
+void orc_gemm(const double *a, const double *w, const double *bias, int64_t M, int64_t N,
+              int64_t K, double *y, double *yabs)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            const double *ar = a + m * K, *wr = w + n * K;
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = ar[k] * wr[k];
+                acc += p;
+                aacc += fabs(p);
+            }
+            if (bias) {
+                acc += bias[n];
+                aacc += fabs(bias[n]);
+            }
+            y[m * N + n] = acc;
+            if (yabs) yabs[m * N + n] = aacc;
+        }
+}
+
+/* ------------------------------------------------------ gated-MLP chain */
+
+/* GELU, tanh form: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))). */
+double orc_gelu_tanh(double g)
+{
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * g * (1.0 + tanh(c * (g + 0.044715 * g * g * g)));
+}
+
+/* act = bf16(gelu_tanh(g) * u) for bf16 inputs g, u. */
+void orc_gelu_mul(const uint16_t *g, const uint16_t *u, int64_t n, uint16_t *act)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double gv = orc_bf16_value(g[i]), uv = orc_bf16_value(u[i]);
+        act[i] = orc_bf16_round(orc_gelu_tanh(gv) * uv);
+    }
+}
+
+/* One gated-MLP layer, then the next, L times ([P1] "Merging gate and up",
+ * "Fusing the BF16 decoder boundary"), starting from x = x_in (M x H bf16):
+ *   g, u = bf16(x @ Wgate^T), bf16(x @ Wup^T)     (merged [Wgate; Wup])
+ *   act  = bf16(gelu_tanh(g) * u)
+ *   x    = bf16(x + bf16(act @ Wdown^T))
+ * Weights are row-major OCP codes with per-row scales: wgu[l] is 2I x H
+ * (rows 0..I-1 gate, I..2I-1 up), wd[l] is H x I.  Optional stage outputs
+ * (per layer, may be NULL): gu_out L x M x 2I bf16, act_out L x M x I bf16,
+ * x_layers L x M x H bf16. */
+void orc_mlp_chain(const uint16_t *x_in, const uint8_t *const *wgu, const float *const *sgu,
+                   const uint8_t *const *wd, const float *const *sd, int L, int64_t M,
+                   int64_t H, int64_t I, uint16_t *x_out, uint16_t *gu_out, uint16_t *act_out,
+                   uint16_t *x_layers)
+{
+    double *x = malloc(sizeof(double) * M * H);
+    double *wg = malloc(sizeof(double) * 2 * I * H);
+    double *wdn = malloc(sizeof(double) * H * I);
+    double *gu = malloc(sizeof(double) * M * 2 * I);
+    double *act = malloc(sizeof(double) * M * I);
+    double *dn = malloc(sizeof(double) * M * H);
+    uint16_t *gb = malloc(sizeof(uint16_t) * M * 2 * I);
+    uint16_t *ab = malloc(sizeof(uint16_t) * M * I);
+    uint16_t *xb = malloc(sizeof(uint16_t) * M * H);
+    memcpy(xb, x_in, sizeof(uint16_t) * M * H);
+    for (int l = 0; l < L; ++l) {
+        orc_bf16_to_f64(xb, M * H, x);
+        orc_dequant_rows(wgu[l], sgu[l], 2 * I, H, ORC_OCP, wg);
+        orc_dequant_rows(wd[l], sd[l], H, I, ORC_OCP, wdn);
+        orc_gemm(x, wg, NULL, M, 2 * I, H, gu, NULL);
+        orc_bf16_round_array(gu, M * 2 * I, gb);
+        for (int64_t m = 0; m < M; ++m)
+            orc_gelu_mul(gb + m * 2 * I, gb + m * 2 * I + I, I, ab + m * I);
+        orc_bf16_to_f64(ab, M * I, act);
+        orc_gemm(act, wdn, NULL, M, H, I, dn, NULL);
+        for (int64_t i = 0; i < M * H; ++i) {
+            double d = orc_bf16_value(orc_bf16_round(dn[i]));
+            xb[i] = orc_bf16_round(orc_bf16_value(xb[i]) + d);
+        }
+        if (gu_out) memcpy(gu_out + (int64_t)l * M * 2 * I, gb, sizeof(uint16_t) * M * 2 * I);
+        if (act_out) memcpy(act_out + (int64_t)l * M * I, ab, sizeof(uint16_t) * M * I);
+        if (x_layers) memcpy(x_layers + (int64_t)l * M * H, xb, sizeof(uint16_t) * M * H);
+    }
+    memcpy(x_out, xb, sizeof(uint16_t) * M * H);
+    free(x); free(wg); free(wdn); free(gu); free(act); free(dn); free(gb); free(ab); free(xb);
+}
