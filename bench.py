@@ -1,0 +1,342 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8-weight GEMM path on one MI355X.
+
+Headline workload: the action-decoder GEMM pair at M = 50 rows with OCP
+E4M3 per-channel-scaled weights, up-projection 1024 -> 4096 and
+down-projection 4096 -> 1024 (bf16 activations ~N(0,1), weights ~N(0,0.02),
+seeded; synthetic stand-ins for the camera observations and checkpoints the
+pages measure on).  One step = one up call + one down call.  Inputs are
+resident in HBM before timing starts.
+
+Cache regime: "cold" (default) rotates every step through distinct copies of
+the packed weights totalling >= 1 GiB, so weights stream from HBM rather than
+the 256 MB Infinity Cache; "warm" reuses one copy.
+
+Timing: W untimed warmup steps, then K steps recorded once into a HIP graph
+(the way the pages run inference) and replayed between HIP events on the
+launch stream, with torch.cuda.synchronize() on both sides.  value = mean
+microseconds per GEMM call (lower is better).
+
+Prints one JSON line.  --gpus above 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, published
+FP8_PEAK_TFLOPS = 5000.0
+
+M, H, I = 50, 1024, 4096
+UP = (M, I, H)                 # (M, N, K): 50 x 1024 -> 4096
+DOWN = (M, H, I)               # 50 x 4096 -> 1024
+
+
+def alg_bytes_fp8w(m, n, k):
+    """Algorithmic HBM bytes of one FP8-weight GEMM call: W + scales + A + Y."""
+    return n * k + 4 * n + 2 * m * k + 2 * m * n
+
+
+def alg_bytes_bf16w(m, n, k):
+    return 2 * n * k + 2 * m * k + 2 * m * n
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cache", choices=["cold", "warm"], default="cold")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the GEMMs shard by output columns with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bf16_gemm_vla_amd as vla
+    import synthetic
+
+    vla.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    def up_bits(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a.copy()).to(dev)
+
+    def quantize(W, wfmt=vla.VLA_WFMT_E4M3_OCP):
+        N, K = W.shape
+        q = torch.empty(vla.vla_packed_bytes(N, K, wfmt), dtype=torch.uint8, device=dev)
+        s = torch.empty(N, dtype=torch.float32, device=dev) if wfmt != vla.VLA_WFMT_BF16 else None
+        vla.vla_quantize_pack(up_bits(W), q, s, N, K, wfmt, vla.VLA_LAYOUT_MFMA)
+        return q, s
+
+    # ---------------------------------------------------------- headline
+    log("building skinny workload")
+    A_up = up_bits(synthetic.activations(M, H, synthetic.IDS["skinny.up.A"]))
+    A_dn = up_bits(synthetic.activations(M, I, synthetic.IDS["skinny.down.A"]))
+    W_up = synthetic.weights(I, H, synthetic.IDS["skinny.up.W"])
+    W_dn = synthetic.weights(H, I, synthetic.IDS["skinny.down.W"])
+    q_up, s_up = quantize(W_up)
+    q_dn, s_dn = quantize(W_dn)
+    copies = 1
+    if args.cache == "cold":
+        copies = max(1, (1 << 30) // (q_up.numel() + q_dn.numel()))
+    qs_up = [q_up] + [q_up.clone() for _ in range(copies - 1)]
+    qs_dn = [q_dn] + [q_dn.clone() for _ in range(copies - 1)]
+    Y_up = torch.empty(M * I, dtype=torch.int16, device=dev)
+    Y_dn = torch.empty(M * H, dtype=torch.int16, device=dev)
+    ws_bytes = max(vla.vla_gemm_workspace_bytes(*UP, 1), vla.vla_gemm_workspace_bytes(*DOWN, 1))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        c = i % copies
+        vla.vla_gemm_fp8w(A_up, None, qs_up[c], s_up, None, None, Y_up, ws, ws_bytes, *UP)
+        vla.vla_gemm_fp8w(A_dn, None, qs_dn[c], s_dn, None, None, Y_dn, ws, ws_bytes, *DOWN)
+
+    def time_graph(fn, n, reps=1):
+        """Record fn(0..n-1) into one graph; replay `reps` times; ms per replay."""
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                fn(i)
+        g.replay()                      # one untimed replay
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def time_eager(fn, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    log(f"warmup {args.warmup} steps ({copies} weight copies)")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ms_graph = time_graph(step, args.steps)
+    ms_eager = time_eager(step, args.steps)
+    us_call = ms_graph * 1000.0 / (2 * args.steps)
+    bytes_step = alg_bytes_fp8w(*UP) + alg_bytes_fp8w(*DOWN)
+    achieved = bytes_step / (ms_graph * 1e-3 / args.steps) / 1e9
+    extra = {
+        "us_per_call_eager": round(ms_eager * 1000.0 / (2 * args.steps), 3),
+        "weight_copies": copies,
+    }
+
+    # per-shape split (same protocol)
+    for name, shp, qs, A, s, Y in (("up", UP, qs_up, A_up, s_up, Y_up), ("down", DOWN, qs_dn, A_dn, s_dn, Y_dn)):
+        def one(i, shp=shp, qs=qs, A=A, s=s, Y=Y):
+            vla.vla_gemm_fp8w(A, None, qs[i % copies], s, None, None, Y, ws, ws_bytes, *shp)
+        ms = time_graph(one, args.steps)
+        extra[f"{name}_us"] = round(ms * 1000.0 / args.steps, 3)
+        extra[f"{name}_GBps"] = round(alg_bytes_fp8w(*shp) / (ms * 1e-3 / args.steps) / 1e9, 1)
+
+    if not args.no_extra:
+        extra.update(secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, args))
+
+    result = {
+        "metric": "µs/call + achieved HBM GB/s (M≤64) / MFMA TFLOP/s (M≥512), FP8-weight GEMM",
+        "value": round(us_call, 3),
+        "unit": "µs/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_graph / args.steps, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 activations, N(0,0.02) fp32 weights -> OCP E4M3 per-channel)",
+        "config": {
+            "workload": "action-decoder skinny FP8-weight GEMM pair, M=50: up 1024->4096 + down 4096->1024",
+            "M": M, "hidden": H, "intermediate": I, "weights": "OCP E4M3, per-output-channel fp32 scale",
+            "cache": args.cache, "timing": "HIP graph of K steps replayed between HIP events",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, synthetic, W_up, W_dn)
+    print(json.dumps(result), flush=True)
+
+
+def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, args):
+    """Encoder-size GEMMs, the 18-layer chain, the BF16-weight skinny GEMMs
+    and the dialect conversion, each timed the same way (graph + events)."""
+    out = {}
+    log("secondary: bf16-weight skinny")
+    for name, (m, n, k) in (("bf16_up", UP), ("bf16_down", DOWN)):
+        A = up_bits(synthetic.activations(m, k, 900 + n))
+        q, _ = quantize(synthetic.weights(n, k, 901 + n), vla.VLA_WFMT_BF16)
+        copies = max(1, (1 << 30) // q.numel()) if args.cache == "cold" else 1
+        qs = [q] + [q.clone() for _ in range(copies - 1)]
+        Y = torch.empty(m * n, dtype=torch.int16, device=dev)
+        wsb = vla.vla_gemm_workspace_bytes(m, n, k, 0)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+
+        def one(i, A=A, qs=qs, Y=Y, ws=ws, wsb=wsb, m=m, n=n, k=k, copies=copies):
+            vla.vla_gemm_bf16(A, qs[i % copies], None, None, Y, ws, wsb, m, n, k)
+        ms = time_graph(one, 128)
+        us = ms * 1000.0 / 128
+        out[f"{name}_us"] = round(us, 3)
+        out[f"{name}_GBps"] = round(alg_bytes_bf16w(m, n, k) / (us * 1e-6) / 1e9, 1)
+        del qs
+
+    log("secondary: wide GEMMs")
+    Mw = 768
+    for name, (n, k) in (("wide_up", (16384, 2048)), ("wide_down", (2048, 16384))):
+        A = up_bits(synthetic.activations(Mw, k, 910 + n))
+        q, s = quantize(synthetic.weights(n, k, 911 + n))
+        Y = torch.empty(Mw * n, dtype=torch.int16, device=dev)
+        wsb = vla.vla_gemm_workspace_bytes(Mw, n, k, 1)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+        qa = torch.empty(Mw * k, dtype=torch.uint8, device=dev)
+        sa = torch.empty(1, dtype=torch.float32, device=dev)
+        wq_b = vla.vla_quantize_act_workspace_bytes(Mw, k)
+        wq = torch.zeros(wq_b, dtype=torch.uint8, device=dev)
+        flops = 2.0 * Mw * n * k
+
+        def w8a16(i):
+            vla.vla_gemm_fp8w(A, None, q, s, None, None, Y, ws, wsb, Mw, n, k)
+
+        def actq(i):
+            vla.vla_quantize_act(A, qa, sa, wq, wq_b, Mw, k)
+
+        def fp8fp8(i):
+            vla.vla_gemm_fp8w(qa, sa, q, s, None, None, Y, ws, wsb, Mw, n, k)
+
+        for tag, fn, peak in (("w8a16", w8a16, BF16_PEAK_TFLOPS), ("fp8xfp8", fp8fp8, FP8_PEAK_TFLOPS)):
+            if tag == "fp8xfp8":
+                actq(0)
+            ms = time_graph(fn, 20)
+            us = ms * 1000.0 / 20
+            tf = flops / (us * 1e-6) / 1e12
+            out[f"{name}_{tag}_us"] = round(us, 2)
+            out[f"{name}_{tag}_TFLOPs"] = round(tf, 1)
+            out[f"{name}_{tag}_frac"] = round(tf / peak, 4)
+        ms = time_graph(actq, 20)
+        out[f"{name}_act_quant_us"] = round(ms * 1000.0 / 20, 2)
+
+    log("secondary: 18-layer chain")
+    L = 18
+    gate, up, down = synthetic.chain_weights(L, H, I)
+    wgu, sgu, wd, sd = [], [], [], []
+    for l in range(L):
+        a, b = quantize(np.concatenate([gate[l], up[l]]))
+        c, d = quantize(down[l])
+        wgu.append(a); sgu.append(b); wd.append(c); sd.append(d)
+    xin = up_bits(synthetic.activations(M, H, synthetic.IDS["chain.x"]))
+    xout = torch.empty(M * H, dtype=torch.int16, device=dev)
+    sb = vla.vla_mlp_chain_scratch_bytes(M, H, I)
+    scratch = torch.zeros(sb, dtype=torch.uint8, device=dev)
+    cs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    h = vla.vla_mlp_chain_create(wgu, sgu, wd, sd, xin, xout, scratch, sb, L, M, H, I, cs)
+    try:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            vla.vla_mlp_chain_replay(h, cs)
+        cs.synchronize()
+        warm, cold = [], []
+        for i in range(40):
+            if i % 2 == 1:
+                flush.fill_(i & 0xFF)            # evict the 216 MiB of weights from cache
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cs)
+            vla.vla_mlp_chain_replay(h, cs)
+            e1.record(cs)
+            cs.synchronize()
+            (cold if i % 2 == 1 else warm).append(e0.elapsed_time(e1) * 1000.0)
+        out["chain_us_per_replay_warm"] = round(float(np.median(warm)), 2)
+        out["chain_us_per_replay_cold"] = round(float(np.median(cold)), 2)
+        chain_bytes = L * (2 * I * H + 8 * I + H * I + 4 * H) + 2 * 2 * M * H
+        out["chain_cold_GBps"] = round(chain_bytes / (np.median(cold) * 1e-6) / 1e9, 1)
+        del flush
+    finally:
+        vla.vla_mlp_chain_destroy(h)
+
+    log("secondary: dialect conversion 16384 x 2048")
+    N, K = 16384, 2048
+    W = up_bits(synthetic.weights(N, K, synthetic.IDS["dialect.W"]))
+    qf = torch.empty(N * K, dtype=torch.uint8, device=dev)
+    sf = torch.empty(N, dtype=torch.float32, device=dev)
+    qo = torch.empty(N * K, dtype=torch.uint8, device=dev)
+    so = torch.empty(N, dtype=torch.float32, device=dev)
+    qp = torch.empty(N * K, dtype=torch.uint8, device=dev)
+    t_q = time_graph(lambda i: vla.vla_quantize_pack(W, qf, sf, N, K, vla.VLA_WFMT_E4M3_FNUZ,
+                                                     vla.VLA_LAYOUT_ROWMAJOR), 10) * 100.0
+    t_r = time_graph(lambda i: vla.vla_reencode_fnuz_to_ocp(qf, sf, qo, so, N, K, vla.VLA_LAYOUT_ROWMAJOR), 10) * 100.0
+    t_p = time_graph(lambda i: vla.vla_pack_fp8(qo, qp, N, K), 10) * 100.0
+    out["dialect_quantize_fnuz_us"] = round(t_q, 2)
+    out["dialect_quantize_GBps"] = round((4 * N * K + N * K + 4 * N) / (t_q * 1e-6) / 1e9, 1)
+    out["dialect_reencode_us"] = round(t_r, 2)
+    out["dialect_reencode_GBps"] = round((2 * N * K + 8 * N) / (t_r * 1e-6) / 1e9, 1)
+    out["dialect_pack_us"] = round(t_p, 2)
+    return out
+
+
+def cpu_baseline(np, synthetic, W_up, W_dn):
+    """The oracle (unchanged) on the same workload: dequantize + fp64 GEMM per
+    call, alternating up and down, for about 10 s of host time."""
+    import oracle
+
+    A_up = oracle.bf16_value(synthetic.activations(M, H, synthetic.IDS["skinny.up.A"]))
+    A_dn = oracle.bf16_value(synthetic.activations(M, I, synthetic.IDS["skinny.down.A"]))
+    q_up, s_up = oracle.quantize_rows(W_up, oracle.OCP)
+    q_dn, s_dn = oracle.quantize_rows(W_dn, oracle.OCP)
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        for A, q, s in ((A_up, q_up, s_up), (A_dn, q_dn, s_dn)):
+            oracle.gemm(A, oracle.dequant_rows(q, s))
+            calls += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or calls >= 2000:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(el * 1e6 / calls, 1), "unit": "µs/call", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} calls (alternating up/down, M=50) of dequantize + fp64 GEMM, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,415 @@
+// C ABI of the library: argument validation, status codes and the
+// gated-MLP chain handle (HIP graph capture / replay).  Kernels live in
+// codec.hip and gemm.hip; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+#include <vector>
+
+#include "vla.h"
+#include "vla_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fn, const char* fmt, ...) {
+    char msg[384];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, sizeof(msg), fmt, ap);
+    va_end(ap);
+    snprintf(g_err, sizeof(g_err), "%s: %s", fn, msg);
+    return code;
+}
+
+int hip_fail(const char* fn, const char* what, hipError_t e) {
+    return fail(VLA_EHIP, fn, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                                   \
+    do {                                                                                 \
+        if ((p) == nullptr) return fail(VLA_EINVAL, fn, "%s is NULL", #p);               \
+        if (!aligned16(p)) return fail(VLA_EALIGN, fn, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+#define OPTIONAL_PTR(p)                                                                  \
+    do {                                                                                 \
+        if ((p) != nullptr && !aligned16(p))                                             \
+            return fail(VLA_EALIGN, fn, "%s is not 16-byte aligned", #p);                \
+    } while (0)
+
+int check_nk(const char* fn, int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0) return fail(VLA_EINVAL, fn, "N=%lld K=%lld must be positive", (long long)N, (long long)K);
+    if (N % 16 != 0) return fail(VLA_ESHAPE, fn, "N=%lld is not a multiple of 16", (long long)N);
+    if (K % 32 != 0) return fail(VLA_ESHAPE, fn, "K=%lld is not a multiple of 32", (long long)K);
+    if (N > (int64_t(1) << 30) || K > (int64_t(1) << 30) || N * K > (int64_t(1) << 40))
+        return fail(VLA_ESHAPE, fn, "N=%lld K=%lld too large", (long long)N, (long long)K);
+    return VLA_OK;
+}
+
+int check_mnk(const char* fn, int64_t M, int64_t N, int64_t K) {
+    if (M <= 0) return fail(VLA_EINVAL, fn, "M=%lld must be positive", (long long)M);
+    if (M > (int64_t(1) << 24)) return fail(VLA_ESHAPE, fn, "M=%lld too large", (long long)M);
+    return check_nk(fn, N, K);
+}
+
+int run_gemm(const char* fn, const vla::GemmProblem& pr, size_t ws_bytes, hipStream_t s) {
+    const vla::GemmPlan p = vla::plan_gemm(pr.M, pr.N, pr.K, pr.atype, pr.wtype, pr.epi);
+    if (!p.ok)
+        return fail(VLA_ESHAPE, fn, "M=%lld N=%lld K=%lld needs more split-K counters than the workspace holds",
+                    (long long)pr.M, (long long)pr.N, (long long)pr.K);
+    const size_t need = vla::gemm_ws_bytes(p, pr.M, pr.N);
+    if (ws_bytes < need)
+        return fail(VLA_EWORKSPACE, fn, "workspace %zu bytes < required %zu", ws_bytes, need);
+    hipError_t e = vla::launch_gemm(pr, s);
+    if (e != hipSuccess) return hip_fail(fn, "kernel launch", e);
+    return VLA_OK;
+}
+
+}  // namespace
+
+struct vla_mlp_chain {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int layers = 0;
+};
+
+namespace {
+std::mutex g_chain_mu;
+std::unordered_set<const vla_mlp_chain*> g_chains;
+
+struct ChainLayout {
+    size_t x_off, act_off, ws_off, total, ws_bytes;
+};
+
+ChainLayout chain_layout(int64_t M, int64_t H, int64_t I) {
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    ChainLayout c{};
+    c.x_off = 0;
+    c.act_off = up(static_cast<size_t>(M) * H * 2);
+    c.ws_off = c.act_off + up(static_cast<size_t>(M) * I * 2);
+    const auto pg = vla::plan_gemm(M, 2 * I, H, vla::AType::BF16, vla::WType::FP8, vla::Epi::GELU_MUL);
+    const auto pd = vla::plan_gemm(M, H, I, vla::AType::BF16, vla::WType::FP8, vla::Epi::PLAIN);
+    const size_t a = vla::gemm_ws_bytes(pg, M, 2 * I), b = vla::gemm_ws_bytes(pd, M, H);
+    c.ws_bytes = up(a > b ? a : b);
+    c.total = c.ws_off + c.ws_bytes;
+    return c;
+}
+
+int check_chain(const char* fn, const uint8_t* const* wgu, const float* const* sgu,
+                const uint8_t* const* wd, const float* const* sd, const uint16_t* x_in,
+                uint16_t* x_out, void* scratch, size_t scratch_bytes, int L, int64_t M,
+                int64_t H, int64_t I) {
+    if (!wgu || !sgu || !wd || !sd) return fail(VLA_EINVAL, fn, "weight pointer arrays must not be NULL");
+    if (L <= 0) return fail(VLA_EINVAL, fn, "L=%d must be positive", L);
+    if (int rc = check_mnk(fn, M, 2 * I, H)) return rc;
+    if (int rc = check_nk(fn, H, I)) return rc;
+    if (I % 16 != 0) return fail(VLA_ESHAPE, fn, "I=%lld is not a multiple of 16", (long long)I);
+    REQUIRE_PTR(x_in);
+    REQUIRE_PTR(x_out);
+    REQUIRE_PTR(scratch);
+    for (int l = 0; l < L; ++l) {
+        if (!wgu[l] || !sgu[l] || !wd[l] || !sd[l]) return fail(VLA_EINVAL, fn, "layer %d has a NULL weight", l);
+        if (!aligned16(wgu[l]) || !aligned16(sgu[l]) || !aligned16(wd[l]) || !aligned16(sd[l]))
+            return fail(VLA_EALIGN, fn, "layer %d weight not 16-byte aligned", l);
+    }
+    const ChainLayout c = chain_layout(M, H, I);
+    if (scratch_bytes < c.total)
+        return fail(VLA_EWORKSPACE, fn, "scratch %zu bytes < required %zu", scratch_bytes, c.total);
+    const uint8_t* xo = reinterpret_cast<const uint8_t*>(x_out);
+    const uint8_t* xi = reinterpret_cast<const uint8_t*>(x_in);
+    const uint8_t* sc = static_cast<const uint8_t*>(scratch);
+    const size_t xb = static_cast<size_t>(M) * H * 2;
+    auto overlap = [](const uint8_t* a, size_t na, const uint8_t* b, size_t nb) { return a < b + nb && b < a + na; };
+    if (overlap(xo, xb, xi, xb) || overlap(xo, xb, sc, c.total))
+        return fail(VLA_EINVAL, fn, "x_out overlaps x_in or scratch");
+    return VLA_OK;
+}
+
+int enqueue_chain(const char* fn, const uint8_t* const* wgu, const float* const* sgu,
+                  const uint8_t* const* wd, const float* const* sd, const uint16_t* x_in,
+                  uint16_t* x_out, void* scratch, int L, int64_t M, int64_t H, int64_t I,
+                  hipStream_t s) {
+    const ChainLayout c = chain_layout(M, H, I);
+    uint8_t* base = static_cast<uint8_t*>(scratch);
+    uint16_t* xbuf = reinterpret_cast<uint16_t*>(base + c.x_off);
+    uint16_t* act = reinterpret_cast<uint16_t*>(base + c.act_off);
+    void* ws = base + c.ws_off;
+    const uint16_t* x = x_in;
+    for (int l = 0; l < L; ++l) {
+        vla::GemmProblem g{};
+        g.A = x; g.W = wgu[l]; g.s_w = sgu[l]; g.Y = act; g.ws = ws;
+        g.M = M; g.N = 2 * I; g.K = H;
+        g.atype = vla::AType::BF16; g.wtype = vla::WType::FP8; g.epi = vla::Epi::GELU_MUL;
+        if (int rc = run_gemm(fn, g, c.ws_bytes, s)) return rc;
+        uint16_t* y = (l == L - 1) ? x_out : xbuf;
+        vla::GemmProblem d{};
+        d.A = act; d.W = wd[l]; d.s_w = sd[l]; d.resid = x; d.Y = y; d.ws = ws;
+        d.M = M; d.N = H; d.K = I;
+        d.atype = vla::AType::BF16; d.wtype = vla::WType::FP8; d.epi = vla::Epi::PLAIN;
+        if (int rc = run_gemm(fn, d, c.ws_bytes, s)) return rc;
+        x = y;
+    }
+    return VLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vla_status_string(int status) {
+    switch (status) {
+        case VLA_OK: return "ok";
+        case VLA_EINVAL: return "invalid argument";
+        case VLA_ESHAPE: return "unsupported shape";
+        case VLA_EALIGN: return "misaligned pointer";
+        case VLA_EWORKSPACE: return "workspace too small";
+        case VLA_EHIP: return "HIP error";
+        case VLA_ESTATE: return "invalid handle state";
+        default: return "unknown status";
+    }
+}
+
+const char* vla_last_error(void) { return g_err; }
+
+size_t vla_packed_bytes(int64_t N, int64_t K, int wfmt) {
+    if (N <= 0 || K <= 0) return 0;
+    return static_cast<size_t>(N) * static_cast<size_t>(K) * (wfmt == VLA_WFMT_BF16 ? 2 : 1);
+}
+
+int vla_quantize_pack(const float* W, void* Wq, float* scales, int64_t N, int64_t K, int wfmt,
+                      int layout, void* stream) {
+    const char* fn = "vla_quantize_pack";
+    if (wfmt < VLA_WFMT_BF16 || wfmt > VLA_WFMT_E4M3_FNUZ) return fail(VLA_EINVAL, fn, "unknown wfmt %d", wfmt);
+    if (layout != VLA_LAYOUT_ROWMAJOR && layout != VLA_LAYOUT_MFMA) return fail(VLA_EINVAL, fn, "unknown layout %d", layout);
+    if (int rc = check_nk(fn, N, K)) return rc;
+    REQUIRE_PTR(W);
+    REQUIRE_PTR(Wq);
+    if (wfmt == VLA_WFMT_BF16) {
+        if (scales != nullptr) return fail(VLA_EINVAL, fn, "scales must be NULL for BF16");
+    } else {
+        REQUIRE_PTR(scales);
+    }
+    hipError_t e = vla::launch_quantize_pack(W, Wq, scales, N, K, wfmt, layout, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
+}
+
+int vla_pack_fp8(const uint8_t* q_rowmajor, uint8_t* q_packed, int64_t N, int64_t K, void* stream) {
+    const char* fn = "vla_pack_fp8";
+    if (int rc = check_nk(fn, N, K)) return rc;
+    REQUIRE_PTR(q_rowmajor);
+    REQUIRE_PTR(q_packed);
+    const size_t nb = static_cast<size_t>(N) * K;
+    const uint8_t *a = q_rowmajor, *b = q_packed;
+    if (a < b + nb && b < a + nb) return fail(VLA_EINVAL, fn, "input and output overlap");
+    hipError_t e = vla::launch_pack_fp8(q_rowmajor, q_packed, N, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
+}
+
+int vla_reencode_fnuz_to_ocp(const uint8_t* q_fnuz, const float* s_fnuz, uint8_t* q_ocp,
+                             float* s_ocp, int64_t N, int64_t K, int layout, void* stream) {
+    const char* fn = "vla_reencode_fnuz_to_ocp";
+    if (layout != VLA_LAYOUT_ROWMAJOR && layout != VLA_LAYOUT_MFMA) return fail(VLA_EINVAL, fn, "unknown layout %d", layout);
+    if (int rc = check_nk(fn, N, K)) return rc;
+    REQUIRE_PTR(q_fnuz);
+    REQUIRE_PTR(s_fnuz);
+    REQUIRE_PTR(q_ocp);
+    REQUIRE_PTR(s_ocp);
+    const size_t nb = static_cast<size_t>(N) * K;
+    auto partial = [](const void* x, const void* y, size_t n) {
+        const uint8_t *a = static_cast<const uint8_t*>(x), *b = static_cast<const uint8_t*>(y);
+        return a != b && a < b + n && b < a + n;
+    };
+    if (partial(q_fnuz, q_ocp, nb) || partial(s_fnuz, s_ocp, static_cast<size_t>(N) * 4))
+        return fail(VLA_EINVAL, fn, "outputs partially overlap inputs");
+    hipError_t e = vla::launch_reencode(q_fnuz, s_fnuz, q_ocp, s_ocp, N, K, layout, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
+}
+
+size_t vla_quantize_act_workspace_bytes(int64_t M, int64_t K) { return vla::quantize_act_ws_bytes(M, K); }
+
+int vla_quantize_act(const uint16_t* A, uint8_t* qa, float* s_a, void* ws, size_t ws_bytes,
+                     int64_t M, int64_t K, void* stream) {
+    const char* fn = "vla_quantize_act";
+    if (int rc = check_mnk(fn, M, 16, K)) return rc;
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(qa);
+    REQUIRE_PTR(s_a);
+    REQUIRE_PTR(ws);
+    const size_t need = vla::quantize_act_ws_bytes(M, K);
+    if (ws_bytes < need) return fail(VLA_EWORKSPACE, fn, "workspace %zu bytes < required %zu", ws_bytes, need);
+    hipError_t e = vla::launch_quantize_act(A, qa, s_a, ws, M, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
+}
+
+size_t vla_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int wfmt) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    const vla::WType wt = (wfmt == VLA_WFMT_BF16) ? vla::WType::BF16 : vla::WType::FP8;
+    size_t best = 0;
+    const vla::AType ats[2] = {vla::AType::BF16, vla::AType::FP8};
+    const vla::Epi eps[2] = {vla::Epi::PLAIN, vla::Epi::GELU_MUL};
+    for (auto at : ats)
+        for (auto ep : eps) {
+            const size_t b = vla::gemm_ws_bytes(vla::plan_gemm(M, N, K, at, wt, ep), M, N);
+            if (b > best) best = b;
+        }
+    return best;
+}
+
+int vla_gemm_fp8w(const void* A, const float* s_a, const uint8_t* Wq, const float* s_w,
+                  const uint16_t* bias, const uint16_t* residual, uint16_t* Y, void* ws,
+                  size_t ws_bytes, int64_t M, int64_t N, int64_t K, void* stream) {
+    const char* fn = "vla_gemm_fp8w";
+    if (int rc = check_mnk(fn, M, N, K)) return rc;
+    REQUIRE_PTR(A);
+    OPTIONAL_PTR(s_a);
+    REQUIRE_PTR(Wq);
+    REQUIRE_PTR(s_w);
+    OPTIONAL_PTR(bias);
+    OPTIONAL_PTR(residual);
+    REQUIRE_PTR(Y);
+    REQUIRE_PTR(ws);
+    vla::GemmProblem p{};
+    p.A = A; p.s_a = s_a; p.W = Wq; p.s_w = s_w; p.bias = bias; p.resid = residual; p.Y = Y; p.ws = ws;
+    p.M = M; p.N = N; p.K = K;
+    p.atype = s_a ? vla::AType::FP8 : vla::AType::BF16;
+    p.wtype = vla::WType::FP8;
+    p.epi = vla::Epi::PLAIN;
+    return run_gemm(fn, p, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int vla_gemm_bf16(const uint16_t* A, const uint16_t* Wq, const uint16_t* bias,
+                  const uint16_t* residual, uint16_t* Y, void* ws, size_t ws_bytes, int64_t M,
+                  int64_t N, int64_t K, void* stream) {
+    const char* fn = "vla_gemm_bf16";
+    if (int rc = check_mnk(fn, M, N, K)) return rc;
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(Wq);
+    OPTIONAL_PTR(bias);
+    OPTIONAL_PTR(residual);
+    REQUIRE_PTR(Y);
+    REQUIRE_PTR(ws);
+    vla::GemmProblem p{};
+    p.A = A; p.W = Wq; p.bias = bias; p.resid = residual; p.Y = Y; p.ws = ws;
+    p.M = M; p.N = N; p.K = K;
+    p.atype = vla::AType::BF16;
+    p.wtype = vla::WType::BF16;
+    p.epi = vla::Epi::PLAIN;
+    return run_gemm(fn, p, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int vla_gemm_fp8w_gelu_mul(const uint16_t* A, const uint8_t* Wgu, const float* s_gu,
+                           uint16_t* act, uint16_t* gu, void* ws, size_t ws_bytes, int64_t M,
+                           int64_t I, int64_t K, void* stream) {
+    const char* fn = "vla_gemm_fp8w_gelu_mul";
+    if (int rc = check_mnk(fn, M, 2 * I, K)) return rc;
+    if (I % 16 != 0) return fail(VLA_ESHAPE, fn, "I=%lld is not a multiple of 16", (long long)I);
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(Wgu);
+    REQUIRE_PTR(s_gu);
+    REQUIRE_PTR(act);
+    OPTIONAL_PTR(gu);
+    REQUIRE_PTR(ws);
+    vla::GemmProblem p{};
+    p.A = A; p.W = Wgu; p.s_w = s_gu; p.Y = act; p.gu = gu; p.ws = ws;
+    p.M = M; p.N = 2 * I; p.K = K;
+    p.atype = vla::AType::BF16;
+    p.wtype = vla::WType::FP8;
+    p.epi = vla::Epi::GELU_MUL;
+    return run_gemm(fn, p, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t vla_mlp_chain_scratch_bytes(int64_t M, int64_t H, int64_t I) {
+    if (M <= 0 || H <= 0 || I <= 0) return 0;
+    return chain_layout(M, H, I).total;
+}
+
+int vla_mlp_chain_enqueue(const uint8_t* const* wgu, const float* const* sgu,
+                          const uint8_t* const* wd, const float* const* sd, const uint16_t* x_in,
+                          uint16_t* x_out, void* scratch, size_t scratch_bytes, int L, int64_t M,
+                          int64_t H, int64_t I, void* stream) {
+    const char* fn = "vla_mlp_chain_enqueue";
+    if (int rc = check_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, scratch_bytes, L, M, H, I)) return rc;
+    return enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I,
+                         static_cast<hipStream_t>(stream));
+}
+
+int vla_mlp_chain_create(const uint8_t* const* wgu, const float* const* sgu,
+                         const uint8_t* const* wd, const float* const* sd, const uint16_t* x_in,
+                         uint16_t* x_out, void* scratch, size_t scratch_bytes, int L, int64_t M,
+                         int64_t H, int64_t I, void* capture_stream, vla_mlp_chain** out) {
+    const char* fn = "vla_mlp_chain_create";
+    if (!out) return fail(VLA_EINVAL, fn, "out is NULL");
+    *out = nullptr;
+    if (!capture_stream) return fail(VLA_EINVAL, fn, "capture_stream must not be the null stream");
+    if (int rc = check_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, scratch_bytes, L, M, H, I)) return rc;
+    hipStream_t s = static_cast<hipStream_t>(capture_stream);
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed);
+    if (e != hipSuccess) return hip_fail(fn, "hipStreamBeginCapture", e);
+    int rc = enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I, s);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(s, &graph);
+    if (rc != VLA_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+    }
+    if (e != hipSuccess) return hip_fail(fn, "hipStreamEndCapture", e);
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        return hip_fail(fn, "hipGraphInstantiate", e);
+    }
+    vla_mlp_chain* h = new (std::nothrow) vla_mlp_chain;
+    if (!h) {
+        (void)hipGraphExecDestroy(exec);
+        (void)hipGraphDestroy(graph);
+        return fail(VLA_EINVAL, fn, "out of host memory");
+    }
+    h->graph = graph;
+    h->exec = exec;
+    h->layers = L;
+    {
+        std::lock_guard<std::mutex> lk(g_chain_mu);
+        g_chains.insert(h);
+    }
+    *out = h;
+    return VLA_OK;
+}
+
+int vla_mlp_chain_replay(vla_mlp_chain* chain, void* stream) {
+    const char* fn = "vla_mlp_chain_replay";
+    {
+        std::lock_guard<std::mutex> lk(g_chain_mu);
+        if (!chain || g_chains.find(chain) == g_chains.end())
+            return fail(VLA_ESTATE, fn, "no graph captured (handle is NULL or destroyed)");
+    }
+    hipError_t e = hipGraphLaunch(chain->exec, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? VLA_OK : hip_fail(fn, "hipGraphLaunch", e);
+}
+
+int vla_mlp_chain_destroy(vla_mlp_chain* chain) {
+    const char* fn = "vla_mlp_chain_destroy";
+    if (!chain) return VLA_OK;
+    {
+        std::lock_guard<std::mutex> lk(g_chain_mu);
+        auto it = g_chains.find(chain);
+        if (it == g_chains.end()) return fail(VLA_ESTATE, fn, "handle already destroyed");
+        g_chains.erase(it);
+    }
+    hipError_t e1 = hipGraphExecDestroy(chain->exec);
+    hipError_t e2 = hipGraphDestroy(chain->graph);
+    delete chain;
+    if (e1 != hipSuccess) return hip_fail(fn, "hipGraphExecDestroy", e1);
+    if (e2 != hipSuccess) return hip_fail(fn, "hipGraphDestroy", e2);
+    return VLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,270 @@
+// Weight/activation codecs on gfx950: per-output-channel quantize + MFMA
+// lane pack, FP8 byte pack, FNUZ -> OCP re-encode, per-tensor activation
+// quantization.  These run once at load time (weights) or once per call
+// (activations of the FP8 x FP8 GEMM) and are HBM-bound byte streams.
+//
+// Every fp32 operation here is a single IEEE operation (division is the
+// correctly rounded __fdiv_rn; no contraction), so results match the
+// reference quantizer bit for bit.
+#pragma clang fp contract(off)
+
+#include "vla_device.h"
+#include "vla_internal.h"
+
+namespace vla {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Offset (in elements) of the 8-value slot `slot` of 16-row tile n0 in the
+// given layout.  slot = k0 * 64 + lane, lane = 16 k1 + n1.
+__device__ __forceinline__ int64_t slot_offset(int layout, int64_t n0, int64_t slot, int64_t K) {
+    const int64_t k0 = slot >> 6, lane = slot & 63, k1 = lane >> 4, n1 = lane & 15;
+    if (layout == 1) return (n0 * (K >> 5) * 64 + slot) * 8;          // MFMA layout
+    return (n0 * 16 + n1) * K + k0 * 32 + k1 * 8;                     // row-major
+}
+
+// One workgroup per 16-row tile.  Phase 1: row absmax -> scale.  Phase 2:
+// each thread encodes 8-value slots (reads 2 x 16 B, writes 8 B / 16 B).
+template <int WFMT>
+__global__ __launch_bounds__(kThreads) void quantize_pack_kernel(const float* __restrict__ W,
+                                                                 void* __restrict__ Wq,
+                                                                 float* __restrict__ scales,
+                                                                 int64_t K, int layout) {
+    __shared__ float s_scale[16];
+    const int64_t n0 = blockIdx.x;
+    const int t = threadIdx.x;
+    const float* tile = W + n0 * 16 * K;
+
+    if (WFMT != VLA_WFMT_BF16) {
+        // 16 threads per row, float4 loads strided by 64 floats
+        const int r = t >> 4, c = t & 15;
+        const float* row = tile + static_cast<int64_t>(r) * K;
+        float m = 0.0f;
+        for (int64_t k = 4 * c; k < K; k += 64) {
+            float4 v = *reinterpret_cast<const float4*>(row + k);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+        m = group_max<16>(m);
+        if (c == 0) {
+            const float maxv = (WFMT == VLA_WFMT_E4M3_FNUZ) ? 240.0f : 448.0f;
+            const float sc = (m == 0.0f) ? 1.0f : __fdiv_rn(m, maxv);
+            s_scale[r] = sc;
+            scales[n0 * 16 + r] = sc;
+        }
+        __syncthreads();
+    }
+
+    const int64_t nslots = (K >> 5) * 64;
+    for (int64_t slot = t; slot < nslots; slot += kThreads) {
+        const int64_t k0 = slot >> 6;
+        const int lane = static_cast<int>(slot & 63), k1 = lane >> 4, n1 = lane & 15;
+        const float* src = tile + static_cast<int64_t>(n1) * K + k0 * 32 + k1 * 8;
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 b = *reinterpret_cast<const float4*>(src + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const int64_t off = slot_offset(layout, n0, slot, K);
+        if (WFMT == VLA_WFMT_BF16) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+                       (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Wq) + off) =
+                make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            const float sc = s_scale[n1];
+            uint32_t w[2] = {0, 0};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float x = __fdiv_rn(v[i], sc);
+                const uint32_t code = (WFMT == VLA_WFMT_E4M3_FNUZ) ? encode_e4m3<true>(x)
+                                                                    : encode_e4m3<false>(x);
+                w[i >> 2] |= code << (8 * (i & 3));
+            }
+            *reinterpret_cast<uint2*>(static_cast<uint8_t*>(Wq) + off) = make_uint2(w[0], w[1]);
+        }
+    }
+}
+
+// Row-major FP8 -> MFMA layout: one thread per 8-byte slot.
+__global__ __launch_bounds__(kThreads) void pack_fp8_kernel(const uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ qp, int64_t N,
+                                                            int64_t K) {
+    const int64_t total = N * K / 8;
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const int64_t per_tile = (K >> 5) * 64;
+        const int64_t n0 = i / per_tile, slot = i % per_tile;
+        const uint2 v = *reinterpret_cast<const uint2*>(q + slot_offset(0, n0, slot, K));
+        *reinterpret_cast<uint2*>(qp + i * 8) = v;
+    }
+}
+
+// FNUZ -> OCP, one workgroup per 16-row tile.  The tile's per-row flag
+// "contains a +-240 code" picks j; the byte map for each j is built once
+// per workgroup in LDS from the bit-level decoder/encoder.  Every byte is
+// read in phase 1 before any is written in phase 2 by the same thread, so
+// in-place use is safe.
+__global__ __launch_bounds__(kThreads) void reencode_kernel(const uint8_t* q, const float* sc,
+                                                            uint8_t* q2, float* sc2, int64_t K,
+                                                            int layout) {
+    __shared__ uint8_t lut[2][256];
+    __shared__ int has240[16];
+    const int64_t n0 = blockIdx.x;
+    const int t = threadIdx.x;
+    if (t < 16) has240[t] = 0;
+    {
+        // lut[j][b] = encode_ocp(2^j * decode_fnuz(b)); FNUZ NaN -> 0x7F
+        const uint32_t b = static_cast<uint32_t>(t);
+        if (b == 0x80u) {
+            lut[0][b] = 0x7F;
+            lut[1][b] = 0x7F;
+        } else {
+            const float v = decode_e4m3<true>(b);
+            lut[0][b] = encode_e4m3<false>(v);
+            lut[1][b] = encode_e4m3<false>(v * 2.0f);
+        }
+    }
+    __syncthreads();
+    const int64_t nslots = (K >> 5) * 64;
+    for (int64_t slot = t; slot < nslots; slot += kThreads) {
+        const int n1 = static_cast<int>(slot & 15);
+        const uint2 v = *reinterpret_cast<const uint2*>(q + slot_offset(layout, n0, slot, K));
+        bool hit = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t byte = ((i < 4 ? v.x : v.y) >> (8 * (i & 3))) & 0x7Fu;
+            hit |= byte == 0x7Fu;
+        }
+        if (hit) atomicOr(&has240[n1], 1);
+    }
+    __syncthreads();
+    for (int64_t slot = t; slot < nslots; slot += kThreads) {
+        const int n1 = static_cast<int>(slot & 15);
+        const int j = has240[n1] ? 0 : 1;
+        const int64_t off = slot_offset(layout, n0, slot, K);
+        const uint2 v = *reinterpret_cast<const uint2*>(q + off);
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t byte = ((i < 4 ? v.x : v.y) >> (8 * (i & 3))) & 0xFFu;
+            w[i >> 2] |= static_cast<uint32_t>(lut[j][byte]) << (8 * (i & 3));
+        }
+        *reinterpret_cast<uint2*>(q2 + off) = make_uint2(w[0], w[1]);
+    }
+    if (t < 16) sc2[n0 * 16 + t] = has240[t] ? sc[n0 * 16 + t] : sc[n0 * 16 + t] * 0.5f;
+}
+
+// Activation quantization, pass 1: per-block absmax of 8-element chunks.
+constexpr int kActBlocks = 512;
+
+__global__ __launch_bounds__(kThreads) void act_absmax_kernel(const uint16_t* __restrict__ A,
+                                                              float* __restrict__ partial,
+                                                              int64_t chunks) {
+    __shared__ float red[kThreads / kWave];
+    float m = 0.0f;
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < chunks;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const uint4 v = *reinterpret_cast<const uint4*>(A + i * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(w[j] & 0xFFFFu))));
+            m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(w[j] >> 16))));
+        }
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float r = red[0];
+        for (int i = 1; i < kThreads / kWave; ++i) r = fmaxf(r, red[i]);
+        partial[blockIdx.x] = r;
+    }
+}
+
+// Pass 2: every block reduces the partial maxima (same order everywhere),
+// forms s_a, and encodes its share of chunks.
+__global__ __launch_bounds__(kThreads) void act_encode_kernel(const uint16_t* __restrict__ A,
+                                                              const float* __restrict__ partial,
+                                                              uint8_t* __restrict__ qa,
+                                                              float* __restrict__ s_a,
+                                                              int64_t chunks, int nparts) {
+    __shared__ float s_sc;
+    if (threadIdx.x < kWave) {
+        float m = 0.0f;
+        for (int i = threadIdx.x; i < nparts; i += kWave) m = fmaxf(m, partial[i]);
+        m = wave_max(m);
+        if (threadIdx.x == 0) {
+            const float sc = (m == 0.0f) ? 1.0f : __fdiv_rn(m, 448.0f);
+            s_sc = sc;
+            if (blockIdx.x == 0) *s_a = sc;
+        }
+    }
+    __syncthreads();
+    const float sc = s_sc;
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < chunks;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const uint4 v = *reinterpret_cast<const uint4*>(A + i * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[2] = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint16_t h = static_cast<uint16_t>((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+            const uint32_t code = encode_e4m3<false>(__fdiv_rn(bf16_to_f32(h), sc));
+            o[j >> 2] |= code << (8 * (j & 3));
+        }
+        *reinterpret_cast<uint2*>(qa + i * 8) = make_uint2(o[0], o[1]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_pack(const float* W, void* Wq, float* scales, int64_t N, int64_t K,
+                                int wfmt, int layout, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(N / 16));
+    switch (wfmt) {
+        case VLA_WFMT_BF16:
+            quantize_pack_kernel<VLA_WFMT_BF16><<<grid, kThreads, 0, s>>>(W, Wq, scales, K, layout);
+            break;
+        case VLA_WFMT_E4M3_OCP:
+            quantize_pack_kernel<VLA_WFMT_E4M3_OCP><<<grid, kThreads, 0, s>>>(W, Wq, scales, K, layout);
+            break;
+        default:
+            quantize_pack_kernel<VLA_WFMT_E4M3_FNUZ><<<grid, kThreads, 0, s>>>(W, Wq, scales, K, layout);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_fp8(const uint8_t* q, uint8_t* qp, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t total = N * K / 8;
+    const int64_t blocks = (total + kThreads - 1) / kThreads;
+    const unsigned grid = static_cast<unsigned>(blocks < 65536 ? blocks : 65536);
+    pack_fp8_kernel<<<grid, kThreads, 0, s>>>(q, qp, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_reencode(const uint8_t* q, const float* sc, uint8_t* q2, float* sc2, int64_t N,
+                           int64_t K, int layout, hipStream_t s) {
+    reencode_kernel<<<static_cast<unsigned>(N / 16), kThreads, 0, s>>>(q, sc, q2, sc2, K, layout);
+    return hipGetLastError();
+}
+
+size_t quantize_act_ws_bytes(int64_t, int64_t) { return kActBlocks * sizeof(float); }
+
+hipError_t launch_quantize_act(const uint16_t* A, uint8_t* qa, float* s_a, void* ws, int64_t M,
+                               int64_t K, hipStream_t s) {
+    const int64_t chunks = M * K / 8;
+    float* partial = static_cast<float*>(ws);
+    act_absmax_kernel<<<kActBlocks, kThreads, 0, s>>>(A, partial, chunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t want = (chunks + kThreads - 1) / kThreads;
+    const unsigned grid = static_cast<unsigned>(want < 2048 ? (want > 0 ? want : 1) : 2048);
+    act_encode_kernel<<<grid, kThreads, 0, s>>>(A, partial, qa, s_a, chunks, kActBlocks);
+    return hipGetLastError();
+}
+
+}  // namespace vla

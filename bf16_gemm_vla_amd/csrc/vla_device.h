@@ -1,0 +1,128 @@
+// Device-side helpers shared by the gfx950 kernels: bit-level E4M3 and bf16
+// conversions, MFMA operand types and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vla {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even on the 16 dropped bits; NaN stays a
+// quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// ------------------------------------------------------------------- E4M3
+
+// Dialect constants: OCP (bias 7, max 448 = 0x43E00000, smallest normal
+// 2^-6) and FNUZ (bias 8, max 240 = 0x43700000, smallest normal 2^-7).
+template <bool FNUZ>
+struct E4M3 {
+    static constexpr int bias = FNUZ ? 8 : 7;
+    static constexpr uint32_t max_bits = FNUZ ? 0x43700000u : 0x43E00000u;
+    static constexpr uint32_t min_normal_bits = FNUZ ? 0x3C000000u : 0x3C800000u;
+    static constexpr uint8_t max_code = FNUZ ? 0x7F : 0x7E;
+    // subnormal quantum is 2^(1 - bias - 3); its reciprocal as an fp32
+    static constexpr float inv_quantum = FNUZ ? 1024.0f : 512.0f;
+};
+
+// fp32 -> E4M3 code: round to nearest even, saturate at +-max; NaN -> OCP
+// 0x7F|sign or FNUZ 0x80; zero keeps its sign in OCP, is 0x00 in FNUZ.
+template <bool FNUZ>
+__device__ __forceinline__ uint8_t encode_e4m3(float x) {
+    using F = E4M3<FNUZ>;
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return FNUZ ? 0x80 : static_cast<uint8_t>(0x7F | sign);
+    if (a >= F::max_bits) return static_cast<uint8_t>(F::max_code | sign);
+    uint32_t code;
+    if (a >= F::min_normal_bits) {
+        // keep 3 of the 23 fraction bits, ties to even, then rebias
+        const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+        code = r - static_cast<uint32_t>((127 - F::bias) << 3);
+    } else {
+        // subnormal range: count quanta, rintf rounds ties to even; the
+        // scaling by a power of two is exact
+        code = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * F::inv_quantum));
+    }
+    if (FNUZ && code == 0) return 0;
+    return static_cast<uint8_t>(code | sign);
+}
+
+// E4M3 code -> fp32 (exact).  NaN codes give a quiet NaN.
+template <bool FNUZ>
+__device__ __forceinline__ float decode_e4m3(uint32_t b) {
+    using F = E4M3<FNUZ>;
+    const uint32_t mag = b & 0x7Fu;
+    const bool neg = (b & 0x80u) != 0;
+    if (FNUZ ? (b == 0x80u) : (mag == 0x7Fu)) return __uint_as_float(0x7FC00000u);
+    const uint32_t e = mag >> 3, m = mag & 7u;
+    float v;
+    if (e == 0)
+        v = static_cast<float>(m) * (1.0f / F::inv_quantum);
+    else
+        v = __uint_as_float(((e + 127u - F::bias) << 23) | (m << 20));
+    return neg ? -v : v;
+}
+
+// Four OCP E4M3 codes (one dword) -> four bf16 (two dwords), exact: the
+// hardware converts pairs of FP8 to fp32, and an FP8 value has at most 4
+// significant bits, so its fp32 pattern's high half is the bf16 pattern.
+__device__ __forceinline__ u32x2_t ocp4_to_bf16x4(uint32_t w) {
+    auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    u32x2_t r;
+    r.x = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+    r.y = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+    return r;
+}
+
+// Eight OCP E4M3 codes -> eight bf16 as an MFMA operand.
+__device__ __forceinline__ bf16x8_t ocp8_to_bf16x8(u32x2_t w) {
+    u32x2_t a = ocp4_to_bf16x4(w.x), b = ocp4_to_bf16x4(w.y);
+    u32x4_t v = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// --------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Max over aligned groups of `G` consecutive lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float gelu_tanh(float g) {
+    const float c = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+}
+
+}  // namespace vla

@@ -1,0 +1,67 @@
+// Host-side declarations shared between the C ABI layer and the kernel
+// launchers.  Launchers assume validated arguments and report launch errors
+// through their hipError_t return value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "vla.h"
+
+namespace vla {
+
+// ---------------------------------------------------------------- codec
+hipError_t launch_quantize_pack(const float* W, void* Wq, float* scales, int64_t N, int64_t K,
+                                int wfmt, int layout, hipStream_t s);
+hipError_t launch_pack_fp8(const uint8_t* q, uint8_t* qp, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_reencode(const uint8_t* q, const float* sc, uint8_t* q2, float* sc2, int64_t N,
+                           int64_t K, int layout, hipStream_t s);
+size_t quantize_act_ws_bytes(int64_t M, int64_t K);
+hipError_t launch_quantize_act(const uint16_t* A, uint8_t* qa, float* s_a, void* ws, int64_t M,
+                               int64_t K, hipStream_t s);
+
+// ----------------------------------------------------------------- GEMM
+enum class AType { BF16 = 0, FP8 = 1 };
+enum class WType { BF16 = 0, FP8 = 1 };
+enum class Epi { PLAIN = 0, GELU_MUL = 1 };
+
+struct GemmProblem {
+    const void* A;
+    const float* s_a;       // device scalar for FP8 A, else nullptr
+    const void* W;          // packed weights
+    const float* s_w;       // per-row scales (FP8 weights), else nullptr
+    const uint16_t* bias;   // nullable
+    const uint16_t* resid;  // nullable
+    uint16_t* Y;            // PLAIN: M x N; GELU_MUL: M x N/2
+    uint16_t* gu;           // GELU_MUL debug output M x N, nullable
+    void* ws;
+    int64_t M, N, K;        // N = weight rows
+    AType atype;
+    WType wtype;
+    Epi epi;
+};
+
+// Launch plan chosen for a problem (host-side, deterministic per shape).
+struct GemmPlan {
+    int kernel;     // 0 = skinny (M <= 64), 1 = wide
+    int nt;         // 16-column tiles per workgroup (skinny)
+    int steps;      // K steps (of 32) per wave per workgroup chunk (skinny)
+    int waves;      // wavefronts per workgroup (skinny)
+    int ksplit;     // number of K chunks across workgroups
+    int groups;     // N groups (grid x)
+    int mblocks;    // M blocks (grid y of the wide kernel)
+    bool ok;        // false when the shape exceeds the split-K counter space
+};
+
+// The first kCounterBytes of every GEMM workspace hold the split-K arrival
+// counters (one uint32 per output tile group), at the same place for every
+// shape, so one zero-filled workspace can serve calls of different shapes.
+constexpr size_t kCounterBytes = 65536;
+constexpr int kMaxCounters = static_cast<int>(kCounterBytes / 4);
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi);
+size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N);
+hipError_t launch_gemm(const GemmProblem& pr, hipStream_t s);
+
+}  // namespace vla

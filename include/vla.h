@@ -1,0 +1,226 @@
+/*
+ * vla.h - C ABI of the MI355X (gfx950) FP8/BF16-weight GEMM library for
+ * small-batch vision-language-action inference.
+ *
+ * Conventions (all entry points):
+ *  - Arguments come in the order device pointers, sizes, scalars, stream,
+ *    the order of the kernel calls shown on "FlashRT: an inference engine for
+ *    real-time robot control" (itsolotime.com), section 3.3 (pipeline table:
+ *    pointers, then dims, then eps, then stream).
+ *  - Every pointer named "device" is device memory owned by the caller; the
+ *    library never allocates, frees or retains device memory, except that a
+ *    chain handle records the pointers it was created with.
+ *  - bf16 tensors are passed as uint16_t bit patterns.  FP8 tensors are
+ *    uint8_t E4M3 codes.  Matrices are row-major unless a layout says
+ *    otherwise.  Weights are N x K: one row per output channel.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *    on it and return without synchronising; they are safe to record under
+ *    stream capture (no allocation, no host reads of device values, no
+ *    memset nodes) - the property the page "Deploying DeepSeek-V4-Flash on
+ *    AMD MI300X" (lehuy.net), section "HIP Graphs", requires of captured
+ *    launches.
+ *  - Return value: VLA_OK (0) or a positive VLA_E* code; nothing is thrown.
+ *    vla_status_string() names a code and vla_last_error() gives a message
+ *    for the calling thread's last failure.  Launch failures are read with
+ *    hipGetLastError right after the launch and reported as VLA_EHIP.
+ *  - Alignment: every device pointer must be 16-byte aligned (VLA_EALIGN).
+ *
+ * Shapes: N must be a multiple of 16 and K a multiple of 32 (one 16x16x32
+ * MFMA tile); M >= 1 is free (ragged rows are masked).
+ */
+#ifndef VLA_H
+#define VLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define VLA_OK 0
+#define VLA_EINVAL 1      /* NULL pointer, non-positive size, unknown enum */
+#define VLA_ESHAPE 2      /* N % 16, K % 32, or mismatched shapes */
+#define VLA_EALIGN 3      /* a device pointer is not 16-byte aligned */
+#define VLA_EWORKSPACE 4  /* workspace or scratch smaller than required */
+#define VLA_EHIP 5        /* a HIP runtime call or kernel launch failed */
+#define VLA_ESTATE 6      /* chain handle not created, or already destroyed */
+
+/* Weight formats. */
+#define VLA_WFMT_BF16 0
+#define VLA_WFMT_E4M3_OCP 1   /* OCP E4M3: bias 7, max 448, NaN S.1111.111, no inf */
+#define VLA_WFMT_E4M3_FNUZ 2  /* E4M3 FNUZ: bias 8, max 240, NaN 0x80 only, no -0, no inf */
+
+/* Weight layouts. */
+#define VLA_LAYOUT_ROWMAJOR 0
+/* MFMA lane layout for gfx950's 16x16x32 BF16/FP8 MFMA (8 values per lane;
+ * "Real-time VLA inference on AMD hardware" (cyberneticphysics.com),
+ * introduction and section "Packing around the instruction", which gives
+ * the 4-values-per-lane CDNA3 form).  Element (n, k), n = 16 n0 + n1,
+ * k = 32 k0 + 8 k1 + k2, sits at element offset
+ *     ((n0 * (K / 32) + k0) * 64 + 16 k1 + n1) * 8 + k2,
+ * so each lane's 8 values (8 bytes FP8, 16 bytes BF16) are contiguous and a
+ * wavefront's 64 slices of one 16x32 fragment form one contiguous block. */
+#define VLA_LAYOUT_MFMA 1
+
+const char *vla_status_string(int status);
+/* Message of the calling thread's last failed call ("" if none). */
+const char *vla_last_error(void);
+
+/* --------------------------------------------------------- weight codecs */
+
+/* Bytes of an N x K weight in format `wfmt` (either layout). */
+size_t vla_packed_bytes(int64_t N, int64_t K, int wfmt);
+
+/* Quantize (FP8) or round (BF16) an fp32 weight and lay it out.
+ * "Real-time VLA inference on AMD hardware", section "Packing around the
+ * instruction": weights are quantized and packed once at load time and stay
+ * at fixed addresses.
+ *   W      device fp32, N x K row-major (one row per output channel).
+ *   Wq     device output, vla_packed_bytes(N, K, wfmt) bytes, in `layout`.
+ *   scales device fp32[N] output for FP8 formats, must be NULL for BF16.
+ * FP8: scales[n] = fp32(max_k |W[n,k]| / 448) (OCP) or / 240 (FNUZ), 1 for an
+ * all-zero row; code = encode(fp32(W[n,k] / scales[n])), IEEE division,
+ * round to nearest even, saturating at +-max.  BF16: round to nearest even.
+ * W must be finite.  Errors: EINVAL, ESHAPE, EALIGN, EHIP. */
+int vla_quantize_pack(const float *W, void *Wq, float *scales, int64_t N, int64_t K, int wfmt,
+                      int layout, void *stream);
+
+/* Reorder an N x K row-major FP8 code matrix into VLA_LAYOUT_MFMA (a pure
+ * byte permutation).  q_rowmajor and q_packed must not overlap. */
+int vla_pack_fp8(const uint8_t *q_rowmajor, uint8_t *q_packed, int64_t N, int64_t K,
+                 void *stream);
+
+/* Re-encode E4M3 FNUZ codes + per-row scales to OCP E4M3 codes + scales so
+ * that every value dec(q) * s is preserved.  The pages ("Real-time VLA
+ * inference on AMD hardware", introduction and "Different FP8
+ * representation"; "Deploying DeepSeek-V4-Flash on AMD MI300X", FP8 dialect
+ * section) state that a byte reads as half the value under FNUZ.  Per row n:
+ * j = 1 when the row holds no +-240 code (0x7F / 0xFF): every byte is kept
+ * and s' = s / 2 (value-exact); otherwise j = 0: q' = encode_ocp(dec_fnuz(q))
+ * (exact except the 16 odd-mantissa codes below 2^-6, which are ties and go
+ * to the even code, error <= 2^-10 * s) and s' = s.  FNUZ NaN (0x80) -> 0x7F.
+ *   q_fnuz, s_fnuz  device inputs, N x K codes in `layout`, fp32[N].
+ *   q_ocp,  s_ocp   device outputs, same shapes; may alias the inputs
+ *                   exactly (in-place) but not partially. */
+int vla_reencode_fnuz_to_ocp(const uint8_t *q_fnuz, const float *s_fnuz, uint8_t *q_ocp,
+                             float *s_ocp, int64_t N, int64_t K, int layout, void *stream);
+
+/* Per-tensor OCP quantization of bf16 activations for the FP8 x FP8 GEMM:
+ * s_a = fp32(max |A| / 448) (1 if A is all zero), qa = encode_ocp(fp32(A / s_a)).
+ *   A   device bf16 M x K;  qa device uint8 M x K;  s_a device float[1].
+ *   ws  device workspace of vla_quantize_act_workspace_bytes(M, K) bytes
+ *       (no initial contents required).
+ * s_a stays on the device (no host read), so the call can be captured. */
+size_t vla_quantize_act_workspace_bytes(int64_t M, int64_t K);
+int vla_quantize_act(const uint16_t *A, uint8_t *qa, float *s_a, void *ws, size_t ws_bytes,
+                     int64_t M, int64_t K, void *stream);
+
+/* ------------------------------------------------------------------ GEMM */
+
+/* Workspace for vla_gemm_fp8w / vla_gemm_bf16 / vla_gemm_fp8w_gelu_mul at
+ * this shape (N = weight rows; for gelu_mul N = 2 I).  Its first 64 KiB
+ * hold one arrival counter per output tile group (the same place for every
+ * shape); the rest holds split-K partial sums.  The workspace must be
+ * ZERO-FILLED before its first use; every completed call leaves the
+ * counters at zero again, so one zeroed buffer (sized for the largest
+ * shape) serves any number of later calls and graph replays, of any
+ * shapes, that run one after another.  Calls that run concurrently must
+ * not share a workspace. */
+size_t vla_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int wfmt);
+
+/* Y = bf16( s[n] * sum_k A[m,k] * dec(Wq[n,k]) + bias[n] ), optionally
+ * followed by Y = bf16(residual + Y).
+ * "Real-time VLA inference on AMD hardware", sections "FP8 helps the encoder
+ * and hurts the decoder" and "Merging gate and up" (bias in the epilogue).
+ *   A        device: bf16 M x K when s_a == NULL (BF16 x FP8 weights);
+ *            OCP E4M3 codes M x K when s_a != NULL (FP8 x FP8, the value of
+ *            A is dec(A) * s_a[0]; s_a is a device float[1]).
+ *   Wq, s_w  OCP E4M3 weight in VLA_LAYOUT_MFMA and its fp32[N] scales.
+ *   bias     device bf16[N] or NULL.
+ *   residual device bf16 M x N or NULL; may alias Y exactly (in-place add).
+ *   Y        device bf16 M x N output.
+ * Arithmetic: fp32 accumulation of exact bf16 (or fp8) products; epilogue
+ * y = acc * s_w[n] (FP8 x FP8: acc * (s_a * s_w[n])) + bias, rounded to
+ * bf16 nearest-even; residual added in fp32 and rounded again.  The
+ * summation order is fixed per shape, so repeated calls are bitwise equal.
+ * Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP. */
+int vla_gemm_fp8w(const void *A, const float *s_a, const uint8_t *Wq, const float *s_w,
+                  const uint16_t *bias, const uint16_t *residual, uint16_t *Y, void *ws,
+                  size_t ws_bytes, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* As vla_gemm_fp8w with BF16 weights (VLA_LAYOUT_MFMA) and no weight scale:
+ * Y = bf16( sum_k A[m,k] * Wq[n,k] + bias[n] ) (+ residual). */
+int vla_gemm_bf16(const uint16_t *A, const uint16_t *Wq, const uint16_t *bias,
+                  const uint16_t *residual, uint16_t *Y, void *ws, size_t ws_bytes, int64_t M,
+                  int64_t N, int64_t K, void *stream);
+
+/* Merged gate/up GEMM with the GELU-tanh * up epilogue of a gated MLP.
+ * "Real-time VLA inference on AMD hardware", section "Merging gate and up":
+ * the gate and up weights are concatenated, W = [W_gate; W_up] (2I x K,
+ * rows 0..I-1 gate, I..2I-1 up), and one GEMM computes both.
+ *   g = bf16(s[n] * A @ W_gate^T), u = bf16(s[I+n] * A @ W_up^T),
+ *   act = bf16( 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) * u ).
+ *   A     device bf16 M x K.
+ *   Wgu   OCP E4M3 2I x K in VLA_LAYOUT_MFMA, s_gu its fp32[2I] scales.
+ *   act   device bf16 M x I output.
+ *   gu    device bf16 M x 2I output of [g, u], or NULL.
+ * I must be a multiple of 16.  Workspace: vla_gemm_workspace_bytes(M, 2I, K, OCP). */
+int vla_gemm_fp8w_gelu_mul(const uint16_t *A, const uint8_t *Wgu, const float *s_gu,
+                           uint16_t *act, uint16_t *gu, void *ws, size_t ws_bytes, int64_t M,
+                           int64_t I, int64_t K, void *stream);
+
+/* ------------------------------------------------------- gated-MLP chain */
+
+/* L gated-MLP layers applied to x (M x H bf16):
+ *   act = gelu_mul(x @ [Wgate_l; Wup_l]^T)        (vla_gemm_fp8w_gelu_mul)
+ *   x   = bf16(x + bf16(act @ Wdown_l^T))         (vla_gemm_fp8w, residual)
+ * "Real-time VLA inference on AMD hardware", section "How FlashRT works":
+ * the whole sequence is recorded once as a HIP graph and replayed, with
+ * weights at fixed addresses.
+ *   wgu, sgu  host arrays of L device pointers: OCP 2I x H weights
+ *             (VLA_LAYOUT_MFMA) and fp32[2I] scales.
+ *   wd, sd    host arrays of L device pointers: OCP H x I weights and
+ *             fp32[H] scales.
+ *   x_in      device bf16 M x H input (read only).
+ *   x_out     device bf16 M x H output (must not overlap x_in or scratch).
+ *   scratch   device, vla_mlp_chain_scratch_bytes(M, H, I) bytes,
+ *             ZERO-FILLED before first use (it embeds a GEMM workspace).
+ * Every device pointer must stay valid, at the same address, for the life
+ * of a handle. */
+size_t vla_mlp_chain_scratch_bytes(int64_t M, int64_t H, int64_t I);
+
+/* Enqueue the chain's 2L kernels directly (no graph). */
+int vla_mlp_chain_enqueue(const uint8_t *const *wgu, const float *const *sgu,
+                          const uint8_t *const *wd, const float *const *sd,
+                          const uint16_t *x_in, uint16_t *x_out, void *scratch,
+                          size_t scratch_bytes, int L, int64_t M, int64_t H, int64_t I,
+                          void *stream);
+
+typedef struct vla_mlp_chain vla_mlp_chain;
+
+/* Record the chain once on `capture_stream` (relaxed capture mode, which
+ * records only that stream's work; it must not be the null stream) and
+ * instantiate it.  *out receives a host handle owned by the caller. */
+int vla_mlp_chain_create(const uint8_t *const *wgu, const float *const *sgu,
+                         const uint8_t *const *wd, const float *const *sd,
+                         const uint16_t *x_in, uint16_t *x_out, void *scratch,
+                         size_t scratch_bytes, int L, int64_t M, int64_t H, int64_t I,
+                         void *capture_stream, vla_mlp_chain **out);
+
+/* Launch the recorded graph on `stream`.  ESTATE for a NULL or destroyed
+ * handle (the page "FlashRT: an inference engine for real-time robot
+ * control", section 4.1, raises "No graph captured" on replay before
+ * capture). */
+int vla_mlp_chain_replay(vla_mlp_chain *chain, void *stream);
+
+/* Free the graph and the handle.  The handle must not be used afterwards;
+ * destroying NULL is a no-op returning VLA_OK. */
+int vla_mlp_chain_destroy(vla_mlp_chain *chain);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VLA_H */

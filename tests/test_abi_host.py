@@ -1,0 +1,140 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/vla.h declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bf16_gemm_vla_amd as vla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vla_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vla.LIB_PATH):
+        from bf16_gemm_vla_amd import build
+        build.build()
+    return vla.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(vla.SIGNATURES), set(names) ^ set(vla.SIGNATURES)
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert vla.status_string(code) not in ("", "unknown status")
+    assert vla.status_string(99) == "unknown status"
+
+
+def test_size_queries(lib):
+    assert vla.vla_packed_bytes(64, 128, vla.VLA_WFMT_E4M3_OCP) == 64 * 128
+    assert vla.vla_packed_bytes(64, 128, vla.VLA_WFMT_BF16) == 64 * 128 * 2
+    assert vla.vla_packed_bytes(0, 128, 1) == 0
+    assert vla.vla_gemm_workspace_bytes(50, 4096, 1024, 1) >= 256
+    assert vla.vla_gemm_workspace_bytes(50, 1024, 4096, 1) > vla.vla_gemm_workspace_bytes(50, 1024, 128, 1)
+    assert vla.vla_quantize_act_workspace_bytes(768, 2048) > 0
+    assert vla.vla_mlp_chain_scratch_bytes(50, 1024, 4096) > 50 * 1024 * 2 + 50 * 4096 * 2
+
+
+def test_size_queries_never_crash(lib):
+    """Host-side planning for every shape class, including ones too narrow
+    for the fused gate/up epilogue (N/16 odd or 1)."""
+    for M in (1, 4, 50, 64, 65, 768, 100000):
+        for N in (16, 32, 48, 80, 1024, 4096, 8192, 16384, 1 << 20):
+            for K in (32, 64, 96, 1024, 4096, 16384):
+                for wfmt in (0, 1):
+                    assert vla.vla_gemm_workspace_bytes(M, N, K, wfmt) >= 65536
+    assert vla.vla_gemm_workspace_bytes(0, 16, 32, 1) == 0
+
+
+A16 = 0x10000        # a 16-byte aligned fake address, never dereferenced on error paths
+
+
+def rc_of(fn, *args):
+    return getattr(vla.load(), fn)(*args)
+
+
+@pytest.mark.parametrize("N,K,code", [(17, 128, vla.VLA_ESHAPE), (64, 100, vla.VLA_ESHAPE),
+                                      (0, 128, vla.VLA_EINVAL), (64, -32, vla.VLA_EINVAL)])
+def test_gemm_shape_errors(lib, N, K, code):
+    rc = rc_of("vla_gemm_fp8w", A16, None, A16, A16, None, None, A16, A16, 1 << 20, 50, N, K, None)
+    assert rc == code
+    assert "vla_gemm_fp8w" in vla.last_error()
+
+
+def test_gemm_pointer_errors(lib):
+    assert rc_of("vla_gemm_fp8w", None, None, A16, A16, None, None, A16, A16, 1 << 20, 50, 64, 128, None) == vla.VLA_EINVAL
+    assert rc_of("vla_gemm_fp8w", A16 + 2, None, A16, A16, None, None, A16, A16, 1 << 20, 50, 64, 128, None) == vla.VLA_EALIGN
+    assert rc_of("vla_gemm_fp8w", A16, None, A16, A16, A16 + 8, None, A16, A16, 1 << 20, 50, 64, 128, None) == vla.VLA_EALIGN
+    assert rc_of("vla_gemm_bf16", A16, A16, None, None, None, A16, 1 << 20, 50, 64, 128, None) == vla.VLA_EINVAL
+    assert rc_of("vla_gemm_fp8w", A16, None, A16, A16, None, None, A16, A16, 1 << 20, 0, 64, 128, None) == vla.VLA_EINVAL
+
+
+def test_gemm_workspace_too_small(lib):
+    # the counter region alone is 64 KiB
+    assert rc_of("vla_gemm_fp8w", A16, None, A16, A16, None, None, A16, A16, 65535, 50, 1024, 4096, None) == vla.VLA_EWORKSPACE
+    assert rc_of("vla_gemm_fp8w", A16, None, A16, A16, None, None, A16, A16, 65535, 768, 2048, 16384, None) == vla.VLA_EWORKSPACE
+
+
+def test_gelu_mul_shape_errors(lib):
+    # I = 24 is not a multiple of 16
+    assert rc_of("vla_gemm_fp8w_gelu_mul", A16, A16, A16, A16, None, A16, 1 << 20, 50, 24, 128, None) == vla.VLA_ESHAPE
+
+
+def test_codec_errors(lib):
+    assert rc_of("vla_quantize_pack", A16, A16, A16, 64, 128, 7, 1, None) == vla.VLA_EINVAL
+    assert rc_of("vla_quantize_pack", A16, A16, A16, 64, 128, 1, 5, None) == vla.VLA_EINVAL
+    assert rc_of("vla_quantize_pack", A16, A16, A16, 64, 128, vla.VLA_WFMT_BF16, 1, None) == vla.VLA_EINVAL
+    assert rc_of("vla_quantize_pack", A16, A16, None, 64, 128, vla.VLA_WFMT_E4M3_OCP, 1, None) == vla.VLA_EINVAL
+    assert rc_of("vla_quantize_pack", A16, A16, A16, 64, 96 + 8, 1, 1, None) == vla.VLA_ESHAPE
+    assert rc_of("vla_pack_fp8", A16, A16 + 64, 64, 128, None) == vla.VLA_EINVAL        # overlap
+    assert rc_of("vla_reencode_fnuz_to_ocp", A16, A16, A16 + 16, A16, 64, 128, 1, None) == vla.VLA_EINVAL
+    assert rc_of("vla_quantize_act", A16, A16, A16, A16, 0, 50, 1024, None) == vla.VLA_EWORKSPACE
+
+
+def test_chain_errors(lib):
+    arr = (ctypes.c_void_p * 2)(A16, A16)
+    need = vla.vla_mlp_chain_scratch_bytes(50, 1024, 4096)
+    big = 1 << 30
+    # scratch too small
+    assert rc_of("vla_mlp_chain_enqueue", arr, arr, arr, arr, A16, 1 << 33, A16 * 3, need - 1, 2, 50, 1024, 4096, None) == vla.VLA_EWORKSPACE
+    # x_out overlapping scratch
+    assert rc_of("vla_mlp_chain_enqueue", arr, arr, arr, arr, A16, big + 16, big, need, 2, 50, 1024, 4096, None) == vla.VLA_EINVAL
+    # null layer pointer
+    bad = (ctypes.c_void_p * 2)(A16, None)
+    assert rc_of("vla_mlp_chain_enqueue", bad, arr, arr, arr, A16, 1 << 33, big, need, 2, 50, 1024, 4096, None) == vla.VLA_EINVAL
+    # L <= 0, bad I
+    assert rc_of("vla_mlp_chain_enqueue", arr, arr, arr, arr, A16, 1 << 33, big, need, 0, 50, 1024, 4096, None) == vla.VLA_EINVAL
+    assert rc_of("vla_mlp_chain_enqueue", arr, arr, arr, arr, A16, 1 << 33, big, need, 2, 50, 1024, 4104, None) == vla.VLA_ESHAPE
+    # create on the null stream is refused before any capture
+    out = ctypes.c_void_p()
+    assert rc_of("vla_mlp_chain_create", arr, arr, arr, arr, A16, 1 << 33, big, need, 2, 50, 1024, 4096, None, ctypes.byref(out)) == vla.VLA_EINVAL
+    assert out.value is None
+
+
+def test_chain_handle_state_machine(lib):
+    assert rc_of("vla_mlp_chain_replay", None, None) == vla.VLA_ESTATE
+    assert "No graph captured".lower() in vla.last_error().lower() or "no graph captured" in vla.last_error()
+    assert rc_of("vla_mlp_chain_destroy", None) == vla.VLA_OK
+    # an address that was never a handle is rejected, not dereferenced
+    assert rc_of("vla_mlp_chain_replay", A16, None) == vla.VLA_ESTATE
+    assert rc_of("vla_mlp_chain_destroy", A16) == vla.VLA_ESTATE
+
+
+def test_python_wrapper_raises(lib):
+    with pytest.raises(RuntimeError, match="vla_gemm_bf16: unsupported shape"):
+        vla.vla_gemm_bf16(A16, A16, None, None, A16, A16, 1 << 20, 50, 20, 128, stream=0)

@@ -1,0 +1,130 @@
+"""GPU parity of the codecs: quantize+pack, FP8 pack, FNUZ->OCP re-encode and
+activation quantization must equal the oracle byte for byte."""
+import numpy as np
+import pytest
+import torch
+
+import bf16_gemm_vla_amd as vla
+import oracle
+import synthetic
+from oracle import FNUZ, OCP
+from tests.gpu_util import Guarded, dev, host, zeros_ws
+
+pytestmark = pytest.mark.gpu
+
+WFMT = {OCP: vla.VLA_WFMT_E4M3_OCP, FNUZ: vla.VLA_WFMT_E4M3_FNUZ}
+
+
+def gpu_quantize(W: np.ndarray, wfmt: int, layout: int):
+    N, K = W.shape
+    nbytes = vla.vla_packed_bytes(N, K, wfmt)
+    q = Guarded(nbytes)
+    s = Guarded(N * 4) if wfmt != vla.VLA_WFMT_BF16 else None
+    vla.vla_quantize_pack(dev(W), q.t, None if s is None else s.t, N, K, wfmt, layout)
+    q.check()
+    if s is not None:
+        s.check()
+    return q, s
+
+
+def oracle_codes(W, dialect, layout):
+    q, s = oracle.quantize_rows(W, dialect)
+    return (oracle.pack(q, 8) if layout == vla.VLA_LAYOUT_MFMA else q.reshape(-1)), s
+
+
+SHAPES = [(64, 128, "tiny.W"), (16, 32, "edge.min"), (48, 96, "edge.ragged"), (1024, 4096, "skinny.down.W")]
+
+
+@pytest.mark.parametrize("dialect", [OCP, FNUZ])
+@pytest.mark.parametrize("layout", [vla.VLA_LAYOUT_MFMA, vla.VLA_LAYOUT_ROWMAJOR])
+@pytest.mark.parametrize("N,K,name", SHAPES)
+def test_quantize_pack_bit_exact(dialect, layout, N, K, name):
+    print(f"quantize_pack dialect={dialect} layout={layout} N={N} K={K}", flush=True)
+    W = synthetic.weights(N, K, synthetic.IDS.get(name, 555))
+    W[N // 2] = 0.0                                   # all-zero row -> s = 1, codes 0
+    W[1, 0] = -0.0
+    q, s = gpu_quantize(W, WFMT[dialect], layout)
+    ref_q, ref_s = oracle_codes(W, dialect, layout)
+    assert np.array_equal(s.numpy(np.float32), ref_s)
+    got = q.numpy(np.uint8)
+    assert np.array_equal(got, ref_q), f"{(got != ref_q).sum()} bytes differ"
+
+
+def test_quantize_pack_bf16_bit_exact():
+    N, K = 256, 512
+    W = synthetic.weights(N, K, 556)
+    W[3, :8] = np.float32([1.0, -2.5, 3.0039062, 1e-40, -1e-38, 65504.0, 3.3895314e38, 0.0])
+    q, _ = gpu_quantize(W, vla.VLA_WFMT_BF16, vla.VLA_LAYOUT_MFMA)
+    ref = oracle.pack(oracle.bf16_round(W.astype(np.float64)), 8)
+    assert np.array_equal(q.numpy(np.uint16), ref)
+
+
+def test_dialect_config_fnuz_reencode_pack():
+    """16384 x 2048 N(0, 0.02) -> FNUZ (absmax/240) -> OCP -> MFMA pack, byte for byte."""
+    N, K = 16384, 2048
+    print("dialect config: quantize FNUZ row-major, re-encode, pack", flush=True)
+    W = synthetic.weights(N, K, synthetic.IDS["dialect.W"])
+    q, s = gpu_quantize(W, vla.VLA_WFMT_E4M3_FNUZ, vla.VLA_LAYOUT_ROWMAJOR)
+    q2, s2 = Guarded(N * K), Guarded(N * 4)
+    vla.vla_reencode_fnuz_to_ocp(q.t, s.t, q2.t, s2.t, N, K, vla.VLA_LAYOUT_ROWMAJOR)
+    qp = Guarded(N * K)
+    vla.vla_pack_fp8(q2.t, qp.t, N, K)
+    for b in (q2, s2, qp):
+        b.check()
+    ref_q, ref_s = oracle.quantize_rows(W, FNUZ)
+    assert np.array_equal(q.numpy(np.uint8).reshape(N, K), ref_q)
+    ref_q2, ref_s2 = oracle.reencode_fnuz_to_ocp(ref_q, ref_s)
+    assert np.array_equal(s2.numpy(np.float32), ref_s2)
+    assert np.array_equal(q2.numpy(np.uint8).reshape(N, K), ref_q2)
+    assert np.array_equal(qp.numpy(np.uint8), oracle.pack(ref_q2, 8))
+
+
+@pytest.mark.parametrize("layout", [vla.VLA_LAYOUT_MFMA, vla.VLA_LAYOUT_ROWMAJOR])
+def test_reencode_j1_rows_and_in_place(layout):
+    """Rows without +-240 keep their bytes at half scale; in-place use allowed."""
+    g = synthetic.rng(4242)
+    N, K = 64, 256
+    allowed = np.array([b for b in range(256) if b not in (0x7F, 0xFF, 0x80)], np.uint8)
+    q = allowed[g.integers(0, len(allowed), (N, K))]
+    q[::3, 5] = 0x7F            # every third row holds +240 -> j = 0
+    q[1, 7] = 0x80              # FNUZ NaN
+    s = g.uniform(1e-4, 1e-2, N).astype(np.float32)
+    ref_q, ref_s = oracle.reencode_fnuz_to_ocp(q, s)
+    stored = oracle.pack(q, 8) if layout == vla.VLA_LAYOUT_MFMA else q.reshape(-1)
+    dq, ds = dev(stored), dev(s)
+    vla.vla_reencode_fnuz_to_ocp(dq, ds, dq, ds, N, K, layout)       # in place
+    want = oracle.pack(ref_q, 8) if layout == vla.VLA_LAYOUT_MFMA else ref_q.reshape(-1)
+    assert np.array_equal(host(dq), want)
+    assert np.array_equal(host(ds), ref_s)
+
+
+def test_pack_fp8_matches_oracle():
+    g = synthetic.rng(4243)
+    N, K = 80, 160
+    q = g.integers(0, 256, (N, K)).astype(np.uint8)
+    out = Guarded(N * K)
+    vla.vla_pack_fp8(dev(q), out.t, N, K)
+    out.check()
+    assert np.array_equal(out.numpy(np.uint8), oracle.pack(q, 8))
+
+
+@pytest.mark.parametrize("M,K", [(4, 128), (50, 1024), (768, 2048), (3, 32)])
+def test_quantize_act_bit_exact(M, K):
+    A = synthetic.activations(M, K, 4300 + M)
+    qa, sa = Guarded(M * K), Guarded(16)
+    ws = zeros_ws(vla.vla_quantize_act_workspace_bytes(M, K))
+    vla.vla_quantize_act(dev(A), qa.t, sa.t, ws, ws.numel(), M, K)
+    qa.check()
+    ref_q, ref_s = oracle.quantize_act(A)
+    assert sa.numpy(np.float32)[0] == ref_s
+    assert np.array_equal(qa.numpy(np.uint8).reshape(M, K), ref_q)
+
+
+def test_quantize_act_all_zero():
+    M, K = 8, 64
+    A = np.zeros((M, K), np.uint16)
+    qa, sa = Guarded(M * K), Guarded(16)
+    ws = zeros_ws(vla.vla_quantize_act_workspace_bytes(M, K))
+    vla.vla_quantize_act(dev(A), qa.t, sa.t, ws, ws.numel(), M, K)
+    assert sa.numpy(np.float32)[0] == 1.0
+    assert np.all(qa.numpy(np.uint8) == 0)

@@ -1,0 +1,198 @@
+"""GPU parity of the GEMMs against the oracle's fp64 GEMM on the same
+dequantized operands: |y - y_ref| <= 4e-3 * sum_k |a w| elementwise; lane-map
+probe (one-hot weights must reproduce A's columns bit for bit); canaries,
+repeatability, bias, residual (in place), ragged shapes and sampled checks at
+the full encoder sizes."""
+import numpy as np
+import pytest
+import torch
+
+import bf16_gemm_vla_amd as vla
+import oracle
+import synthetic
+from oracle import OCP
+from tests.gpu_util import Guarded, assert_gemm_close, bf16_f64, dev, host, zeros_ws
+
+pytestmark = pytest.mark.gpu
+
+
+class Weights:
+    """An fp32 weight quantized+packed on the GPU, and its oracle codes."""
+
+    def __init__(self, W: np.ndarray, wfmt: int):
+        self.N, self.K = W.shape
+        self.wfmt = wfmt
+        nbytes = vla.vla_packed_bytes(self.N, self.K, wfmt)
+        self.q = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.s = torch.empty(self.N, dtype=torch.float32, device="cuda") if wfmt != vla.VLA_WFMT_BF16 else None
+        vla.vla_quantize_pack(dev(W), self.q, self.s, self.N, self.K, wfmt, vla.VLA_LAYOUT_MFMA)
+        if wfmt == vla.VLA_WFMT_BF16:
+            self.w = oracle.bf16_value(oracle.bf16_round(W.astype(np.float64)))
+        else:
+            qo, so = oracle.quantize_rows(W, OCP)
+            self.w = oracle.dequant_rows(qo, so, OCP)
+
+
+def run_gemm(A_dev, w: Weights, M, s_a=None, bias=None, resid=None, Y=None):
+    N, K = w.N, w.K
+    ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, N, K, w.wfmt))
+    out = Y if Y is not None else Guarded(M * N * 2)
+    ydev = out.t if isinstance(out, Guarded) else out
+    if w.wfmt == vla.VLA_WFMT_BF16:
+        vla.vla_gemm_bf16(A_dev, w.q, bias, resid, ydev, ws, ws.numel(), M, N, K)
+    else:
+        vla.vla_gemm_fp8w(A_dev, s_a, w.q, w.s, bias, resid, ydev, ws, ws.numel(), M, N, K)
+    if isinstance(out, Guarded):
+        out.check()
+        return out.numpy(np.uint16).reshape(M, N), ws
+    return host(out, np.uint16).reshape(M, N), ws
+
+
+def check(M, N, K, wfmt, seed, bias=False):
+    print(f"gemm M={M} N={N} K={K} wfmt={wfmt} bias={bias}", flush=True)
+    A = synthetic.activations(M, K, seed)
+    w = Weights(synthetic.weights(N, K, seed + 1), wfmt)
+    b_bits = synthetic.activations(1, N, seed + 2)[0] if bias else None
+    y, ws = run_gemm(dev(A), w, M, bias=None if b_bits is None else dev(b_bits))
+    ref, yabs = oracle.gemm(bf16_f64(A), w.w, None if b_bits is None else bf16_f64(b_bits))
+    assert_gemm_close(y, ref, yabs)
+    # split-K counters are back at zero after the call
+    assert int(host(ws[:256]).view(np.uint32).sum()) == 0
+    return y
+
+
+# ---------------------------------------------------------------- probes
+
+@pytest.mark.parametrize("M", [50, 200])
+def test_lane_map_probe_one_hot(M):
+    """Each weight row a single 1.0 code: Y must equal permuted columns of A exactly."""
+    g = synthetic.rng(5000 + M)
+    N, K = 128, 256
+    perm = g.integers(0, K, N)
+    q = np.zeros((N, K), np.uint8)
+    q[np.arange(N), perm] = 0x38
+    qp = dev(oracle.pack(q, 8))
+    s = dev(np.ones(N, np.float32))
+    A = synthetic.activations(M, K, 5001)
+    ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, N, K, 1))
+    Y = Guarded(M * N * 2)
+    vla.vla_gemm_fp8w(dev(A), None, qp, s, None, None, Y.t, ws, ws.numel(), M, N, K)
+    Y.check()
+    assert np.array_equal(Y.numpy(np.uint16).reshape(M, N), A[:, perm])
+
+
+def test_lane_map_probe_one_hot_fp8_x_fp8():
+    """FP8 x FP8: one-hot weights select A's codes; s_a = 1 gives dec(A) exactly."""
+    g = synthetic.rng(5100)
+    M, N, K = 192, 128, 256
+    perm = g.integers(0, K, N)
+    q = np.zeros((N, K), np.uint8)
+    q[np.arange(N), perm] = 0x38
+    qa = g.integers(0, 256, (M, K)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x38           # no NaN codes
+    qa[qa == 0x80] = 0x00                    # a one-hot sum of -0 and +0 products is +0
+    ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, N, K, 1))
+    Y = Guarded(M * N * 2)
+    vla.vla_gemm_fp8w(dev(qa), dev(np.ones(1, np.float32)), dev(oracle.pack(q, 8)), dev(np.ones(N, np.float32)),
+                      None, None, Y.t, ws, ws.numel(), M, N, K)
+    want = oracle.bf16_round(oracle.decode(qa, OCP)[:, perm])
+    got = Y.numpy(np.uint16).reshape(M, N)
+    bad = got != want
+    if bad.any():
+        codes = sorted(set(qa[:, perm][bad].tolist()))
+        raise AssertionError(f"{bad.sum()} mismatches; A codes involved: {[hex(c) for c in codes[:32]]}; "
+                             f"got {[hex(v) for v in got[bad][:8]]} want {[hex(v) for v in want[bad][:8]]}")
+
+
+# ------------------------------------------------------- configs + edges
+
+def test_tiny_config():
+    """A 4 x 128 bf16, W 64 x 128 -> OCP per-channel (absmax/448)."""
+    check(4, 64, 128, vla.VLA_WFMT_E4M3_OCP, synthetic.IDS["tiny.A"])
+
+
+@pytest.mark.parametrize("wfmt", [vla.VLA_WFMT_E4M3_OCP, vla.VLA_WFMT_BF16])
+@pytest.mark.parametrize("N,K", [(4096, 1024), (1024, 4096)])
+def test_skinny_configs(wfmt, N, K):
+    """Action-decoder shapes, M = 50, up- and down-projection."""
+    check(50, N, K, wfmt, synthetic.IDS["skinny.up.A"] if N == 4096 else synthetic.IDS["skinny.down.A"])
+
+
+@pytest.mark.parametrize("M", [1, 10, 16, 17, 33, 64, 65, 100, 129, 571])
+def test_ragged_rows(M):
+    check(M, 96, 160, vla.VLA_WFMT_E4M3_OCP, 6000 + M)
+
+
+@pytest.mark.parametrize("N,K", [(16, 32), (48, 96), (80, 32), (16, 4096), (2048, 64), (272, 1056)])
+@pytest.mark.parametrize("M", [50, 300])
+def test_ragged_tiles(M, N, K):
+    check(M, N, K, vla.VLA_WFMT_E4M3_OCP, 6100 + N + K)
+
+
+@pytest.mark.parametrize("M", [50, 256])
+def test_bias_epilogue(M):
+    check(M, 256, 512, vla.VLA_WFMT_E4M3_OCP, 6200 + M, bias=True)
+    check(M, 256, 512, vla.VLA_WFMT_BF16, 6300 + M, bias=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(50, 1024, 4096), (200, 256, 1024)])
+def test_residual_in_place(M, N, K):
+    A = synthetic.activations(M, K, 6400)
+    w = Weights(synthetic.weights(N, K, 6401), vla.VLA_WFMT_E4M3_OCP)
+    x = synthetic.activations(M, N, 6402)
+    xd = dev(x)
+    ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, N, K, 1))
+    vla.vla_gemm_fp8w(dev(A), None, w.q, w.s, None, xd, xd, ws, ws.numel(), M, N, K)   # x += A W^T
+    got = bf16_f64(host(xd, np.uint16).reshape(M, N))
+    ref, yabs = oracle.gemm(bf16_f64(A), w.w)
+    xf = bf16_f64(x)
+    bound = 4e-3 * yabs + 2.0 ** -8 * (np.abs(xf) + np.abs(ref))
+    assert np.all(np.abs(got - (xf + ref)) <= bound)
+
+
+@pytest.mark.parametrize("M,N,K", [(50, 4096, 1024), (50, 1024, 4096), (768, 512, 4096)])
+def test_repeat_runs_bitwise_equal(M, N, K):
+    A = dev(synthetic.activations(M, K, 6500))
+    w = Weights(synthetic.weights(N, K, 6501), vla.VLA_WFMT_E4M3_OCP)
+    ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, N, K, 1))
+    outs = []
+    for _ in range(5):
+        Y = torch.empty(M * N, dtype=torch.int16, device="cuda")
+        vla.vla_gemm_fp8w(A, None, w.q, w.s, None, None, Y, ws, ws.numel(), M, N, K)
+        outs.append(host(Y))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+# ----------------------------------------------------- encoder-size runs
+
+def _sampled_rows(M, n, seed):
+    return np.sort(synthetic.rng(seed).choice(M, n, replace=False))
+
+
+@pytest.mark.parametrize("N,K", [(16384, 2048), (2048, 16384)])
+@pytest.mark.parametrize("fp8_act", [False, True])
+def test_wide_config_sampled(N, K, fp8_act):
+    """M = 768 encoder shapes at full size; 24 sampled rows x all N vs the oracle."""
+    M = 768
+    print(f"wide config N={N} K={K} fp8_act={fp8_act}", flush=True)
+    tid = synthetic.IDS["wide.up.A"] if N == 16384 else synthetic.IDS["wide.down.A"]
+    A = synthetic.activations(M, K, tid)
+    w = Weights(synthetic.weights(N, K, tid + 1), vla.VLA_WFMT_E4M3_OCP)
+    Ad = dev(A)
+    if fp8_act:
+        qa = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+        sa = torch.empty(1, dtype=torch.float32, device="cuda")
+        wq = torch.zeros(vla.vla_quantize_act_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+        vla.vla_quantize_act(Ad, qa, sa, wq, wq.numel(), M, K)
+        y, _ = run_gemm(qa, w, M, s_a=sa)
+        ref_qa, ref_sa = oracle.quantize_act(A)
+        assert np.array_equal(host(qa).reshape(M, K), ref_qa)
+        a_val = oracle.decode(ref_qa, OCP) * np.float64(ref_sa)
+    else:
+        y, _ = run_gemm(Ad, w, M)
+        a_val = bf16_f64(A)
+    rows = _sampled_rows(M, 24, 6600 + N)
+    ref, yabs = oracle.gemm(a_val[rows], w.w)
+    assert_gemm_close(y[rows], ref, yabs)
+    assert np.isfinite(bf16_f64(y)).all()
