@@ -60,6 +60,9 @@ def main():
     ap.add_argument("--cache", choices=["cold", "warm"], default="cold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy 8 times (scale reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -69,6 +72,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        src = torch.full((256 << 20,), 7, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "copies": 8}))
+        return
 
     import bf16_gemm_vla_amd as vla
     import synthetic
@@ -150,8 +162,11 @@ def main():
     us_call = ms_graph * 1000.0 / (2 * args.steps)
     bytes_step = alg_bytes_fp8w(*UP) + alg_bytes_fp8w(*DOWN)
     achieved = bytes_step / (ms_graph * 1e-3 / args.steps) / 1e9
+    floor_buf = torch.zeros(1, device=dev)
+    floor_us = time_graph(lambda i: floor_buf.fill_(1.0), args.steps) * 1000.0 / args.steps
     extra = {
         "us_per_call_eager": round(ms_eager * 1000.0 / (2 * args.steps), 3),
+        "graph_launch_floor_us": round(floor_us, 3),
         "weight_copies": copies,
     }
 
@@ -190,7 +205,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "extra": extra,
     }
@@ -313,6 +328,27 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
     out["dialect_reencode_GBps"] = round((2 * N * K + 8 * N) / (t_r * 1e-6) / 1e9, 1)
     out["dialect_pack_us"] = round(t_p, 2)
     return out
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "skinny_fp8_m50_pmc_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "bf16_gemm_vla_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the skinny kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs, scaled by a plain copy's counters; None if
+    the summary is missing or the kernel source changed since it was taken."""
+    import hashlib
+
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if kv.get("kernel_source_sha256") != sha:
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(np, synthetic, W_up, W_dn):
