@@ -51,6 +51,7 @@ struct GemmPlan {
     int ksplit;     // number of K chunks across workgroups
     int groups;     // N groups (grid x)
     int mblocks;    // M blocks (grid y of the wide kernel)
+    bool alds;      // skinny: stage activations through LDS
     bool ok;        // false when the shape exceeds the split-K counter space
 };
 
