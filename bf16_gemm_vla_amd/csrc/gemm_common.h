@@ -1,0 +1,159 @@
+// Pieces shared by the GEMM kernels: kernel arguments, the fused epilogues
+// (scale, bias, residual, GELU-tanh * up) and the cross-workgroup split-K
+// protocol.
+//
+// Cross-workgroup protocol: partials are written and read only with
+// device-coherent accesses (the sc1 cache policy of agent-scope atomic
+// stores and loads on gfx950, served at the level of the hierarchy every
+// XCD sees), and every wave waits for its stores to complete before the
+// workgroup's arrival is counted with an agent-scope atomic.  That is the
+// ordering a release/acquire pair provides for these accesses, without the
+// L2 write-back and invalidate a device-scope fence issues (~20 us per call
+// on MI355X, against a kernel of a few microseconds).
+#pragma once
+
+#include "vla_device.h"
+#include "vla_internal.h"
+
+namespace vla {
+namespace gemm_detail {
+
+struct KArgs {
+    const void* A;
+    const float* s_a;
+    const void* W;
+    const float* s_w;
+    const uint16_t* bias;
+    const uint16_t* resid;
+    uint16_t* Y;
+    uint16_t* gu;
+    uint32_t* tickets;
+    float* part;
+    uint32_t part_bytes;
+    int M, N, K;
+    int ksplit;
+    int groups;
+};
+
+// ------------------------------------------------------------- epilogue
+
+// Epilogue inputs of one output fragment (row m, output columns n..n+3),
+// loaded early so their latency overlaps the weight stream.
+struct EpiIn {
+    float4 s;       // weight scales (gate scales for the fused gate/up epilogue)
+    float4 su;      // up scales (fused gate/up epilogue)
+    uint2 bias;
+    uint2 resid;
+};
+
+__device__ __forceinline__ uint16_t lo16(uint32_t w) { return static_cast<uint16_t>(w & 0xFFFFu); }
+__device__ __forceinline__ uint16_t hi16(uint32_t w) { return static_cast<uint16_t>(w >> 16); }
+__device__ __forceinline__ uint2 pack4(const uint16_t* x) {
+    return make_uint2(x[0] | (static_cast<uint32_t>(x[1]) << 16), x[2] | (static_cast<uint32_t>(x[3]) << 16));
+}
+
+template <WType WT, Epi EPI>
+__device__ __forceinline__ EpiIn load_epi(const KArgs& a, int m, int n, bool with_resid) {
+    EpiIn e;
+    e.s = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    e.su = e.s;
+    e.bias = make_uint2(0, 0);
+    e.resid = make_uint2(0, 0);
+    if (WT == WType::FP8) e.s = *reinterpret_cast<const float4*>(a.s_w + n);
+    if (EPI == Epi::GELU_MUL) {
+        e.su = *reinterpret_cast<const float4*>(a.s_w + (a.N >> 1) + n);
+    } else {
+        if (a.bias) e.bias = *reinterpret_cast<const uint2*>(a.bias + n);
+        if (a.resid && with_resid) e.resid = *reinterpret_cast<const uint2*>(a.resid + static_cast<int64_t>(m) * a.N + n);
+    }
+    return e;
+}
+
+// y = v * scale (+ bias) -> bf16, then bf16(residual + y); four columns.
+template <AType AT, WType WT>
+__device__ __forceinline__ void store_plain(const KArgs& a, int m, int n, f32x4_t v, const EpiIn& e, float sa) {
+    const float sc[4] = {e.s.x * sa, e.s.y * sa, e.s.z * sa, e.s.w * sa};
+    const uint16_t b[4] = {lo16(e.bias.x), hi16(e.bias.x), lo16(e.bias.y), hi16(e.bias.y)};
+    uint16_t o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float y = (WT == WType::FP8 || AT == AType::FP8) ? v[r] * sc[r] : v[r];
+        if (a.bias) y += bf16_to_f32(b[r]);
+        o[r] = f32_to_bf16(y);
+    }
+    if (a.resid) {
+        const uint16_t rv[4] = {lo16(e.resid.x), hi16(e.resid.x), lo16(e.resid.y), hi16(e.resid.y)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16(bf16_to_f32(rv[r]) + bf16_to_f32(o[r]));
+    }
+    *reinterpret_cast<uint2*>(a.Y + static_cast<int64_t>(m) * a.N + n) = pack4(o);
+}
+
+// Gate values vg and up values vu for row m, gate columns n..n+3 (n < I).
+__device__ __forceinline__ void store_gelu(const KArgs& a, int m, int n, f32x4_t vg, f32x4_t vu, const EpiIn& e) {
+    const int I = a.N >> 1;
+    const float sgv[4] = {e.s.x, e.s.y, e.s.z, e.s.w}, suv[4] = {e.su.x, e.su.y, e.su.z, e.su.w};
+    uint16_t g[4], u[4], o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        g[r] = f32_to_bf16(vg[r] * sgv[r]);
+        u[r] = f32_to_bf16(vu[r] * suv[r]);
+        o[r] = f32_to_bf16(gelu_tanh(bf16_to_f32(g[r])) * bf16_to_f32(u[r]));
+    }
+    *reinterpret_cast<uint2*>(a.Y + static_cast<int64_t>(m) * I + n) = pack4(o);
+    if (a.gu) {
+        *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + n) = pack4(g);
+        *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + I + n) = pack4(u);
+    }
+}
+
+// Device-coherent 16-byte partial stores / loads.  They use the cache
+// policy of agent-scope atomic accesses (sc1), served at the level of the
+// hierarchy every XCD sees, through a buffer resource bounded to the
+// partial region (out-of-range offsets read zero and drop writes).
+constexpr int kCpolSC1 = 16;                 // cache-policy bit SC1
+constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit data format
+
+struct Coherent {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ Coherent(void* base, uint32_t bytes) : r(__builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, kRsrcWord3)) {}
+    __device__ void store(uint32_t off, f32x4_t v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kCpolSC1);
+    }
+    __device__ f32x4_t load(uint32_t off) const {
+        return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSC1));
+    }
+};
+
+// Split-K arrival, called by every thread after storing its partials with
+// Coherent::store.  Returns true in the one workgroup that arrives last for
+// `slot`; that workgroup then reads every partial with Coherent::load and
+// must call splitk_reset when done.
+__device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, int ksplit) {
+    __shared__ int s_last;
+    // wait until this wave's partial stores have completed (gfx9 counts
+    // stores in vmcnt); the barrier then orders every wave's stores before
+    // the arrival below
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(tickets + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == static_cast<uint32_t>(ksplit - 1)) ? 1 : 0;
+    }
+    __syncthreads();
+    return s_last != 0;
+}
+
+__device__ __forceinline__ void splitk_reset(uint32_t* tickets, int slot) {
+    if (threadIdx.x == 0) __hip_atomic_store(tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace gemm_detail
+
+// Wide kernel (gemm_wide.hip).  For the wide kernel GemmPlan::nt holds the
+// tile width BN (128 or 256).
+template <AType AT, WType WT, Epi EPI>
+hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStream_t s);
+size_t wide_part_bytes(const GemmPlan& p);
+
+}  // namespace vla

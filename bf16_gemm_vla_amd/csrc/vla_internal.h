@@ -58,8 +58,11 @@ struct GemmPlan {
 // The first kCounterBytes of every GEMM workspace hold the split-K arrival
 // counters (one uint32 per output tile group), at the same place for every
 // shape, so one zero-filled workspace can serve calls of different shapes.
+// Its last 4 KiB are never written: an always-zero page that out-of-range
+// lanes of the wide kernel load from.
 constexpr size_t kCounterBytes = 65536;
-constexpr int kMaxCounters = static_cast<int>(kCounterBytes / 4);
+constexpr size_t kZeroPageOffset = kCounterBytes - 4096;
+constexpr int kMaxCounters = static_cast<int>(kZeroPageOffset / 4);
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi);
 size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N);
