@@ -338,11 +338,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
     }
     // Wide kernel: 192-row blocks; 256-column tiles when they give enough
     // workgroups, else 128-column tiles and K split until ~256 workgroups
-    // (each split keeps at least 8 K tiles).
+    // (each split keeps at least 8 K tiles).  FP8 x FP8 runs 12 waves (3 per
+    // SIMD, 64x64 wave tiles) to hide its longer LDS operand reads; the bf16
+    // MFMA paths run 8 (96-row wave tiles, more operand reuse per LDS read).
     GemmPlan p{};
     p.kernel = 1;
     p.steps = 0;
-    p.waves = 8;
+    p.waves = (at == AType::FP8) ? 12 : 8;
+    p.wnw = 4;
     p.mblocks = static_cast<int>((M + 191) / 192);
     if (epi == Epi::GELU_MUL) {
         p.nt = 256;

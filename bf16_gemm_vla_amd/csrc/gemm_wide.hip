@@ -22,18 +22,20 @@
 // per stage (which lets a partial vmcnt wait keep later stages in flight).
 #include "gemm_common.h"
 
+#include <type_traits>
+
 namespace vla {
 namespace {
 
 using namespace gemm_detail;
 
 constexpr int kWideBM = 192;
-constexpr int kWideWaves = 8;
-constexpr int kWideThreads = kWideWaves * 64;
 constexpr int kArowBytes = 128;   // K bytes of one activation row per stage
 
-template <AType AT, WType WT, int BN>
+template <AType AT, WType WT, int BN, int WMW, int WNW>
 struct WideCfg {
+    static constexpr int WAVES = WMW * WNW;                           // WMW along M x WNW along N
+    static constexpr int THREADS = WAVES * 64;
     static constexpr int AB = (AT == AType::FP8) ? 1 : 2;            // activation bytes / element
     static constexpr int WLB = (WT == WType::FP8) ? 8 : 16;          // weight bytes per lane slot
     static constexpr int BK = kArowBytes / AB;                       // K elements per stage
@@ -42,14 +44,20 @@ struct WideCfg {
     static constexpr int WT_STRIDE = WT_BYTES + 128;                 // + bank padding
     static constexpr int A_BYTES = kWideBM * kArowBytes;             // 24 KiB
     static constexpr int W_BYTES = (BN / 16) * WT_STRIDE;
-    static constexpr int STAGE = A_BYTES + W_BYTES;
+    static constexpr int DUMMY = A_BYTES + W_BYTES;                  // 1 KiB sink for padding loads
+    static constexpr int STAGE = DUMMY + 1024;
     static constexpr int STAGES = (3 * STAGE <= 160 * 1024) ? 3 : 2;
-    static constexpr int WN = BN / 4;                                 // wave tile width
+    static constexpr int WN = BN / WNW;                               // wave tile width
     static constexpr int NSUB = WN / 32;
-    static constexpr int MSUB = 3;                                    // 96 rows per wave
-    // loads one wave issues per stage (all uniform): activations + weights
-    static constexpr int VM_PER_STAGE = (kWideBM / 8) / kWideWaves + (BN / 16) * (WT_BYTES / 1024) / kWideWaves;
-    static_assert((kWideBM / 8) % kWideWaves == 0 && ((BN / 16) * (WT_BYTES / 1024)) % kWideWaves == 0, "uniform issue");
+    static constexpr int WMR = kWideBM / WMW;                         // wave tile height
+    static constexpr int MSUB = WMR / 32;
+    // loads per wave per stage; instructions beyond the real count load the
+    // zero page into the sink, so every wave issues the same number
+    static constexpr int A_INSTR = kWideBM / 8;
+    static constexpr int W_INSTR = (BN / 16) * (WT_BYTES / 1024);
+    static constexpr int TA = (A_INSTR + WAVES - 1) / WAVES;
+    static constexpr int TW = (W_INSTR + WAVES - 1) / WAVES;
+    static constexpr int VM_PER_STAGE = TA + TW;
 };
 
 // Global weight tile (16 rows) of local tile tt in group g.
@@ -65,10 +73,10 @@ __device__ __forceinline__ int wide_wtile(int g, int tt, int N) {
     }
 }
 
-template <AType AT, WType WT, Epi EPI, int BN>
-__global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
-    using C = WideCfg<AT, WT, BN>;
-    static_assert(EPI == Epi::PLAIN || BN == 256, "the fused gate/up epilogue pairs two 32-column sub-tiles");
+template <AType AT, WType WT, Epi EPI, int BN, int WMW, int WNW>
+__global__ __launch_bounds__(WMW * WNW * 64) void wide_gemm_kernel(KArgs a) {
+    using C = WideCfg<AT, WT, BN, WMW, WNW>;
+    static_assert(EPI == Epi::PLAIN || (BN == 256 && WNW == 4), "the fused gate/up epilogue pairs two 32-column sub-tiles");
     // one LDS object per pipeline stage, so the compiler's wait insertion can
     // tell the buffer being read from the ones being filled
     __shared__ __attribute__((aligned(16))) uint8_t lds0[C::STAGE];
@@ -76,7 +84,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds2[C::STAGES == 3 ? C::STAGE : 16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / WNW, wn = wave % WNW;  // wave grid WMW x WNW
     const int g = blockIdx.x, mb = blockIdx.y, split = blockIdx.z;
     const int m0 = mb * kWideBM;
     const int ksteps = a.K >> 5;
@@ -90,37 +98,42 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
     // every wave issues the same number of loads per stage
     const uint8_t* zero_page = reinterpret_cast<const uint8_t*>(a.tickets) + kZeroPageOffset;
 
-    // ---- global -> LDS of K tile kt into stage buffer sa
-    auto issue = [&](int kt, uint8_t* sa) __attribute__((always_inline)) {
-        uint8_t* sw = sa + C::A_BYTES;
-        // activations: 24 instructions of 8 rows x 128 B
-#pragma unroll
-        for (int t = 0; t < kWideBM / 8 / kWideWaves; ++t) {
-            const int i = wave + t * kWideWaves;
+    // ---- global -> LDS: load number t (0 <= t < VM_PER_STAGE) of this wave
+    //      for K tile kt into stage buffer sa.  Loads t < TA carry activation
+    //      rows, the rest weight tiles.
+    auto load = [&](int kt, uint8_t* sa, int t) __attribute__((always_inline)) {
+        if (t < C::TA) {
+            // activations: A_INSTR instructions of 8 rows x 128 B
+            const int i = wave + t * C::WAVES;
             const int row = i * 8 + (lane >> 3), pos = lane & 7;
             const int c = pos ^ ((row >> 1) & 7);
             const int gm = m0 + row;
             const int64_t kel = static_cast<int64_t>(kt) * C::BK + c * (16 / C::AB);
-            const uint8_t* src = (gm < a.M && kel < a.K)
+            const bool real = i < C::A_INSTR;
+            const uint8_t* src = (real && gm < a.M && kel < a.K)
                 ? static_cast<const uint8_t*>(a.A) + (static_cast<int64_t>(gm) * a.K + kel) * C::AB
                 : zero_page + lane * 16;
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sa + i * 1024), 16, 0, 0);
-        }
-        // weights: per 16-row tile WT_BYTES contiguous bytes, 1 KiB per instruction
-        constexpr int PER_TILE = C::WT_BYTES / 1024;
-#pragma unroll
-        for (int t = 0; t < (BN / 16) * PER_TILE / kWideWaves; ++t) {
-            const int j = wave + t * kWideWaves;
-            const int tt = j / PER_TILE, p = j % PER_TILE;
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sa + (real ? i * 1024 : C::DUMMY)), 16, 0, 0);
+        } else {
+            // weights: per 16-row tile WT_BYTES contiguous bytes, 1 KiB per instruction
+            constexpr int PER_TILE = C::WT_BYTES / 1024;
+            uint8_t* sw = sa + C::A_BYTES;
+            const int j = wave + (t - C::TA) * C::WAVES;
+            const bool real = j < C::W_INSTR;
+            const int tt = real ? j / PER_TILE : 0, p = real ? j % PER_TILE : 0;
             const int gt = wide_wtile<EPI, BN>(g, tt, a.N);
             const int sb = p * 1024 + lane * 16;
             const int f = sb / (64 * C::WLB);
             const int k0 = kt * C::FRAGS + f;
-            const uint8_t* src = (gt < ntiles16 && k0 < ksteps)
+            const uint8_t* src = (real && gt < ntiles16 && k0 < ksteps)
                 ? static_cast<const uint8_t*>(a.W) + (static_cast<int64_t>(gt) * ksteps + kt * C::FRAGS) * 64 * C::WLB + sb
                 : zero_page + lane * 16;
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sw + tt * C::WT_STRIDE + p * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sw + (real ? tt * C::WT_STRIDE + p * 1024 : C::DUMMY - C::A_BYTES)), 16, 0, 0);
         }
+    };
+    auto issue = [&](int kt, uint8_t* sa) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < C::VM_PER_STAGE; ++t) load(kt, sa, t);
     };
 
     using Acc = __attribute__((ext_vector_type(16))) float;
@@ -132,12 +145,23 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
 
     const int l32 = lane & 31, g2 = lane >> 5;
     // ---- one stage of MFMAs from stage buffer sa
-    auto compute = [&](const uint8_t* sa) __attribute__((always_inline)) {
+    // While computing, the wave spreads the loads of the K tile kt_next into
+    // nxt over the K sub-steps (LOADS false: no loads), so a wave stalled on
+    // a full memory queue still has MFMAs issued around its loads.
+    auto compute = [&](const uint8_t* sa, int kt_next, uint8_t* nxt, auto LOADS) __attribute__((always_inline)) {
         const uint8_t* sw = sa + C::A_BYTES;
+        constexpr int NKS = (AT == AType::FP8) ? 2 : 4;
+        auto loads_of = [&](int ks) __attribute__((always_inline)) {
+            if constexpr (decltype(LOADS)::value) {
+#pragma unroll
+                for (int t = ks * C::VM_PER_STAGE / NKS; t < (ks + 1) * C::VM_PER_STAGE / NKS; ++t) load(kt_next, nxt, t);
+            }
+        };
         if constexpr (AT == AType::FP8) {
             // two 32x32x64 steps per stage
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                loads_of(ks);
                 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
                 i32x8_t wop[C::NSUB], aop[C::MSUB];
 #pragma unroll
@@ -152,7 +176,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
                 }
 #pragma unroll
                 for (int ms = 0; ms < C::MSUB; ++ms) {
-                    const int r = wm * 96 + ms * 32 + l32;
+                    const int r = wm * C::WMR + ms * 32 + l32;
                     const int c0 = 4 * ks + 2 * g2;
                     const int sw_ = (r >> 1) & 7;
                     u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(sa + r * kArowBytes + ((c0 ^ sw_) * 16));
@@ -169,6 +193,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
             // four 32x32x16 bf16 steps per stage
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
+                loads_of(ks);
                 bf16x8_t wop[C::NSUB], aop[C::MSUB];
 #pragma unroll
                 for (int ns = 0; ns < C::NSUB; ++ns) {
@@ -180,7 +205,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
                 }
 #pragma unroll
                 for (int ms = 0; ms < C::MSUB; ++ms) {
-                    const int r = wm * 96 + ms * 32 + l32;
+                    const int r = wm * C::WMR + ms * 32 + l32;
                     const int c = 2 * ks + g2;
                     aop[ms] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + r * kArowBytes + ((c ^ ((r >> 1) & 7)) * 16)));
                 }
@@ -206,14 +231,13 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
         __builtin_amdgcn_s_waitcnt(C::STAGES == 3 ? VM_KEEP1 : VM_ZERO);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        issue(kt_begin + i + C::STAGES - 1, nxt);
-        compute(cur);
+        compute(cur, kt_begin + i + C::STAGES - 1, nxt, std::true_type{});
     };
     auto tail = [&](const uint8_t* cur) __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(VM_ZERO);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        compute(cur);
+        compute(cur, 0, nullptr, std::false_type{});
     };
     if (nkt > 0) {
         issue(kt_begin, lds0);
@@ -242,10 +266,10 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
     if (a.ksplit > 1) {
         // partial layout: [split][mblock][group][NACC][512 threads] of f32x4
         const int64_t slot = static_cast<int64_t>(mb) * a.groups + g;
-        const int64_t per = static_cast<int64_t>(kWideThreads) * NACC;
+        const int64_t per = static_cast<int64_t>(C::THREADS) * NACC;
         const int64_t sstride = static_cast<int64_t>(gridDim.y) * a.groups * per;
         const Coherent part(a.part, a.part_bytes);
-        auto off = [&](int sp, int f) { return static_cast<uint32_t>((sp * sstride + slot * per + f * kWideThreads + tid) * 16); };
+        auto off = [&](int sp, int f) { return static_cast<uint32_t>((sp * sstride + slot * per + f * C::THREADS + tid) * 16); };
 #pragma unroll
         for (int ns = 0; ns < C::NSUB; ++ns)
 #pragma unroll
@@ -275,7 +299,7 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
     const float sa = (AT == AType::FP8) ? *a.s_a : 1.0f;
 #pragma unroll
     for (int ms = 0; ms < C::MSUB; ++ms) {
-        const int m = m0 + wm * 96 + ms * 32 + l32;
+        const int m = m0 + wm * C::WMR + ms * 32 + l32;
         if (m >= a.M) continue;
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
@@ -305,20 +329,34 @@ __global__ __launch_bounds__(kWideThreads) void wide_gemm_kernel(KArgs a) {
 }  // namespace
 
 size_t wide_part_bytes(const GemmPlan& p) {
-    const int nsub = p.nt / 4 / 32;   // p.nt holds BN for the wide kernel
-    return static_cast<size_t>(p.ksplit) * p.mblocks * p.groups * kWideThreads * (nsub * 3 * 4) * 16;
+    // p.nt = BN; per thread NSUB x MSUB x 4 f32x4
+    const int wmw = p.waves / p.wnw;
+    const int nsub = p.nt / p.wnw / 32, msub = kWideBM / wmw / 32;
+    return static_cast<size_t>(p.ksplit) * p.mblocks * p.groups * (p.waves * 64) * (nsub * msub * 4) * 16;
 }
 
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStream_t s) {
     const dim3 grid(p.groups, p.mblocks, p.ksplit);
-    if constexpr (EPI == Epi::GELU_MUL) {
-        wide_gemm_kernel<AT, WT, EPI, 256><<<grid, kWideThreads, 0, s>>>(ka);
-    } else {
-        if (p.nt == 256) wide_gemm_kernel<AT, WT, EPI, 256><<<grid, kWideThreads, 0, s>>>(ka);
-        else wide_gemm_kernel<AT, WT, EPI, 128><<<grid, kWideThreads, 0, s>>>(ka);
+#define VLA_WIDE(BN_, WMW_, WNW_)                                                             \
+    if (p.nt == BN_ && p.waves == WMW_ * WNW_ && p.wnw == WNW_) {                              \
+        wide_gemm_kernel<AT, WT, EPI, BN_, WMW_, WNW_><<<grid, WMW_ * WNW_ * 64, 0, s>>>(ka);  \
+        return hipGetLastError();                                                              \
     }
-    return hipGetLastError();
+    if constexpr (EPI == Epi::GELU_MUL) {
+        VLA_WIDE(256, 2, 4)
+        VLA_WIDE(256, 3, 4)
+    } else {
+        VLA_WIDE(256, 2, 4)
+        VLA_WIDE(256, 3, 4)
+        VLA_WIDE(128, 2, 4)
+        VLA_WIDE(128, 3, 4)
+        VLA_WIDE(256, 2, 2)
+        VLA_WIDE(128, 2, 2)
+        VLA_WIDE(128, 3, 2)
+    }
+#undef VLA_WIDE
+    return hipErrorInvalidValue;
 }
 
 template hipError_t launch_wide<AType::BF16, WType::FP8, Epi::PLAIN>(const gemm_detail::KArgs&, const GemmPlan&, hipStream_t);

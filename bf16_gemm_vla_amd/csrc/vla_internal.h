@@ -45,9 +45,10 @@ struct GemmProblem {
 // Launch plan chosen for a problem (host-side, deterministic per shape).
 struct GemmPlan {
     int kernel;     // 0 = skinny (M <= 64), 1 = wide
-    int nt;         // 16-column tiles per workgroup (skinny)
+    int nt;         // skinny: 16-column tiles per workgroup; wide: tile width BN
     int steps;      // K steps (of 32) per wave per workgroup chunk (skinny)
-    int waves;      // wavefronts per workgroup (skinny)
+    int waves;      // wavefronts per workgroup
+    int wnw;        // wide: wavefronts along N (the rest are along M)
     int ksplit;     // number of K chunks across workgroups
     int groups;     // N groups (grid x)
     int mblocks;    // M blocks (grid y of the wide kernel)
