@@ -69,9 +69,9 @@ __device__ __forceinline__ EpiIn load_epi(const KArgs& a, int m, int n, bool wit
     return e;
 }
 
-// y = v * scale (+ bias) -> bf16, then bf16(residual + y); four columns.
+// y = v * scale (+ bias) -> bf16 for four columns (before any residual).
 template <AType AT, WType WT>
-__device__ __forceinline__ void store_plain(const KArgs& a, int m, int n, f32x4_t v, const EpiIn& e, float sa) {
+__device__ __forceinline__ uint2 epi_plain4(const KArgs& a, f32x4_t v, const EpiIn& e, float sa) {
     const float sc[4] = {e.s.x * sa, e.s.y * sa, e.s.z * sa, e.s.w * sa};
     const uint16_t b[4] = {lo16(e.bias.x), hi16(e.bias.x), lo16(e.bias.y), hi16(e.bias.y)};
     uint16_t o[4];
@@ -81,17 +81,30 @@ __device__ __forceinline__ void store_plain(const KArgs& a, int m, int n, f32x4_
         if (a.bias) y += bf16_to_f32(b[r]);
         o[r] = f32_to_bf16(y);
     }
-    if (a.resid) {
-        const uint16_t rv[4] = {lo16(e.resid.x), hi16(e.resid.x), lo16(e.resid.y), hi16(e.resid.y)};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = f32_to_bf16(bf16_to_f32(rv[r]) + bf16_to_f32(o[r]));
-    }
-    *reinterpret_cast<uint2*>(a.Y + static_cast<int64_t>(m) * a.N + n) = pack4(o);
+    return pack4(o);
 }
 
-// Gate values vg and up values vu for row m, gate columns n..n+3 (n < I).
-__device__ __forceinline__ void store_gelu(const KArgs& a, int m, int n, f32x4_t vg, f32x4_t vu, const EpiIn& e) {
-    const int I = a.N >> 1;
+// bf16(residual + y) on two packed bf16 values.
+__device__ __forceinline__ uint32_t add_resid2(uint32_t y, uint32_t r) {
+    const uint16_t lo = f32_to_bf16(bf16_to_f32(lo16(r)) + bf16_to_f32(lo16(y)));
+    const uint16_t hi = f32_to_bf16(bf16_to_f32(hi16(r)) + bf16_to_f32(hi16(y)));
+    return lo | (static_cast<uint32_t>(hi) << 16);
+}
+
+// y = v * scale (+ bias) -> bf16, then bf16(residual + y); four columns.
+template <AType AT, WType WT>
+__device__ __forceinline__ void store_plain(const KArgs& a, int m, int n, f32x4_t v, const EpiIn& e, float sa) {
+    uint2 o = epi_plain4<AT, WT>(a, v, e, sa);
+    if (a.resid) {
+        o.x = add_resid2(o.x, e.resid.x);
+        o.y = add_resid2(o.y, e.resid.y);
+    }
+    *reinterpret_cast<uint2*>(a.Y + static_cast<int64_t>(m) * a.N + n) = o;
+}
+
+// act = bf16(gelu_tanh(g) * u) with g = bf16(vg * sg), u = bf16(vu * su);
+// four gate columns.  g and u are returned for the optional gate/up output.
+__device__ __forceinline__ uint2 epi_gelu4(f32x4_t vg, f32x4_t vu, const EpiIn& e, uint2& gp, uint2& up) {
     const float sgv[4] = {e.s.x, e.s.y, e.s.z, e.s.w}, suv[4] = {e.su.x, e.su.y, e.su.z, e.su.w};
     uint16_t g[4], u[4], o[4];
 #pragma unroll
@@ -100,10 +113,20 @@ __device__ __forceinline__ void store_gelu(const KArgs& a, int m, int n, f32x4_t
         u[r] = f32_to_bf16(vu[r] * suv[r]);
         o[r] = f32_to_bf16(gelu_tanh(bf16_to_f32(g[r])) * bf16_to_f32(u[r]));
     }
-    *reinterpret_cast<uint2*>(a.Y + static_cast<int64_t>(m) * I + n) = pack4(o);
+    gp = pack4(g);
+    up = pack4(u);
+    return pack4(o);
+}
+
+// Gate values vg and up values vu for row m, gate columns n..n+3 (n < I).
+__device__ __forceinline__ void store_gelu(const KArgs& a, int m, int n, f32x4_t vg, f32x4_t vu, const EpiIn& e) {
+    const int I = a.N >> 1;
+    uint2 g, u;
+    const uint2 o = epi_gelu4(vg, vu, e, g, u);
+    *reinterpret_cast<uint2*>(a.Y + static_cast<int64_t>(m) * I + n) = o;
     if (a.gu) {
-        *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + n) = pack4(g);
-        *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + I + n) = pack4(u);
+        *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + n) = g;
+        *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + I + n) = u;
     }
 }
 

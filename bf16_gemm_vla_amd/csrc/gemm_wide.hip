@@ -296,32 +296,76 @@ __global__ __launch_bounds__(WMW * WNW * 64) void wide_gemm_kernel(KArgs a) {
                 }
         splitk_reset(a.tickets, static_cast<int>(slot));
     }
+    // ---- output: one pass per 32-row sub-tile ms.  Each wave scales (and
+    //      biases, or applies GELU * up to) its accumulators in registers and
+    //      writes the bf16 results into a [WMW*32][OUT_W] LDS tile; then the
+    //      whole workgroup stores those rows as 16-byte column chunks, adding
+    //      the residual on the way, so every wave writes full row segments.
+    //      The passes alternate between two stage buffers: a wave writing
+    //      pass ms+2 has passed the barrier every wave reaches only after
+    //      storing pass ms.
+    constexpr int OUT_W = (EPI == Epi::PLAIN) ? BN : 128;   // output columns of the tile
+    constexpr int PR = WMW * 32;                             // rows per pass
+    constexpr int OSTRIDE = OUT_W * 2 + 16;                  // bytes per LDS row (+ bank padding)
+    constexpr int CPR = OUT_W / 8;                           // 16-byte chunks per row
+    static_assert(PR * OSTRIDE <= C::STAGE, "an output pass fits one stage buffer");
     const float sa = (AT == AType::FP8) ? *a.s_a : 1.0f;
+    const int outN = (EPI == Epi::PLAIN) ? a.N : (a.N >> 1);
+    __syncthreads();   // every wave has finished reading the stage buffers
 #pragma unroll
     for (int ms = 0; ms < C::MSUB; ++ms) {
+        uint8_t* ot = (ms & 1) ? lds1 : lds0;
         const int m = m0 + wm * C::WMR + ms * 32 + l32;
-        if (m >= a.M) continue;
+        uint8_t* orow = ot + (wm * 32 + l32) * OSTRIDE;
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
             const int nrow = 8 * rq + 4 * g2;    // first of 4 consecutive channels in the sub-tile
             if constexpr (EPI == Epi::PLAIN) {
 #pragma unroll
                 for (int ns = 0; ns < C::NSUB; ++ns) {
-                    const int n = g * BN + wn * C::WN + ns * 32 + nrow;
+                    const int nl = wn * C::WN + ns * 32 + nrow;
+                    const int n = g * BN + nl;
                     if (n >= a.N) continue;
                     const Acc& v = acc[ns][ms];
-                    store_plain<AT, WT>(a, m, n, f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]},
-                                        load_epi<WT, EPI>(a, m, n, true), sa);
+                    *reinterpret_cast<uint2*>(orow + nl * 2) =
+                        epi_plain4<AT, WT>(a, f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]},
+                                           load_epi<WT, EPI>(a, m, n, false), sa);
                 }
             } else {
-                const int n = g * 128 + wn * 32 + nrow;       // gate column
-                if (n >= (a.N >> 1)) continue;
+                const int nl = wn * 32 + nrow;
+                const int n = g * 128 + nl;        // gate column
+                if (n >= outN) continue;
                 const Acc& vg = acc[0][ms];
                 const Acc& vu = acc[1][ms];
-                store_gelu(a, m, n, f32x4_t{vg[4 * rq], vg[4 * rq + 1], vg[4 * rq + 2], vg[4 * rq + 3]},
-                           f32x4_t{vu[4 * rq], vu[4 * rq + 1], vu[4 * rq + 2], vu[4 * rq + 3]},
-                           load_epi<WT, EPI>(a, m, n, false));
+                uint2 gq, uq;
+                *reinterpret_cast<uint2*>(orow + nl * 2) =
+                    epi_gelu4(f32x4_t{vg[4 * rq], vg[4 * rq + 1], vg[4 * rq + 2], vg[4 * rq + 3]},
+                              f32x4_t{vu[4 * rq], vu[4 * rq + 1], vu[4 * rq + 2], vu[4 * rq + 3]},
+                              load_epi<WT, EPI>(a, m, n, false), gq, uq);
+                if (a.gu && m < a.M) {
+                    *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + n) = gq;
+                    *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + outN + n) = uq;
+                }
             }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = tid; c < PR * CPR; c += C::THREADS) {
+            const int row = c / CPR, ch = c % CPR;
+            const int gm = m0 + (row >> 5) * C::WMR + ms * 32 + (row & 31);
+            const int n = g * OUT_W + ch * 8;
+            if (gm >= a.M || n >= outN) continue;
+            uint4 v = *reinterpret_cast<const uint4*>(ot + row * OSTRIDE + ch * 16);
+            if constexpr (EPI == Epi::PLAIN) {
+                if (a.resid) {
+                    const uint4 r = *reinterpret_cast<const uint4*>(a.resid + static_cast<int64_t>(gm) * a.N + n);
+                    v.x = add_resid2(v.x, r.x);
+                    v.y = add_resid2(v.y, r.y);
+                    v.z = add_resid2(v.z, r.z);
+                    v.w = add_resid2(v.w, r.w);
+                }
+            }
+            *reinterpret_cast<uint4*>(a.Y + static_cast<int64_t>(gm) * outN + n) = v;
         }
     }
 }
@@ -345,15 +389,14 @@ hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStrea
     }
     if constexpr (EPI == Epi::GELU_MUL) {
         VLA_WIDE(256, 2, 4)
+    } else if constexpr (AT == AType::FP8) {
         VLA_WIDE(256, 3, 4)
+        VLA_WIDE(128, 3, 4)
+        VLA_WIDE(256, 2, 4)
+        VLA_WIDE(128, 2, 4)
     } else {
         VLA_WIDE(256, 2, 4)
-        VLA_WIDE(256, 3, 4)
         VLA_WIDE(128, 2, 4)
-        VLA_WIDE(128, 3, 4)
-        VLA_WIDE(256, 2, 2)
-        VLA_WIDE(128, 2, 2)
-        VLA_WIDE(128, 3, 2)
     }
 #undef VLA_WIDE
     return hipErrorInvalidValue;
