@@ -68,8 +68,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(const float* __
             uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
-                       (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+                w[i] = f32x2_to_bf16x2(v[2 * i], v[2 * i + 1]);
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Wq) + off) =
                 make_uint4(w[0], w[1], w[2], w[3]);
         } else {

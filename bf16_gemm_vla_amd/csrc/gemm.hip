@@ -336,23 +336,24 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
         }
         return skinny_plan(N, K, epi, nt, steps, waves, at == AType::BF16);
     }
-    // Wide kernel: 192-row blocks; 256-column tiles when they give enough
-    // workgroups, else 128-column tiles and K split until ~256 workgroups
-    // (each split keeps at least 8 K tiles).  FP8 x FP8 runs 12 waves (3 per
-    // SIMD, 64x64 wave tiles) to hide its longer LDS operand reads; the bf16
-    // MFMA paths run 8 (96-row wave tiles, more operand reuse per LDS read).
+    // Wide kernel: 192-row blocks of 4 waves; 256-column tiles when they
+    // give enough workgroups, else 128-column tiles and K split until ~256
+    // workgroups (each split keeps at least 8 stages of 64 K).  BF16 weights
+    // always take 128-column tiles (a 256-column stage would not fit the
+    // four-stage LDS ring).  The buffer resources address A and W with
+    // 32-bit offsets.
     GemmPlan p{};
     p.kernel = 1;
     p.steps = 0;
-    p.waves = (at == AType::FP8) ? 12 : 8;
-    p.wnw = 4;
+    p.waves = (at == AType::FP8) ? 4 : 8;
+    p.wnw = p.waves / 2;
     p.mblocks = static_cast<int>((M + 191) / 192);
     if (epi == Epi::GELU_MUL) {
         p.nt = 256;
         p.groups = static_cast<int>(std::max<int64_t>(1, (tiles / 2 + 7) / 8));
     } else {
         const int64_t g256 = (tiles + 15) / 16;
-        if (g256 * p.mblocks >= 192) {
+        if (wt == WType::FP8 && g256 * p.mblocks >= 192) {
             p.nt = 256;
             p.groups = static_cast<int>(g256);
         } else {
@@ -360,13 +361,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
             p.groups = static_cast<int>((tiles + 7) / 8);
         }
     }
-    const int64_t bk = (at == AType::FP8) ? 128 : 64;
-    const int64_t kt_total = (K + bk - 1) / bk;
+    const int64_t kt_total = (K + 63) / 64;
     const int64_t base = static_cast<int64_t>(p.groups) * p.mblocks;
     int ks = 1;
     while (base * ks < 256 && kt_total / (ks * 2) >= 8) ks *= 2;
     p.ksplit = ks;
-    p.ok = base <= kMaxCounters;
+    const int64_t a_bytes = M * K * (at == AType::FP8 ? 1 : 2);
+    const int64_t w_bytes = N * K * (wt == WType::FP8 ? 1 : 2);
+    p.ok = base <= kMaxCounters && a_bytes < (int64_t(1) << 31) && w_bytes < (int64_t(1) << 31);
     return p;
 }
 

@@ -48,9 +48,6 @@ struct EpiIn {
 
 __device__ __forceinline__ uint16_t lo16(uint32_t w) { return static_cast<uint16_t>(w & 0xFFFFu); }
 __device__ __forceinline__ uint16_t hi16(uint32_t w) { return static_cast<uint16_t>(w >> 16); }
-__device__ __forceinline__ uint2 pack4(const uint16_t* x) {
-    return make_uint2(x[0] | (static_cast<uint32_t>(x[1]) << 16), x[2] | (static_cast<uint32_t>(x[3]) << 16));
-}
 
 template <WType WT, Epi EPI>
 __device__ __forceinline__ EpiIn load_epi(const KArgs& a, int m, int n, bool with_resid) {
@@ -72,23 +69,26 @@ __device__ __forceinline__ EpiIn load_epi(const KArgs& a, int m, int n, bool wit
 // y = v * scale (+ bias) -> bf16 for four columns (before any residual).
 template <AType AT, WType WT>
 __device__ __forceinline__ uint2 epi_plain4(const KArgs& a, f32x4_t v, const EpiIn& e, float sa) {
-    const float sc[4] = {e.s.x * sa, e.s.y * sa, e.s.z * sa, e.s.w * sa};
-    const uint16_t b[4] = {lo16(e.bias.x), hi16(e.bias.x), lo16(e.bias.y), hi16(e.bias.y)};
-    uint16_t o[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float y = (WT == WType::FP8 || AT == AType::FP8) ? v[r] * sc[r] : v[r];
-        if (a.bias) y += bf16_to_f32(b[r]);
-        o[r] = f32_to_bf16(y);
+    const bool scaled = (WT == WType::FP8 || AT == AType::FP8);
+    float y[4] = {v[0], v[1], v[2], v[3]};
+    if (scaled) {
+        y[0] *= e.s.x * sa;
+        y[1] *= e.s.y * sa;
+        y[2] *= e.s.z * sa;
+        y[3] *= e.s.w * sa;
     }
-    return pack4(o);
+    if (a.bias) {
+        y[0] += bf16_to_f32(lo16(e.bias.x));
+        y[1] += bf16_to_f32(hi16(e.bias.x));
+        y[2] += bf16_to_f32(lo16(e.bias.y));
+        y[3] += bf16_to_f32(hi16(e.bias.y));
+    }
+    return make_uint2(f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3]));
 }
 
 // bf16(residual + y) on two packed bf16 values.
 __device__ __forceinline__ uint32_t add_resid2(uint32_t y, uint32_t r) {
-    const uint16_t lo = f32_to_bf16(bf16_to_f32(lo16(r)) + bf16_to_f32(lo16(y)));
-    const uint16_t hi = f32_to_bf16(bf16_to_f32(hi16(r)) + bf16_to_f32(hi16(y)));
-    return lo | (static_cast<uint32_t>(hi) << 16);
+    return f32x2_to_bf16x2(bf16_to_f32(lo16(r)) + bf16_to_f32(lo16(y)), bf16_to_f32(hi16(r)) + bf16_to_f32(hi16(y)));
 }
 
 // y = v * scale (+ bias) -> bf16, then bf16(residual + y); four columns.
@@ -105,17 +105,13 @@ __device__ __forceinline__ void store_plain(const KArgs& a, int m, int n, f32x4_
 // act = bf16(gelu_tanh(g) * u) with g = bf16(vg * sg), u = bf16(vu * su);
 // four gate columns.  g and u are returned for the optional gate/up output.
 __device__ __forceinline__ uint2 epi_gelu4(f32x4_t vg, f32x4_t vu, const EpiIn& e, uint2& gp, uint2& up) {
-    const float sgv[4] = {e.s.x, e.s.y, e.s.z, e.s.w}, suv[4] = {e.su.x, e.su.y, e.su.z, e.su.w};
-    uint16_t g[4], u[4], o[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        g[r] = f32_to_bf16(vg[r] * sgv[r]);
-        u[r] = f32_to_bf16(vu[r] * suv[r]);
-        o[r] = f32_to_bf16(gelu_tanh(bf16_to_f32(g[r])) * bf16_to_f32(u[r]));
-    }
-    gp = pack4(g);
-    up = pack4(u);
-    return pack4(o);
+    gp = make_uint2(f32x2_to_bf16x2(vg[0] * e.s.x, vg[1] * e.s.y), f32x2_to_bf16x2(vg[2] * e.s.z, vg[3] * e.s.w));
+    up = make_uint2(f32x2_to_bf16x2(vu[0] * e.su.x, vu[1] * e.su.y), f32x2_to_bf16x2(vu[2] * e.su.z, vu[3] * e.su.w));
+    const float a0 = gelu_tanh(bf16_to_f32(lo16(gp.x))) * bf16_to_f32(lo16(up.x));
+    const float a1 = gelu_tanh(bf16_to_f32(hi16(gp.x))) * bf16_to_f32(hi16(up.x));
+    const float a2 = gelu_tanh(bf16_to_f32(lo16(gp.y))) * bf16_to_f32(lo16(up.y));
+    const float a3 = gelu_tanh(bf16_to_f32(hi16(gp.y))) * bf16_to_f32(hi16(up.y));
+    return make_uint2(f32x2_to_bf16x2(a0, a1), f32x2_to_bf16x2(a2, a3));
 }
 
 // Gate values vg and up values vu for row m, gate columns n..n+3 (n < I).
@@ -152,8 +148,9 @@ struct Coherent {
 // Coherent::store.  Returns true in the one workgroup that arrives last for
 // `slot`; that workgroup then reads every partial with Coherent::load and
 // must call splitk_reset when done.
-__device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, int ksplit) {
-    __shared__ int s_last;
+// `flag` is one int of LDS that no wave touches between the two barriers.
+__device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, int ksplit, int* flag) {
+    int& s_last = *flag;
     // wait until this wave's partial stores have completed (gfx9 counts
     // stores in vmcnt); the barrier then orders every wave's stores before
     // the arrival below
@@ -165,6 +162,11 @@ __device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, 
     }
     __syncthreads();
     return s_last != 0;
+}
+
+__device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, int ksplit) {
+    __shared__ int s_flag;
+    return splitk_arrive_last(tickets, slot, ksplit, &s_flag);
 }
 
 __device__ __forceinline__ void splitk_reset(uint32_t* tickets, int slot) {

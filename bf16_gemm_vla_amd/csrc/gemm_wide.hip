@@ -1,25 +1,34 @@
 // Wide GEMM (M > 64) for gfx950.
 //
-// Output tile 192 (rows of A) x BN (weight rows, 128 or 256) per workgroup
-// of 8 waves arranged 2 x 4; each wave owns 96 x BN/4.  MFMA shapes with the
-// full gfx950 rate: v_mfma_f32_32x32x16_bf16 for bf16 activations (FP8
-// weights are converted to bf16 exactly in registers) and
+// Output tile 192 (rows of A) x BN (weight rows, 256 or 128) per workgroup
+// of 4 waves, one per SIMD, arranged 2 x 2; each wave owns a 96 x BN/2
+// tile (3 x BN/64 accumulators of 32 x 32).  MFMA shapes with the full
+// gfx950 rate: v_mfma_f32_32x32x16_bf16 for bf16 activations (FP8 weights
+// are converted to bf16 exactly in registers) and the scaled
 // v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit E8M0 scales) for
 // FP8 x FP8.  The packed weight tile is the MFMA "A" operand (32 output
 // channels), the activation tile the "B" operand (32 rows), so a lane's
 // accumulator holds runs of 4 consecutive output channels of one row.
 //
-// Both operands enter LDS through direct global->LDS loads, 1 KiB per wave
-// instruction, STAGES deep:
-//  * activations, row-major, 128 bytes of K per row per stage, with the
-//    16-byte chunk c of row r stored at position c ^ ((r >> 1) & 7) so the
-//    32-row fragment reads hit distinct banks;
-//  * weights, already in MFMA fragment order, copied as-is per 16-row tile
-//    with 128 bytes of padding between tiles.
-// Lanes whose source lies outside A or W load from an always-zero page at
-// the end of the workspace's counter region instead, so ragged M, N and K
-// tails contribute nothing and every wave issues the same number of loads
-// per stage (which lets a partial vmcnt wait keep later stages in flight).
+// Operands move global -> LDS with buffer loads that write LDS directly
+// (16 bytes per lane, 1 KiB per wave instruction), 64 K values per stage,
+// in a ring of four stage buffers:
+//  * activations row-major, 128 (bf16) or 64 (FP8) bytes of K per row, the
+//    16-byte chunks of each row XOR-swizzled so the 32-row operand reads hit
+//    distinct banks;
+//  * weights in their packed fragment order, one 1 KiB (FP8) or 2 KiB
+//    (bf16) block per 16-row tile; FP8 blocks of odd tiles have their
+//    128-byte halves swapped, so the two 16-row halves of a 32-row operand
+//    read fall in different banks.
+// Out-of-range rows, tiles and the ragged K tail fall outside the buffer
+// resource and load zeros, so every wave issues the same number of loads
+// per stage.  Each stage has one barrier, placed before the stage's last
+// MFMA step: it publishes the next stage (its loads were waited for with a
+// partial vmcnt that keeps the following stage in flight) and frees the
+// buffer read two stages ago, which the loads of stage i+3 then refill.
+// Operand fragments are double-buffered in registers, so the LDS reads of
+// step s+1 (and of the next stage's first step, right after the barrier)
+// overlap the MFMAs of step s.
 #include "gemm_common.h"
 
 #include <type_traits>
@@ -30,110 +39,209 @@ namespace {
 using namespace gemm_detail;
 
 constexpr int kWideBM = 192;
-constexpr int kArowBytes = 128;   // K bytes of one activation row per stage
+constexpr int kWideBK = 64;          // K elements per pipeline stage
+constexpr int kWideStages = 4;
+constexpr uint32_t kOOB = 0x80000000u;   // voffset beyond every resource's range
 
-template <AType AT, WType WT, int BN, int WMW, int WNW>
+template <AType AT, WType WT, int BN, int WNW>
 struct WideCfg {
-    static constexpr int WAVES = WMW * WNW;                           // WMW along M x WNW along N
-    static constexpr int THREADS = WAVES * 64;
-    static constexpr int AB = (AT == AType::FP8) ? 1 : 2;            // activation bytes / element
-    static constexpr int WLB = (WT == WType::FP8) ? 8 : 16;          // weight bytes per lane slot
-    static constexpr int BK = kArowBytes / AB;                       // K elements per stage
-    static constexpr int FRAGS = BK / 32;                            // 16x32 fragments per tile row
-    static constexpr int WT_BYTES = FRAGS * 64 * WLB;                // one 16-row tile per stage
-    static constexpr int WT_STRIDE = WT_BYTES + 128;                 // + bank padding
-    static constexpr int A_BYTES = kWideBM * kArowBytes;             // 24 KiB
-    static constexpr int W_BYTES = (BN / 16) * WT_STRIDE;
-    static constexpr int DUMMY = A_BYTES + W_BYTES;                  // 1 KiB sink for padding loads
-    static constexpr int STAGE = DUMMY + 1024;
-    static constexpr int STAGES = (3 * STAGE <= 160 * 1024) ? 3 : 2;
-    static constexpr int WN = BN / WNW;                               // wave tile width
+    static constexpr int WAVES = 2 * WNW;                       // 2 along M x WNW along N
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int AB = (AT == AType::FP8) ? 1 : 2;       // activation bytes / element
+    static constexpr int WLB = (WT == WType::FP8) ? 8 : 16;     // weight bytes per lane slot
+    static constexpr int KMF = (AT == AType::FP8) ? 64 : 16;    // K of one MFMA
+    static constexpr int NKS = kWideBK / KMF;                   // MFMA steps per stage
+    static constexpr int ARB = kWideBK * AB;                    // A bytes per row per stage
+    static constexpr int CPR = ARB / 16;                        // 16-byte chunks per A row
+    static constexpr int RPI = 1024 / ARB;                      // A rows per load instruction
+    static constexpr int WTB = (kWideBK / 32) * 64 * WLB;       // W bytes per 16-row tile per stage
+    static constexpr int A_BYTES = kWideBM * ARB;
+    static constexpr int W_BYTES = (BN / 16) * WTB;
+    static constexpr int STAGE = A_BYTES + W_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024;
+    static constexpr int W_LOADS = W_BYTES / 1024;
+    static constexpr int LA = A_LOADS / WAVES;                  // activation loads per wave per stage
+    static constexpr int L = (A_LOADS + W_LOADS) / WAVES;       // loads per wave per stage
+    static constexpr int MSUB = 3;                              // 96-row wave tile
+    static constexpr int WN = BN / WNW;                         // wave tile width
     static constexpr int NSUB = WN / 32;
-    static constexpr int WMR = kWideBM / WMW;                         // wave tile height
-    static constexpr int MSUB = WMR / 32;
-    // loads per wave per stage; instructions beyond the real count load the
-    // zero page into the sink, so every wave issues the same number
-    static constexpr int A_INSTR = kWideBM / 8;
-    static constexpr int W_INSTR = (BN / 16) * (WT_BYTES / 1024);
-    static constexpr int TA = (A_INSTR + WAVES - 1) / WAVES;
-    static constexpr int TW = (W_INSTR + WAVES - 1) / WAVES;
-    static constexpr int VM_PER_STAGE = TA + TW;
+    static_assert(A_LOADS % WAVES == 0 && W_LOADS % WAVES == 0, "loads split evenly over the waves");
+    static_assert(kWideStages * STAGE <= 160 * 1024, "the stage ring fits the LDS");
+    static_assert(L <= 15, "the partial vmcnt wait fits its field");
 };
 
-// Global weight tile (16 rows) of local tile tt in group g.
-template <Epi EPI, int BN>
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (lgkmcnt and expcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Global 16-row weight tile held in LDS tile slot tt of group g, or -1 when
+// the slot lies past the weight matrix.  For the fused gate/up epilogue
+// wave wn owns slots wn*WN/16 .. +WN/16-1 holding WN/32 sub-tiles of 32
+// rows: the first half are gate columns g*BN/2 + wn*WN/2 + ns*32 .. +31,
+// the second half the matching up columns.
+template <Epi EPI, int BN, int WN>
 __device__ __forceinline__ int wide_wtile(int g, int tt, int N) {
+    const int ntiles = N >> 4;
     if constexpr (EPI == Epi::PLAIN) {
-        return g * (BN / 16) + tt;
+        const int t = g * (BN / 16) + tt;
+        return t < ntiles ? t : -1;
     } else {
-        // wave wn holds gate columns g*128 + wn*32 .. +31 (sub-tile 0) and
-        // the matching up columns (sub-tile 1): local rows wn*64 + nsub*32 + r
-        const int wn = tt >> 2, nsub = (tt >> 1) & 1, h = tt & 1;
-        return (nsub ? (N >> 5) : 0) + g * 8 + wn * 2 + h;
+        constexpr int HALF = WN / 64;   // gate sub-tiles per wave
+        const int gates = N >> 5;       // gate tiles
+        const int wn = tt / (WN / 16), q = tt % (WN / 16), ns = q >> 1, h = q & 1;
+        const int gt = g * (BN / 32) + wn * (WN / 32) + (ns % HALF) * 2 + h;
+        if (gt >= gates) return -1;
+        return ns < HALF ? gt : gates + gt;
     }
 }
 
-template <AType AT, WType WT, Epi EPI, int BN, int WMW, int WNW>
-__global__ __launch_bounds__(WMW * WNW * 64) void wide_gemm_kernel(KArgs a) {
-    using C = WideCfg<AT, WT, BN, WMW, WNW>;
-    static_assert(EPI == Epi::PLAIN || (BN == 256 && WNW == 4), "the fused gate/up epilogue pairs two 32-column sub-tiles");
-    // one LDS object per pipeline stage, so the compiler's wait insertion can
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+// 16 bytes per lane from a buffer resource straight into LDS at
+// lds + 16 * lane (lds is wave-uniform); offsets past the resource read 0.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Operand fragments of one MFMA step for one wave.
+template <AType AT, WType WT, int MSUB, int NSUB>
+struct Frags;
+template <WType WT, int MSUB, int NSUB>
+struct Frags<AType::BF16, WT, MSUB, NSUB> {
+    u32x4_t a[MSUB];
+    typename std::conditional<WT == WType::FP8, u32x2_t, u32x4_t>::type w[NSUB];   // as read from LDS
+    bf16x8_t wb[NSUB];                                                             // MFMA operands
+};
+template <WType WT, int MSUB, int NSUB>
+struct Frags<AType::FP8, WT, MSUB, NSUB> {
+    u32x4_t a[MSUB][2];
+    u32x2_t w[NSUB][4];
+};
+
+template <AType AT, WType WT, Epi EPI, int BN, int WNW>
+__global__ __launch_bounds__(128 * WNW) __attribute__((amdgpu_waves_per_eu(WNW / 2, WNW / 2)))
+void wide_gemm_kernel(KArgs a) {
+    using C = WideCfg<AT, WT, BN, WNW>;
+    using F = Frags<AT, WT, C::MSUB, C::NSUB>;
+    static_assert(EPI == Epi::PLAIN || (C::NSUB % 2 == 0 && AT == AType::BF16 && WT == WType::FP8),
+                  "the fused gate/up epilogue pairs gate and up sub-tiles within a wave");
+    // one LDS object per stage buffer, so the compiler's wait insertion can
     // tell the buffer being read from the ones being filled
     __shared__ __attribute__((aligned(16))) uint8_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[C::STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t lds2[C::STAGES == 3 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[C::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t lds3[C::STAGE];
+    uint8_t* const bufs[4] = {lds0, lds1, lds2, lds3};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WNW, wn = wave % WNW;  // wave grid WMW x WNW
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS destinations in SGPRs
+    const int wm = wave / WNW, wn = wave % WNW;
+    const int l32 = lane & 31, g2 = lane >> 5;
     const int g = blockIdx.x, mb = blockIdx.y, split = blockIdx.z;
     const int m0 = mb * kWideBM;
     const int ksteps = a.K >> 5;
-    const int ntiles16 = a.N >> 4;
-    const int kt_total = (a.K + C::BK - 1) / C::BK;
+    const int kt_total = (a.K + kWideBK - 1) / kWideBK;
     const int kt_per = (kt_total + a.ksplit - 1) / a.ksplit;
     const int kt_begin = split * kt_per;
     const int kt_end = min(kt_total, kt_begin + kt_per);
     const int nkt = max(0, kt_end - kt_begin);
-    // out-of-range lanes load from an always-zero page of the workspace, so
-    // every wave issues the same number of loads per stage
-    const uint8_t* zero_page = reinterpret_cast<const uint8_t*>(a.tickets) + kZeroPageOffset;
 
-    // ---- global -> LDS: load number t (0 <= t < VM_PER_STAGE) of this wave
-    //      for K tile kt into stage buffer sa.  Loads t < TA carry activation
-    //      rows, the rest weight tiles.
-    auto load = [&](int kt, uint8_t* sa, int t) __attribute__((always_inline)) {
-        if (t < C::TA) {
-            // activations: A_INSTR instructions of 8 rows x 128 B
-            const int i = wave + t * C::WAVES;
-            const int row = i * 8 + (lane >> 3), pos = lane & 7;
-            const int c = pos ^ ((row >> 1) & 7);
+    // buffer resources bounded to A and W: loads past the end read zero
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(a.A), 0, a.M * a.K * C::AB, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(a.W), 0, ksteps * (a.N >> 4) * 64 * C::WLB, kRsrcWord3);
+
+    // ---- per-lane source offsets of this wave's L loads per stage (without
+    //      the stage term) and the K position each covers (ragged-K mask).
+    //      Load t of wave w is instruction q = w + 4t of the stage; it fills
+    //      LDS bytes q*1024 .. +1023 of the stage buffer (A first, then W).
+    uint32_t voff[C::L], voffT[C::L];   // voffT: the same for the ragged last K tile
+    const int krem = a.K - (kt_total - 1) * kWideBK;    // K values in the last K tile (32 or 64)
+#pragma unroll
+    for (int t = 0; t < C::L; ++t) {
+        const int q = wave + C::WAVES * t;
+        bool in_tail;   // does this lane's chunk lie within the last K tile's krem values?
+        if (t < C::LA) {
+            const int row = q * C::RPI + lane / C::CPR, pos = lane % C::CPR;
+            const int c = (C::CPR == 8) ? (pos ^ ((row >> 1) & 7)) : (pos ^ ((row >> 2) & 3));
             const int gm = m0 + row;
-            const int64_t kel = static_cast<int64_t>(kt) * C::BK + c * (16 / C::AB);
-            const bool real = i < C::A_INSTR;
-            const uint8_t* src = (real && gm < a.M && kel < a.K)
-                ? static_cast<const uint8_t*>(a.A) + (static_cast<int64_t>(gm) * a.K + kel) * C::AB
-                : zero_page + lane * 16;
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sa + (real ? i * 1024 : C::DUMMY)), 16, 0, 0);
+            voff[t] = gm < a.M ? static_cast<uint32_t>((gm * a.K) * C::AB + c * 16) : kOOB;
+            in_tail = c * (16 / C::AB) < krem;
         } else {
-            // weights: per 16-row tile WT_BYTES contiguous bytes, 1 KiB per instruction
-            constexpr int PER_TILE = C::WT_BYTES / 1024;
-            uint8_t* sw = sa + C::A_BYTES;
-            const int j = wave + (t - C::TA) * C::WAVES;
-            const bool real = j < C::W_INSTR;
-            const int tt = real ? j / PER_TILE : 0, p = real ? j % PER_TILE : 0;
-            const int gt = wide_wtile<EPI, BN>(g, tt, a.N);
-            const int sb = p * 1024 + lane * 16;
-            const int f = sb / (64 * C::WLB);
-            const int k0 = kt * C::FRAGS + f;
-            const uint8_t* src = (real && gt < ntiles16 && k0 < ksteps)
-                ? static_cast<const uint8_t*>(a.W) + (static_cast<int64_t>(gt) * ksteps + kt * C::FRAGS) * 64 * C::WLB + sb
-                : zero_page + lane * 16;
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sw + (real ? tt * C::WT_STRIDE + p * 1024 : C::DUMMY - C::A_BYTES)), 16, 0, 0);
+            const int j = q - C::A_LOADS;
+            constexpr int PER_TILE = C::WTB / 1024;
+            const int tt = j / PER_TILE, h = j % PER_TILE;
+            const int gt = wide_wtile<EPI, BN, C::WN>(g, tt, a.N);
+            const int chunk = (WT == WType::FP8) ? (lane ^ (8 * (tt & 1))) : lane;
+            const int sb = h * 1024 + chunk * 16;               // byte within the tile's stage block
+            voff[t] = gt >= 0 ? static_cast<uint32_t>(gt * ksteps * 64 * C::WLB + sb) : kOOB;
+            in_tail = (sb / (64 * C::WLB)) * 32 < krem;         // packed fragment within the tile
+        }
+        voffT[t] = in_tail ? voff[t] : kOOB;
+    }
+    // Loads of a stage past the range (real == false) are pushed outside the
+    // resources through the scalar offset: they only write zeros into a free
+    // buffer, which keeps every stage's load count and wait identical.
+    auto issue = [&](int kt, uint8_t* buf, bool real) __attribute__((always_inline)) {
+        const bool ktail = kt == kt_total - 1;                  // uniform
+        const int sA = real ? kt * C::ARB : static_cast<int>(kOOB);
+        const int sW = real ? kt * C::WTB : static_cast<int>(kOOB);
+#pragma unroll
+        for (int t = 0; t < C::L; ++t) {
+            buffer_load_lds16(t < C::LA ? rA : rW, buf + (wave + C::WAVES * t) * 1024, ktail ? voffT[t] : voff[t],
+                              t < C::LA ? sA : sW);
         }
     };
-    auto issue = [&](int kt, uint8_t* sa) __attribute__((always_inline)) {
+
+    // ---- LDS operand addresses (byte offsets within a stage buffer)
+    int aoff, woff;
+    if constexpr (AT == AType::BF16) {
+        // row r = wm*96 + ms*32 + l32 (+ ms*4096 at read time); chunk 2ks + g2
+        // at position chunk ^ ((r >> 1) & 7); bits 1..3 of r come from l32
+        const int swz = (l32 >> 1) & 7;
+        aoff = (wm * 96 + l32) * 128 + (((g2 ^ swz) & 1) * 16);
+        (void)swz;
+    } else {
+        aoff = (wm * 96 + l32) * 64;
+    }
+    if constexpr (WT == WType::FP8) {
+        const int odd = (l32 >> 4) & 1;
+        woff = C::A_BYTES + ((wn * C::WN) >> 4) * 1024 + odd * 1024 + (l32 & 15) * 8 +
+               ((AT == AType::BF16) ? ((g2 ^ odd) * 128) : (g2 * 512));
+    } else {
+        woff = C::A_BYTES + ((wn * C::WN) >> 4) * 2048 + (l32 >> 4) * 2048 + (l32 & 15) * 16 + g2 * 256;
+    }
+    const int swzA = (AT == AType::BF16) ? ((l32 >> 1) & 7) : ((l32 >> 2) & 3);
+    const int oddW = (l32 >> 4) & 1;
+
+    auto read_step = [&](const uint8_t* buf, int ks, F& f) __attribute__((always_inline)) {
+        if constexpr (AT == AType::BF16) {
+            // chunk (2ks + g2) ^ swz = ((ks ^ (swz >> 1)) << 1) | (g2 ^ (swz & 1))
+            const int hi = ((ks ^ (swzA >> 1)) << 1) * 16;
 #pragma unroll
-        for (int t = 0; t < C::VM_PER_STAGE; ++t) load(kt, sa, t);
+            for (int ms = 0; ms < C::MSUB; ++ms)
+                f.a[ms] = *reinterpret_cast<const u32x4_t*>(buf + aoff + ms * 32 * 128 + hi);
+#pragma unroll
+            for (int ns = 0; ns < C::NSUB; ++ns) {
+                if constexpr (WT == WType::FP8)
+                    f.w[ns] = *reinterpret_cast<const u32x2_t*>(buf + woff + ns * 2 * 1024 + ks * 256);
+                else
+                    f.w[ns] = *reinterpret_cast<const u32x4_t*>(buf + woff + ns * 2 * 2048 + ks * 512);
+            }
+        } else {
+            const int p0 = ((2 * g2) ^ swzA) * 16, p1 = ((2 * g2 + 1) ^ swzA) * 16;
+#pragma unroll
+            for (int ms = 0; ms < C::MSUB; ++ms) {
+                f.a[ms][0] = *reinterpret_cast<const u32x4_t*>(buf + aoff + ms * 32 * 64 + p0);
+                f.a[ms][1] = *reinterpret_cast<const u32x4_t*>(buf + aoff + ms * 32 * 64 + p1);
+            }
+#pragma unroll
+            for (int ns = 0; ns < C::NSUB; ++ns)
+#pragma unroll
+                for (int k1 = 0; k1 < 4; ++k1)
+                    f.w[ns][k1] = *reinterpret_cast<const u32x2_t*>(buf + woff + ns * 2 * 1024 + ((k1 ^ oddW) * 128));
+        }
     };
 
     using Acc = __attribute__((ext_vector_type(16))) float;
@@ -143,128 +251,146 @@ __global__ __launch_bounds__(WMW * WNW * 64) void wide_gemm_kernel(KArgs a) {
 #pragma unroll
         for (int j = 0; j < C::MSUB; ++j) acc[i][j] = Acc{};
 
-    const int l32 = lane & 31, g2 = lane >> 5;
-    // ---- one stage of MFMAs from stage buffer sa
-    // While computing, the wave spreads the loads of the K tile kt_next into
-    // nxt over the K sub-steps (LOADS false: no loads), so a wave stalled on
-    // a full memory queue still has MFMAs issued around its loads.
-    auto compute = [&](const uint8_t* sa, int kt_next, uint8_t* nxt, auto LOADS) __attribute__((always_inline)) {
-        const uint8_t* sw = sa + C::A_BYTES;
-        constexpr int NKS = (AT == AType::FP8) ? 2 : 4;
-        auto loads_of = [&](int ks) __attribute__((always_inline)) {
-            if constexpr (decltype(LOADS)::value) {
+    // weight operands as bf16 (an exact conversion for FP8 weights)
+    auto convert = [&](F& f) __attribute__((always_inline)) {
+        if constexpr (AT == AType::BF16) {
 #pragma unroll
-                for (int t = ks * C::VM_PER_STAGE / NKS; t < (ks + 1) * C::VM_PER_STAGE / NKS; ++t) load(kt_next, nxt, t);
+            for (int ns = 0; ns < C::NSUB; ++ns) {
+                if constexpr (WT == WType::FP8) f.wb[ns] = ocp8_to_bf16x8(f.w[ns]);
+                else f.wb[ns] = as_bf16x8(f.w[ns]);
             }
-        };
-        if constexpr (AT == AType::FP8) {
-            // two 32x32x64 steps per stage
+        }
+    };
+    // MFMAs number lo .. hi-1 of a step, in the order (ns, ms)
+    auto mfmas = [&](const F& f, int lo, int hi) __attribute__((always_inline)) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                loads_of(ks);
-                typedef __attribute__((ext_vector_type(8))) int i32x8_t;
-                i32x8_t wop[C::NSUB], aop[C::MSUB];
+        for (int ns = 0; ns < C::NSUB; ++ns) {
 #pragma unroll
-                for (int ns = 0; ns < C::NSUB; ++ns) {
-                    const int nl = wn * C::WN + ns * 32 + l32;
-                    const uint8_t* base = sw + (nl >> 4) * C::WT_STRIDE + ((2 * ks + g2) * 64 + (nl & 15)) * 8;
-                    u32x2_t q0 = *reinterpret_cast<const u32x2_t*>(base);
-                    u32x2_t q1 = *reinterpret_cast<const u32x2_t*>(base + 16 * 8);
-                    u32x2_t q2 = *reinterpret_cast<const u32x2_t*>(base + 32 * 8);
-                    u32x2_t q3 = *reinterpret_cast<const u32x2_t*>(base + 48 * 8);
-                    wop[ns] = i32x8_t{(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y, (int)q2.x, (int)q2.y, (int)q3.x, (int)q3.y};
+            for (int ms = 0; ms < C::MSUB; ++ms) {
+                const int idx = ns * C::MSUB + ms;
+                if (idx < lo || idx >= hi) continue;
+                if constexpr (AT == AType::BF16) {
+                    acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.wb[ns], as_bf16x8(f.a[ms]), acc[ns][ms], 0, 0, 0);
+                } else {
+                    const i32x8_t wop = {(int)f.w[ns][0].x, (int)f.w[ns][0].y, (int)f.w[ns][1].x, (int)f.w[ns][1].y,
+                                         (int)f.w[ns][2].x, (int)f.w[ns][2].y, (int)f.w[ns][3].x, (int)f.w[ns][3].y};
+                    const i32x8_t aop = {(int)f.a[ms][0].x, (int)f.a[ms][0].y, (int)f.a[ms][0].z, (int)f.a[ms][0].w,
+                                         (int)f.a[ms][1].x, (int)f.a[ms][1].y, (int)f.a[ms][1].z, (int)f.a[ms][1].w};
+                    acc[ns][ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop, aop, acc[ns][ms], 0, 0, 0, 127, 0, 127);
                 }
-#pragma unroll
-                for (int ms = 0; ms < C::MSUB; ++ms) {
-                    const int r = wm * C::WMR + ms * 32 + l32;
-                    const int c0 = 4 * ks + 2 * g2;
-                    const int sw_ = (r >> 1) & 7;
-                    u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(sa + r * kArowBytes + ((c0 ^ sw_) * 16));
-                    u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(sa + r * kArowBytes + (((c0 + 1) ^ sw_) * 16));
-                    aop[ms] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-                }
-#pragma unroll
-                for (int ns = 0; ns < C::NSUB; ++ns)
-#pragma unroll
-                    for (int ms = 0; ms < C::MSUB; ++ms)
-                        acc[ns][ms] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[ns], aop[ms], acc[ns][ms], 0, 0, 0, 127, 0, 127);
-            }
-        } else {
-            // four 32x32x16 bf16 steps per stage
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                loads_of(ks);
-                bf16x8_t wop[C::NSUB], aop[C::MSUB];
-#pragma unroll
-                for (int ns = 0; ns < C::NSUB; ++ns) {
-                    const int nl = wn * C::WN + ns * 32 + l32;
-                    const int k1 = 2 * (ks & 1) + g2;
-                    const uint8_t* p = sw + (nl >> 4) * C::WT_STRIDE + (((ks >> 1) * 64 + 16 * k1 + (nl & 15)) * C::WLB);
-                    if constexpr (WT == WType::FP8) wop[ns] = ocp8_to_bf16x8(*reinterpret_cast<const u32x2_t*>(p));
-                    else wop[ns] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(p));
-                }
-#pragma unroll
-                for (int ms = 0; ms < C::MSUB; ++ms) {
-                    const int r = wm * C::WMR + ms * 32 + l32;
-                    const int c = 2 * ks + g2;
-                    aop[ms] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + r * kArowBytes + ((c ^ ((r >> 1) & 7)) * 16)));
-                }
-#pragma unroll
-                for (int ns = 0; ns < C::NSUB; ++ns)
-#pragma unroll
-                    for (int ms = 0; ms < C::MSUB; ++ms)
-                        acc[ns][ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[ns], aop[ms], acc[ns][ms], 0, 0, 0);
             }
         }
     };
 
-    // ---- pipeline: STAGES-1 K tiles in flight ahead of the one being computed.
-    // Tile i lives in buffer i % STAGES.  Every step issues one tile (tiles
-    // past the split's range load zeros or unused data, never computed), so
-    // each wave has exactly VM_PER_STAGE loads per tile outstanding and a
-    // partial vmcnt wait keeps the next tile in flight.  The barrier after
-    // the wait makes every wave's loads of tile i visible and guarantees no
-    // wave still reads the buffer the step's issue overwrites.
-    constexpr int VM_KEEP1 = (C::VM_PER_STAGE & 15) | ((C::VM_PER_STAGE >> 4) << 14) | 0x0F70;  // vmcnt(VM)
-    constexpr int VM_ZERO = 0x0F70;                                                              // vmcnt(0)
-    auto step = [&](int i, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(C::STAGES == 3 ? VM_KEEP1 : VM_ZERO);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        compute(cur, kt_begin + i + C::STAGES - 1, nxt, std::true_type{});
-    };
-    auto tail = [&](const uint8_t* cur) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(VM_ZERO);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        compute(cur, 0, nullptr, std::false_type{});
-    };
-    if (nkt > 0) {
-        issue(kt_begin, lds0);
-        if constexpr (C::STAGES == 3) issue(kt_begin + 1, lds1);
-        const int full = nkt / C::STAGES;
-        for (int it = 0; it < full; ++it) {
-            const int i = it * C::STAGES;
-            if constexpr (C::STAGES == 3) {
-                step(i, lds0, lds2);
-                step(i + 1, lds1, lds0);
-                step(i + 2, lds2, lds1);
+    // ---- pipeline.  Stage i (K tile kt_begin + i) lives in buffer i % 4.
+    //      Before stage 0: stages 0..2 issued.  In stage i, before its last
+    //      MFMA step: wait until stage i+1 has landed (stage i+2 stays in
+    //      flight: at most L loads outstanding), barrier, read the first
+    //      fragments of stage i+1, issue stage i+3 into the buffer of stage
+    //      i-1.  Stages past the range are issued and read like the others
+    //      (zeros, never multiplied), so every stage runs the same code and
+    //      the waits are compile-time constants.
+    constexpr int S = kWideStages;
+    static_assert(S == 4, "the stage body is unrolled over a ring of four buffers");
+    //      Within a step the order is pinned: the next step's LDS reads go
+    //      out first, interleaved with the first half of the MFMAs, and the
+    //      next step's weight conversions fill the gaps of the second half.
+    //      The stage's last step issues half of its MFMAs before the barrier,
+    //      so the matrix pipe is busy while the waves meet.
+    constexpr int NM = C::NSUB * C::MSUB;        // MFMAs per step
+    constexpr int HALF = NM / 2;
+    F f0, f1;
+    auto stage = [&](auto UC, int i) __attribute__((always_inline)) {
+        constexpr int u = decltype(UC)::value;
+        const uint8_t* cur = bufs[u];
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            const bool odd = ((u * C::NKS + ks) & 1) != 0;
+            F& cf = odd ? f1 : f0;
+            F& of = odd ? f0 : f1;
+            if (ks + 1 < C::NKS) {
+                __builtin_amdgcn_sched_barrier(0);
+                read_step(cur, ks + 1, of);
+                mfmas(cf, 0, NM);
+                convert(of);
+#pragma unroll
+                for (int j = 0; j < HALF; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                }
+#pragma unroll
+                for (int j = HALF; j < NM; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             } else {
-                step(i, lds0, lds1);
-                step(i + 1, lds1, lds0);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(cf, 0, HALF);
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * C::L));
+                __builtin_amdgcn_s_barrier();
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __builtin_amdgcn_sched_barrier(0);
+                read_step(bufs[(u + 1) % S], 0, of);
+                issue(kt_begin + i + S - 1, bufs[(u + S - 1) % S], i + S - 1 < nkt);
+                mfmas(cf, HALF, NM);
+                convert(of);
+#pragma unroll
+                for (int j = HALF; j < NM; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads
+                    __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM loads
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        const int rem = nkt - full * C::STAGES;   // tiles left, already issued
-        if (rem > 0) tail(lds0);
-        if (rem > 1) tail(lds1);
+    };
+    if (nkt > 0) {
+#pragma unroll
+        for (int j = 0; j < S - 1; ++j) issue(kt_begin + j, bufs[j], j < nkt);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * C::L));
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        read_step(lds0, 0, f0);
+        convert(f0);
+        const int full = nkt & ~(S - 1);
+        for (int i0 = 0; i0 < full; i0 += S) {
+            stage(std::integral_constant<int, 0>{}, i0);
+            stage(std::integral_constant<int, 1>{}, i0 + 1);
+            stage(std::integral_constant<int, 2>{}, i0 + 2);
+            stage(std::integral_constant<int, 3>{}, i0 + 3);
+        }
+        const int rem = nkt - full;
+        if (rem > 0) stage(std::integral_constant<int, 0>{}, full);
+        if (rem > 1) stage(std::integral_constant<int, 1>{}, full + 1);
+        if (rem > 2) stage(std::integral_constant<int, 2>{}, full + 2);
     }
-    __builtin_amdgcn_s_waitcnt(VM_ZERO);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+    // ---- epilogue inputs (scales, bias; gate and up scales for the fused
+    //      epilogue) of this lane's output columns, all requested at once so
+    //      their latency is paid once, overlapping the split-K exchange.
+    constexpr int NE = (EPI == Epi::PLAIN) ? C::NSUB : C::NSUB / 2;
+    EpiIn ein[NE][4];
+#pragma unroll
+    for (int ns = 0; ns < NE; ++ns)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int nrow = 8 * rq + 4 * g2;
+            const int n = (EPI == Epi::PLAIN) ? g * BN + wn * C::WN + ns * 32 + nrow
+                                              : g * (BN / 2) + wn * (C::WN / 2) + ns * 32 + nrow;
+            if (n < ((EPI == Epi::PLAIN) ? a.N : (a.N >> 1))) ein[ns][rq] = load_epi<WT, EPI>(a, 0, n, false);
+            else ein[ns][rq] = EpiIn{};
+        }
+    const float sa = (AT == AType::FP8) ? *a.s_a : 1.0f;
 
     // ---- epilogue.  acc[ns][ms] register r: row (output channel) 8*(r/4) + 4*(lane/32) + r%4
     //      of the 32-column sub-tile, activation row lane%32 of the 32-row sub-tile.
     constexpr int NACC = C::NSUB * C::MSUB * 4;
     if (a.ksplit > 1) {
-        // partial layout: [split][mblock][group][NACC][512 threads] of f32x4
+        // partial layout: [split][mblock][group][NACC][256 threads] of f32x4
         const int64_t slot = static_cast<int64_t>(mb) * a.groups + g;
         const int64_t per = static_cast<int64_t>(C::THREADS) * NACC;
         const int64_t sstride = static_cast<int64_t>(gridDim.y) * a.groups * per;
@@ -279,7 +405,8 @@ __global__ __launch_bounds__(WMW * WNW * 64) void wide_gemm_kernel(KArgs a) {
                     const Acc& v = acc[ns][ms];
                     part.store(off(split, (ns * C::MSUB + ms) * 4 + rq), f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]});
                 }
-        if (!splitk_arrive_last(a.tickets, static_cast<int>(slot), a.ksplit)) return;
+        // the flag lives in stage buffer 0: every wave is past its last operand read
+        if (!splitk_arrive_last(a.tickets, static_cast<int>(slot), a.ksplit, reinterpret_cast<int*>(lds0))) return;
 #pragma unroll
         for (int ns = 0; ns < C::NSUB; ++ns)
 #pragma unroll
@@ -296,27 +423,26 @@ __global__ __launch_bounds__(WMW * WNW * 64) void wide_gemm_kernel(KArgs a) {
                 }
         splitk_reset(a.tickets, static_cast<int>(slot));
     }
-    // ---- output: one pass per 32-row sub-tile ms.  Each wave scales (and
-    //      biases, or applies GELU * up to) its accumulators in registers and
-    //      writes the bf16 results into a [WMW*32][OUT_W] LDS tile; then the
-    //      whole workgroup stores those rows as 16-byte column chunks, adding
-    //      the residual on the way, so every wave writes full row segments.
-    //      The passes alternate between two stage buffers: a wave writing
-    //      pass ms+2 has passed the barrier every wave reaches only after
-    //      storing pass ms.
-    constexpr int OUT_W = (EPI == Epi::PLAIN) ? BN : 128;   // output columns of the tile
-    constexpr int PR = WMW * 32;                             // rows per pass
-    constexpr int OSTRIDE = OUT_W * 2 + 16;                  // bytes per LDS row (+ bank padding)
-    constexpr int CPR = OUT_W / 8;                           // 16-byte chunks per row
-    static_assert(PR * OSTRIDE <= C::STAGE, "an output pass fits one stage buffer");
-    const float sa = (AT == AType::FP8) ? *a.s_a : 1.0f;
+    // ---- output: one pass per 32-row sub-tile ms (64 rows: both wm halves).
+    //      Each wave scales (and biases, or applies GELU * up to) its
+    //      accumulators in registers and writes the bf16 results into LDS
+    //      rows [32][OUT_W], wm half in its own stage buffer; then the whole
+    //      workgroup stores the pass as 16-byte row chunks, adding the
+    //      residual on the way.  Passes alternate between buffer pairs
+    //      (0, 1) and (2, 3): a wave writing pass ms+2 has passed the barrier
+    //      every wave reaches only after storing pass ms.
+    constexpr int OUT_W = (EPI == Epi::PLAIN) ? BN : BN / 2;  // output columns of the tile
+    constexpr int OSTRIDE = OUT_W * 2 + 16;                   // bytes per LDS row (+ bank padding)
+    constexpr int CPRO = OUT_W / 8;                           // 16-byte chunks per output row
+    static_assert(32 * OSTRIDE <= C::STAGE, "32 output rows fit one stage buffer");
     const int outN = (EPI == Epi::PLAIN) ? a.N : (a.N >> 1);
     __syncthreads();   // every wave has finished reading the stage buffers
 #pragma unroll
     for (int ms = 0; ms < C::MSUB; ++ms) {
-        uint8_t* ot = (ms & 1) ? lds1 : lds0;
-        const int m = m0 + wm * C::WMR + ms * 32 + l32;
-        uint8_t* orow = ot + (wm * 32 + l32) * OSTRIDE;
+        uint8_t* const pair0 = (ms & 1) ? lds2 : lds0;
+        uint8_t* const pair1 = (ms & 1) ? lds3 : lds1;
+        const int m = m0 + wm * 96 + ms * 32 + l32;
+        uint8_t* orow = (wm ? pair1 : pair0) + l32 * OSTRIDE;
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
             const int nrow = 8 * rq + 4 * g2;    // first of 4 consecutive channels in the sub-tile
@@ -329,33 +455,37 @@ __global__ __launch_bounds__(WMW * WNW * 64) void wide_gemm_kernel(KArgs a) {
                     const Acc& v = acc[ns][ms];
                     *reinterpret_cast<uint2*>(orow + nl * 2) =
                         epi_plain4<AT, WT>(a, f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]},
-                                           load_epi<WT, EPI>(a, m, n, false), sa);
+                                           ein[ns][rq], sa);
                 }
             } else {
-                const int nl = wn * 32 + nrow;
-                const int n = g * 128 + nl;        // gate column
-                if (n >= outN) continue;
-                const Acc& vg = acc[0][ms];
-                const Acc& vu = acc[1][ms];
-                uint2 gq, uq;
-                *reinterpret_cast<uint2*>(orow + nl * 2) =
-                    epi_gelu4(f32x4_t{vg[4 * rq], vg[4 * rq + 1], vg[4 * rq + 2], vg[4 * rq + 3]},
-                              f32x4_t{vu[4 * rq], vu[4 * rq + 1], vu[4 * rq + 2], vu[4 * rq + 3]},
-                              load_epi<WT, EPI>(a, m, n, false), gq, uq);
-                if (a.gu && m < a.M) {
-                    *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + n) = gq;
-                    *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + outN + n) = uq;
+#pragma unroll
+                for (int ns = 0; ns < C::NSUB / 2; ++ns) {
+                    const int nl = wn * (C::WN / 2) + ns * 32 + nrow;
+                    const int n = g * OUT_W + nl;        // gate column
+                    if (n >= outN) continue;
+                    const Acc& vg = acc[ns][ms];
+                    const Acc& vu = acc[ns + C::NSUB / 2][ms];
+                    uint2 gq, uq;
+                    *reinterpret_cast<uint2*>(orow + nl * 2) =
+                        epi_gelu4(f32x4_t{vg[4 * rq], vg[4 * rq + 1], vg[4 * rq + 2], vg[4 * rq + 3]},
+                                  f32x4_t{vu[4 * rq], vu[4 * rq + 1], vu[4 * rq + 2], vu[4 * rq + 3]},
+                                  ein[ns][rq], gq, uq);
+                    if (a.gu && m < a.M) {
+                        *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + n) = gq;
+                        *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + outN + n) = uq;
+                    }
                 }
             }
         }
         __syncthreads();
 #pragma unroll
-        for (int c = tid; c < PR * CPR; c += C::THREADS) {
-            const int row = c / CPR, ch = c % CPR;
-            const int gm = m0 + (row >> 5) * C::WMR + ms * 32 + (row & 31);
+        for (int c = tid; c < 64 * CPRO; c += C::THREADS) {
+            const int row = c / CPRO, ch = c % CPRO;
+            const int gm = m0 + (row >> 5) * 96 + ms * 32 + (row & 31);
             const int n = g * OUT_W + ch * 8;
             if (gm >= a.M || n >= outN) continue;
-            uint4 v = *reinterpret_cast<const uint4*>(ot + row * OSTRIDE + ch * 16);
+            const uint8_t* src = ((row >> 5) ? pair1 : pair0) + (row & 31) * OSTRIDE + ch * 16;
+            uint4 v = *reinterpret_cast<const uint4*>(src);
             if constexpr (EPI == Epi::PLAIN) {
                 if (a.resid) {
                     const uint4 r = *reinterpret_cast<const uint4*>(a.resid + static_cast<int64_t>(gm) * a.N + n);
@@ -373,30 +503,33 @@ __global__ __launch_bounds__(WMW * WNW * 64) void wide_gemm_kernel(KArgs a) {
 }  // namespace
 
 size_t wide_part_bytes(const GemmPlan& p) {
-    // p.nt = BN; per thread NSUB x MSUB x 4 f32x4
-    const int wmw = p.waves / p.wnw;
-    const int nsub = p.nt / p.wnw / 32, msub = kWideBM / wmw / 32;
+    // p.nt = BN; per thread NSUB x MSUB x 4 f32x4, NSUB = BN / wnw / 32, MSUB = 3
+    const int nsub = p.nt / p.wnw / 32, msub = 3;
     return static_cast<size_t>(p.ksplit) * p.mblocks * p.groups * (p.waves * 64) * (nsub * msub * 4) * 16;
 }
 
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStream_t s) {
     const dim3 grid(p.groups, p.mblocks, p.ksplit);
-#define VLA_WIDE(BN_, WMW_, WNW_)                                                             \
-    if (p.nt == BN_ && p.waves == WMW_ * WNW_ && p.wnw == WNW_) {                              \
-        wide_gemm_kernel<AT, WT, EPI, BN_, WMW_, WNW_><<<grid, WMW_ * WNW_ * 64, 0, s>>>(ka);  \
-        return hipGetLastError();                                                              \
+#define VLA_WIDE(BN_, WNW_)                                                             \
+    if (p.nt == BN_ && p.wnw == WNW_ && p.waves == 2 * WNW_) {                          \
+        wide_gemm_kernel<AT, WT, EPI, BN_, WNW_><<<grid, 128 * WNW_, 0, s>>>(ka);       \
+        return hipGetLastError();                                                       \
     }
     if constexpr (EPI == Epi::GELU_MUL) {
-        VLA_WIDE(256, 2, 4)
+        VLA_WIDE(256, 2)
+        VLA_WIDE(256, 4)
+    } else if constexpr (WT == WType::BF16) {
+        VLA_WIDE(128, 2)
+        VLA_WIDE(128, 4)
     } else if constexpr (AT == AType::FP8) {
-        VLA_WIDE(256, 3, 4)
-        VLA_WIDE(128, 3, 4)
-        VLA_WIDE(256, 2, 4)
-        VLA_WIDE(128, 2, 4)
+        VLA_WIDE(256, 2)
+        VLA_WIDE(128, 2)
     } else {
-        VLA_WIDE(256, 2, 4)
-        VLA_WIDE(128, 2, 4)
+        VLA_WIDE(256, 2)
+        VLA_WIDE(128, 2)
+        VLA_WIDE(256, 4)
+        VLA_WIDE(128, 4)
     }
 #undef VLA_WIDE
     return hipErrorInvalidValue;

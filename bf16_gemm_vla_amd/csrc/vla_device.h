@@ -20,13 +20,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even on the 16 dropped bits; NaN stays a
-// quiet NaN.
+// fp32 -> bf16 with gfx950's conversion instruction: round to nearest even
+// (the default rounding mode), NaN stays a quiet NaN.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two fp32 -> two bf16 packed in one dword (lo in the low half), one instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    const bf16x2_t r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // ------------------------------------------------------------------- E4M3
@@ -83,15 +87,15 @@ __device__ __forceinline__ float decode_e4m3(uint32_t b) {
     return neg ? -v : v;
 }
 
-// Four OCP E4M3 codes (one dword) -> four bf16 (two dwords), exact: the
-// hardware converts pairs of FP8 to fp32, and an FP8 value has at most 4
-// significant bits, so its fp32 pattern's high half is the bf16 pattern.
+// Four OCP E4M3 codes (one dword) -> four bf16 (two dwords), exact: every
+// E4M3 value (subnormals included) is a bf16 value, and gfx950 converts a
+// pair of FP8 codes to a pair of bf16 in one instruction (unit scale).
 __device__ __forceinline__ u32x2_t ocp4_to_bf16x4(uint32_t w) {
-    auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-    auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
     u32x2_t r;
-    r.x = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
-    r.y = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+    r.x = __builtin_bit_cast(uint32_t, lo);
+    r.y = __builtin_bit_cast(uint32_t, hi);
     return r;
 }
 

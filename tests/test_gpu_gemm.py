@@ -81,6 +81,28 @@ def test_lane_map_probe_one_hot(M):
     assert np.array_equal(Y.numpy(np.uint16).reshape(M, N), A[:, perm])
 
 
+@pytest.mark.parametrize("M", [50, 200])
+def test_decode_every_code_through_gemm(M):
+    """A one-hot activation row picks one weight code per output: with s = 1,
+    Y[m, n] = dec(q[n, m]) exactly, for every non-NaN OCP code, through the
+    weight path of the skinny (M <= 64) and the wide kernel."""
+    g = synthetic.rng(5200 + M)
+    N, K = 256, 256
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F and c != 0x80], np.uint8)
+    q = codes[g.integers(0, codes.size, (N, K))]
+    q[:, :M] = np.resize(codes, (N, M)) if M * N >= codes.size else q[:, :M]
+    A = np.zeros((M, K), np.uint16)
+    A[np.arange(M), np.arange(M)] = 0x3F80                      # bf16 1.0
+    ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, N, K, 1))
+    Y = Guarded(M * N * 2)
+    vla.vla_gemm_fp8w(dev(A), None, dev(oracle.pack(q, 8)), dev(np.ones(N, np.float32)), None, None,
+                      Y.t, ws, ws.numel(), M, N, K)
+    got = bf16_f64(Y.numpy(np.uint16).reshape(M, N))
+    want = oracle.decode(q[:, :M].T, OCP)
+    assert set(q[:, :M].ravel().tolist()) == set(codes.tolist())
+    assert np.array_equal(got, want)
+
+
 def test_lane_map_probe_one_hot_fp8_x_fp8():
     """FP8 x FP8: one-hot weights select A's codes; s_a = 1 gives dec(A) exactly."""
     g = synthetic.rng(5100)
