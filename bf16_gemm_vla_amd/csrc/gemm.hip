@@ -336,17 +336,17 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
         }
         return skinny_plan(N, K, epi, nt, steps, waves, at == AType::BF16);
     }
-    // Wide kernel: 192-row blocks of 4 waves; 256-column tiles when they
-    // give enough workgroups, else 128-column tiles and K split until ~256
-    // workgroups (each split keeps at least 8 stages of 64 K).  BF16 weights
+    // Wide kernel: 192-row blocks; 256-column tiles when they give enough
+    // workgroups, else 128-column tiles and K split until ~256 workgroups
+    // (each split keeps at least 8 pipeline stages).  Wave layouts: bf16
+    // activations 8 waves (96 x BN/4 wave tiles, 64 K per stage); FP8 x FP8
+    // with 256-column tiles 4 waves (96 x 128, 64 K per stage), with
+    // 128-column tiles 8 waves (96 x 32, 128 K per stage).  BF16 weights
     // always take 128-column tiles (a 256-column stage would not fit the
     // four-stage LDS ring).  The buffer resources address A and W with
     // 32-bit offsets.
     GemmPlan p{};
     p.kernel = 1;
-    p.steps = 0;
-    p.waves = (at == AType::FP8) ? 4 : 8;
-    p.wnw = p.waves / 2;
     p.mblocks = static_cast<int>((M + 191) / 192);
     if (epi == Epi::GELU_MUL) {
         p.nt = 256;
@@ -361,14 +361,23 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
             p.groups = static_cast<int>((tiles + 7) / 8);
         }
     }
-    const int64_t kt_total = (K + 63) / 64;
+    if (at == AType::FP8) {
+        p.waves = (p.nt == 256) ? 4 : 8;
+        p.steps = (p.nt == 256) ? 64 : 128;    // K values per pipeline stage
+    } else {
+        p.waves = 8;
+        p.steps = 64;
+    }
+    p.wnw = p.waves / 2;
+    const int64_t kt_total = (K + p.steps - 1) / p.steps;
     const int64_t base = static_cast<int64_t>(p.groups) * p.mblocks;
     int ks = 1;
     while (base * ks < 256 && kt_total / (ks * 2) >= 8) ks *= 2;
     p.ksplit = ks;
     const int64_t a_bytes = M * K * (at == AType::FP8 ? 1 : 2);
     const int64_t w_bytes = N * K * (wt == WType::FP8 ? 1 : 2);
-    p.ok = base <= kMaxCounters && a_bytes < (int64_t(1) << 31) && w_bytes < (int64_t(1) << 31);
+    // split-K arrival counters: one per 32-row slice (3) of every output tile
+    p.ok = base * 3 <= kMaxCounters && a_bytes < (int64_t(1) << 31) && w_bytes < (int64_t(1) << 31);
     return p;
 }
 

@@ -39,22 +39,22 @@ namespace {
 using namespace gemm_detail;
 
 constexpr int kWideBM = 192;
-constexpr int kWideBK = 64;          // K elements per pipeline stage
 constexpr int kWideStages = 4;
 constexpr uint32_t kOOB = 0x80000000u;   // voffset beyond every resource's range
 
-template <AType AT, WType WT, int BN, int WNW>
+template <AType AT, WType WT, int BN, int WNW, int BK_>
 struct WideCfg {
+    static constexpr int BK = BK_;                              // K elements per pipeline stage
     static constexpr int WAVES = 2 * WNW;                       // 2 along M x WNW along N
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int AB = (AT == AType::FP8) ? 1 : 2;       // activation bytes / element
     static constexpr int WLB = (WT == WType::FP8) ? 8 : 16;     // weight bytes per lane slot
     static constexpr int KMF = (AT == AType::FP8) ? 64 : 16;    // K of one MFMA
-    static constexpr int NKS = kWideBK / KMF;                   // MFMA steps per stage
-    static constexpr int ARB = kWideBK * AB;                    // A bytes per row per stage
+    static constexpr int NKS = BK / KMF;                        // MFMA steps per stage
+    static constexpr int ARB = BK * AB;                         // A bytes per row per stage
     static constexpr int CPR = ARB / 16;                        // 16-byte chunks per A row
     static constexpr int RPI = 1024 / ARB;                      // A rows per load instruction
-    static constexpr int WTB = (kWideBK / 32) * 64 * WLB;       // W bytes per 16-row tile per stage
+    static constexpr int WTB = (BK / 32) * 64 * WLB;            // W bytes per 16-row tile per stage
     static constexpr int A_BYTES = kWideBM * ARB;
     static constexpr int W_BYTES = (BN / 16) * WTB;
     static constexpr int STAGE = A_BYTES + W_BYTES;
@@ -118,10 +118,11 @@ struct Frags<AType::FP8, WT, MSUB, NSUB> {
     u32x2_t w[NSUB][4];
 };
 
-template <AType AT, WType WT, Epi EPI, int BN, int WNW>
+template <AType AT, WType WT, Epi EPI, int BN, int WNW, int BK>
 __global__ __launch_bounds__(128 * WNW) __attribute__((amdgpu_waves_per_eu(WNW / 2, WNW / 2)))
 void wide_gemm_kernel(KArgs a) {
-    using C = WideCfg<AT, WT, BN, WNW>;
+    using C = WideCfg<AT, WT, BN, WNW, BK>;
+    static_assert(AT == AType::FP8 || BK == 64, "bf16 activations stage 64 K values (128 bytes per row)");
     using F = Frags<AT, WT, C::MSUB, C::NSUB>;
     static_assert(EPI == Epi::PLAIN || (C::NSUB % 2 == 0 && AT == AType::BF16 && WT == WType::FP8),
                   "the fused gate/up epilogue pairs gate and up sub-tiles within a wave");
@@ -140,7 +141,7 @@ void wide_gemm_kernel(KArgs a) {
     const int g = blockIdx.x, mb = blockIdx.y, split = blockIdx.z;
     const int m0 = mb * kWideBM;
     const int ksteps = a.K >> 5;
-    const int kt_total = (a.K + kWideBK - 1) / kWideBK;
+    const int kt_total = (a.K + BK - 1) / BK;
     const int kt_per = (kt_total + a.ksplit - 1) / a.ksplit;
     const int kt_begin = split * kt_per;
     const int kt_end = min(kt_total, kt_begin + kt_per);
@@ -157,7 +158,7 @@ void wide_gemm_kernel(KArgs a) {
     //      Load t of wave w is instruction q = w + 4t of the stage; it fills
     //      LDS bytes q*1024 .. +1023 of the stage buffer (A first, then W).
     uint32_t voff[C::L], voffT[C::L];   // voffT: the same for the ragged last K tile
-    const int krem = a.K - (kt_total - 1) * kWideBK;    // K values in the last K tile (32 or 64)
+    const int krem = a.K - (kt_total - 1) * BK;         // K values in the last K tile
 #pragma unroll
     for (int t = 0; t < C::L; ++t) {
         const int q = wave + C::WAVES * t;
@@ -194,53 +195,52 @@ void wide_gemm_kernel(KArgs a) {
         }
     };
 
-    // ---- LDS operand addresses (byte offsets within a stage buffer)
-    int aoff, woff;
-    if constexpr (AT == AType::BF16) {
-        // row r = wm*96 + ms*32 + l32 (+ ms*4096 at read time); chunk 2ks + g2
-        // at position chunk ^ ((r >> 1) & 7); bits 1..3 of r come from l32
-        const int swz = (l32 >> 1) & 7;
-        aoff = (wm * 96 + l32) * 128 + (((g2 ^ swz) & 1) * 16);
-        (void)swz;
-    } else {
-        aoff = (wm * 96 + l32) * 64;
-    }
-    if constexpr (WT == WType::FP8) {
-        const int odd = (l32 >> 4) & 1;
-        woff = C::A_BYTES + ((wn * C::WN) >> 4) * 1024 + odd * 1024 + (l32 & 15) * 8 +
-               ((AT == AType::BF16) ? ((g2 ^ odd) * 128) : (g2 * 512));
-    } else {
-        woff = C::A_BYTES + ((wn * C::WN) >> 4) * 2048 + (l32 >> 4) * 2048 + (l32 & 15) * 16 + g2 * 256;
-    }
-    const int swzA = (AT == AType::BF16) ? ((l32 >> 1) & 7) : ((l32 >> 2) & 3);
+    // ---- LDS operand addresses (byte offsets within a stage buffer).
+    //      Activation row r = wm*96 + ms*32 + l32; its 16-byte chunk c sits
+    //      at position c ^ swz with swz taken from bits of l32 only (the
+    //      wm/ms terms are multiples of 32 rows).  Weight tile slot of the
+    //      lane's row: (wn*WN + ns*32)/16 + (l32 >> 4).
+    const int swzA = (C::CPR == 8) ? ((l32 >> 1) & 7) : ((l32 >> 2) & 3);
     const int oddW = (l32 >> 4) & 1;
+    const int aoff = (wm * 96 + l32) * C::ARB;
+    int woff;
+    if constexpr (WT == WType::BF16)
+        woff = C::A_BYTES + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 16 + g2 * 256;
+    else if constexpr (AT == AType::BF16)
+        woff = C::A_BYTES + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 8 + (g2 ^ oddW) * 128;
+    else
+        woff = C::A_BYTES + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 8 + g2 * 512;
 
     auto read_step = [&](const uint8_t* buf, int ks, F& f) __attribute__((always_inline)) {
         if constexpr (AT == AType::BF16) {
-            // chunk (2ks + g2) ^ swz = ((ks ^ (swz >> 1)) << 1) | (g2 ^ (swz & 1))
-            const int hi = ((ks ^ (swzA >> 1)) << 1) * 16;
+            // 32x32x16: chunk (2ks + g2) ^ swz = ((ks ^ (swz >> 1)) << 1) | (g2 ^ (swz & 1))
+            const int cpos = ((((ks ^ (swzA >> 1)) << 1)) | (g2 ^ (swzA & 1))) * 16;
 #pragma unroll
             for (int ms = 0; ms < C::MSUB; ++ms)
-                f.a[ms] = *reinterpret_cast<const u32x4_t*>(buf + aoff + ms * 32 * 128 + hi);
+                f.a[ms] = *reinterpret_cast<const u32x4_t*>(buf + aoff + ms * 32 * C::ARB + cpos);
 #pragma unroll
             for (int ns = 0; ns < C::NSUB; ++ns) {
+                // packed fragment ks/2, K group 2(ks&1) + g2 (FP8 tiles of odd slots: 128-byte halves swapped)
                 if constexpr (WT == WType::FP8)
-                    f.w[ns] = *reinterpret_cast<const u32x2_t*>(buf + woff + ns * 2 * 1024 + ks * 256);
+                    f.w[ns] = *reinterpret_cast<const u32x2_t*>(buf + woff + ns * 2 * C::WTB + ks * 256);
                 else
-                    f.w[ns] = *reinterpret_cast<const u32x4_t*>(buf + woff + ns * 2 * 2048 + ks * 512);
+                    f.w[ns] = *reinterpret_cast<const u32x4_t*>(buf + woff + ns * 2 * C::WTB + ks * 512);
             }
         } else {
-            const int p0 = ((2 * g2) ^ swzA) * 16, p1 = ((2 * g2 + 1) ^ swzA) * 16;
+            // 32x32x64: the lane's row holds K 64ks + 32g2 .. +31 = chunks c0, c0+1
+            const int c0 = 4 * ks + 2 * g2;
+            const int p0 = (c0 ^ swzA) * 16, p1 = ((c0 + 1) ^ swzA) * 16;
 #pragma unroll
             for (int ms = 0; ms < C::MSUB; ++ms) {
-                f.a[ms][0] = *reinterpret_cast<const u32x4_t*>(buf + aoff + ms * 32 * 64 + p0);
-                f.a[ms][1] = *reinterpret_cast<const u32x4_t*>(buf + aoff + ms * 32 * 64 + p1);
+                f.a[ms][0] = *reinterpret_cast<const u32x4_t*>(buf + aoff + ms * 32 * C::ARB + p0);
+                f.a[ms][1] = *reinterpret_cast<const u32x4_t*>(buf + aoff + ms * 32 * C::ARB + p1);
             }
+            // packed fragment 2ks + g2, K groups k1 = 0..3
 #pragma unroll
             for (int ns = 0; ns < C::NSUB; ++ns)
 #pragma unroll
                 for (int k1 = 0; k1 < 4; ++k1)
-                    f.w[ns][k1] = *reinterpret_cast<const u32x2_t*>(buf + woff + ns * 2 * 1024 + ((k1 ^ oddW) * 128));
+                    f.w[ns][k1] = *reinterpret_cast<const u32x2_t*>(buf + woff + ns * 2 * C::WTB + ks * 1024 + ((k1 ^ oddW) * 128));
         }
     };
 
@@ -388,9 +388,16 @@ void wide_gemm_kernel(KArgs a) {
 
     // ---- epilogue.  acc[ns][ms] register r: row (output channel) 8*(r/4) + 4*(lane/32) + r%4
     //      of the 32-column sub-tile, activation row lane%32 of the 32-row sub-tile.
+    //      The tile is finished in MSUB slices (slice ms = accumulators acc[*][ms]).
+    //      With K split over workgroups every slice has its own arrival counter:
+    //      each workgroup stores all its partials, then counts its arrival on
+    //      every slice at once, and finishes the slices it was last for, so the
+    //      reduction of a tile is spread over its workgroups.  Partials are
+    //      summed in split order, whoever finishes (bitwise repeatable).
     constexpr int NACC = C::NSUB * C::MSUB * 4;
+    uint32_t todo = (1u << C::MSUB) - 1;     // slices this workgroup outputs
     if (a.ksplit > 1) {
-        // partial layout: [split][mblock][group][NACC][256 threads] of f32x4
+        // partial layout: [split][mblock][group][NACC][threads] of f32x4
         const int64_t slot = static_cast<int64_t>(mb) * a.groups + g;
         const int64_t per = static_cast<int64_t>(C::THREADS) * NACC;
         const int64_t sstride = static_cast<int64_t>(gridDim.y) * a.groups * per;
@@ -405,23 +412,55 @@ void wide_gemm_kernel(KArgs a) {
                     const Acc& v = acc[ns][ms];
                     part.store(off(split, (ns * C::MSUB + ms) * 4 + rq), f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]});
                 }
-        // the flag lives in stage buffer 0: every wave is past its last operand read
-        if (!splitk_arrive_last(a.tickets, static_cast<int>(slot), a.ksplit, reinterpret_cast<int*>(lds0))) return;
+        // every wave's partial stores have completed (stores count in vmcnt),
+        // then the barrier orders them before the arrivals; the flags live in
+        // stage buffer 0, which every wave has finished reading
+        int* const flags = reinterpret_cast<int*>(lds0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid < C::MSUB) {
+            const uint32_t prev = __hip_atomic_fetch_add(a.tickets + slot * C::MSUB + tid, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            flags[tid] = (prev == static_cast<uint32_t>(a.ksplit - 1)) ? 1 : 0;
+        }
+        __syncthreads();
+        todo = 0;
 #pragma unroll
-        for (int ns = 0; ns < C::NSUB; ++ns)
+        for (int ms = 0; ms < C::MSUB; ++ms) todo |= flags[ms] ? (1u << ms) : 0u;
+        if (todo == 0) return;
 #pragma unroll
-            for (int ms = 0; ms < C::MSUB; ++ms)
+        for (int ms = 0; ms < C::MSUB; ++ms) {
+            if (!(todo & (1u << ms))) continue;
+            // two splits' loads in flight at a time, summed in split order
+            f32x4_t sum[C::NSUB][4];
+            for (int sp = 0; sp < a.ksplit; sp += 2) {
+                f32x4_t p0[C::NSUB][4], p1[C::NSUB][4];
+                const bool two = sp + 1 < a.ksplit;
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int f = (ns * C::MSUB + ms) * 4 + rq;
-                    f32x4_t v = part.load(off(0, f));
-                    for (int sp = 1; sp < a.ksplit; ++sp) v += part.load(off(sp, f));
-                    acc[ns][ms][4 * rq] = v[0];
-                    acc[ns][ms][4 * rq + 1] = v[1];
-                    acc[ns][ms][4 * rq + 2] = v[2];
-                    acc[ns][ms][4 * rq + 3] = v[3];
-                }
-        splitk_reset(a.tickets, static_cast<int>(slot));
+                for (int ns = 0; ns < C::NSUB; ++ns)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const int f = (ns * C::MSUB + ms) * 4 + rq;
+                        p0[ns][rq] = part.load(off(sp, f));
+                        p1[ns][rq] = two ? part.load(off(sp + 1, f)) : f32x4_t{};
+                    }
+#pragma unroll
+                for (int ns = 0; ns < C::NSUB; ++ns)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        sum[ns][rq] = sp == 0 ? p0[ns][rq] : sum[ns][rq] + p0[ns][rq];
+                        if (two) sum[ns][rq] += p1[ns][rq];
+                    }
+            }
+#pragma unroll
+            for (int ns = 0; ns < C::NSUB; ++ns)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[ns][ms][4 * rq + e] = sum[ns][rq][e];
+            if (tid == 0)
+                __hip_atomic_store(a.tickets + slot * C::MSUB + ms, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     // ---- output: one pass per 32-row sub-tile ms (64 rows: both wm halves).
     //      Each wave scales (and biases, or applies GELU * up to) its
@@ -429,18 +468,21 @@ void wide_gemm_kernel(KArgs a) {
     //      rows [32][OUT_W], wm half in its own stage buffer; then the whole
     //      workgroup stores the pass as 16-byte row chunks, adding the
     //      residual on the way.  Passes alternate between buffer pairs
-    //      (0, 1) and (2, 3): a wave writing pass ms+2 has passed the barrier
-    //      every wave reaches only after storing pass ms.
+    //      (0, 1) and (2, 3): a wave writing pass k+2 has passed the barrier
+    //      every wave reaches only after storing pass k.
     constexpr int OUT_W = (EPI == Epi::PLAIN) ? BN : BN / 2;  // output columns of the tile
     constexpr int OSTRIDE = OUT_W * 2 + 16;                   // bytes per LDS row (+ bank padding)
     constexpr int CPRO = OUT_W / 8;                           // 16-byte chunks per output row
     static_assert(32 * OSTRIDE <= C::STAGE, "32 output rows fit one stage buffer");
     const int outN = (EPI == Epi::PLAIN) ? a.N : (a.N >> 1);
-    __syncthreads();   // every wave has finished reading the stage buffers
+    __syncthreads();   // every wave has finished reading the stage buffers (and the flags)
+    int pass = 0;
 #pragma unroll
     for (int ms = 0; ms < C::MSUB; ++ms) {
-        uint8_t* const pair0 = (ms & 1) ? lds2 : lds0;
-        uint8_t* const pair1 = (ms & 1) ? lds3 : lds1;
+        if (!(todo & (1u << ms))) continue;   // uniform
+        uint8_t* const pair0 = (pass & 1) ? lds2 : lds0;
+        uint8_t* const pair1 = (pass & 1) ? lds3 : lds1;
+        ++pass;
         const int m = m0 + wm * 96 + ms * 32 + l32;
         uint8_t* orow = (wm ? pair1 : pair0) + l32 * OSTRIDE;
 #pragma unroll
@@ -495,7 +537,8 @@ void wide_gemm_kernel(KArgs a) {
                     v.w = add_resid2(v.w, r.w);
                 }
             }
-            *reinterpret_cast<uint4*>(a.Y + static_cast<int64_t>(gm) * outN + n) = v;
+            // streaming store: the output is not read again by this kernel
+            __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(a.Y + static_cast<int64_t>(gm) * outN + n));
         }
     }
 }
@@ -511,25 +554,27 @@ size_t wide_part_bytes(const GemmPlan& p) {
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStream_t s) {
     const dim3 grid(p.groups, p.mblocks, p.ksplit);
-#define VLA_WIDE(BN_, WNW_)                                                             \
-    if (p.nt == BN_ && p.wnw == WNW_ && p.waves == 2 * WNW_) {                          \
-        wide_gemm_kernel<AT, WT, EPI, BN_, WNW_><<<grid, 128 * WNW_, 0, s>>>(ka);       \
+#define VLA_WIDE(BN_, WNW_, BK_)                                                        \
+    if (p.nt == BN_ && p.wnw == WNW_ && p.waves == 2 * WNW_ && p.steps == BK_) {         \
+        wide_gemm_kernel<AT, WT, EPI, BN_, WNW_, BK_><<<grid, 128 * WNW_, 0, s>>>(ka);  \
         return hipGetLastError();                                                       \
     }
     if constexpr (EPI == Epi::GELU_MUL) {
-        VLA_WIDE(256, 2)
-        VLA_WIDE(256, 4)
+        VLA_WIDE(256, 2, 64)
+        VLA_WIDE(256, 4, 64)
     } else if constexpr (WT == WType::BF16) {
-        VLA_WIDE(128, 2)
-        VLA_WIDE(128, 4)
+        VLA_WIDE(128, 2, 64)
+        VLA_WIDE(128, 4, 64)
     } else if constexpr (AT == AType::FP8) {
-        VLA_WIDE(256, 2)
-        VLA_WIDE(128, 2)
+        VLA_WIDE(256, 2, 64)
+        VLA_WIDE(128, 2, 64)
+        VLA_WIDE(128, 2, 128)
+        VLA_WIDE(128, 4, 128)
     } else {
-        VLA_WIDE(256, 2)
-        VLA_WIDE(128, 2)
-        VLA_WIDE(256, 4)
-        VLA_WIDE(128, 4)
+        VLA_WIDE(256, 2, 64)
+        VLA_WIDE(128, 2, 64)
+        VLA_WIDE(256, 4, 64)
+        VLA_WIDE(128, 4, 64)
     }
 #undef VLA_WIDE
     return hipErrorInvalidValue;
