@@ -65,35 +65,41 @@ __device__ __forceinline__ int skinny_tile(int g, int j, int N) {
 // ALDS: stage the (row-major bf16) activation chunk through LDS with direct
 // global->LDS loads, one contiguous KiB per wave instruction, instead of
 // loading MFMA fragments (16 rows x 64 B per instruction) from global memory.
-template <int WAVES, int S>
+template <int WAVES, int S, int MT>
 struct SkinnyLds {
     static constexpr int CH = WAVES * S;             // K steps per workgroup chunk
     static constexpr int RB = CH * 64;               // bf16 bytes of one row's chunk
     static constexpr int RS = RB + 16;               // LDS row stride (bank spread)
-    static constexpr int BYTES = 64 * RS;            // up to 64 rows
+    static constexpr int BYTES = MT * 16 * RS;       // the workgroup's rows
 };
 
-template <AType AT, WType WT, Epi EPI, int NT, int S, int WAVES, bool ALDS>
+// One workgroup: NT 16-column weight tiles x MT 16-row activation tiles
+// (rows m0 .. m0 + 16*MT - 1, m0 = 16*MT*blockIdx.z) x one K chunk
+// (blockIdx.y) of WAVES * S MFMA steps, each wave S steps of it.
+template <AType AT, WType WT, Epi EPI, int NT, int S, int WAVES, bool ALDS, int MT>
 __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
     using WF = typename WFragT<WT>::type;
     using AF = typename AFragT<AT>::type;
     constexpr int WB = (WT == WType::FP8) ? 8 : 16;   // weight bytes per lane per fragment
     constexpr int AB = (AT == AType::FP8) ? 1 : 2;    // activation bytes per element
     constexpr int JO = (EPI == Epi::PLAIN) ? NT : NT / 2;   // output tiles per group
-    constexpr int PAIRS = JO * 4;                            // (output tile, m-tile) fragments
+    constexpr int PAIRS = JO * MT;                           // (output tile, m-tile) fragments
     constexpr int R = (PAIRS + WAVES - 1) / WAVES;           // fragments finished per wave
 
-    using L = SkinnyLds<WAVES, S>;
-    constexpr int RED_BYTES = WAVES * NT * 4 * 64 * 16;
+    using L = SkinnyLds<WAVES, S, MT>;
+    constexpr int RED_BYTES = WAVES * NT * MT * 64 * 16;
     constexpr int LDS_BYTES = (ALDS && L::BYTES > RED_BYTES) ? L::BYTES : RED_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "the workgroup's LDS fits");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-    auto red = reinterpret_cast<f32x4_t(*)[NT][4][64]>(lds);
+    auto red = reinterpret_cast<f32x4_t(*)[NT][MT][64]>(lds);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = blockIdx.x, split = blockIdx.y;
+    const int g = blockIdx.x, split = blockIdx.y, mh = blockIdx.z;
+    const int m0 = mh * MT * 16;                      // first activation row of the workgroup
+    const int mrows = min(a.M - m0, MT * 16);         // rows of the workgroup (> 0)
     const int ksteps = a.K >> 5;
     const int kbase = split * WAVES * S + wave * S;
-    const int mt_count = (a.M + 15) >> 4;
+    const int mt_count = (mrows + 15) >> 4;
     const int ntiles = a.N >> 4;
     const int mrow = lane & 15, q = lane >> 4;
 
@@ -111,19 +117,19 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
             else wf[s][j] = WF{};
         }
     }
-    // 2. activation fragments: row mt*16 + lane%16, 8 K values at 8*(lane/16)
-    AF af[S][4];
+    // 2. activation fragments: row m0 + mt*16 + lane%16, 8 K values at 8*(lane/16)
+    AF af[S][MT];
     if constexpr (ALDS) {
         // issue this wave's share of the chunk's row pieces (1 KiB each)
         const int kstep0 = split * L::CH;
         constexpr int PIECES = (L::RB + 1023) / 1024;
         const int kel_row = kstep0 * 32;                       // first K element of the chunk
-        for (int piece = wave; piece < a.M * PIECES; piece += WAVES) {
-            const int row = piece / PIECES, p = piece % PIECES;
+        for (int piece = wave; piece < mrows * PIECES; piece += WAVES) {
+            const int row = piece / PIECES, p = piece % PIECES;    // row within the workgroup
             const int byte = p * 1024 + lane * 16;             // within the row chunk
             const int kel = kel_row + byte / 2;
             if (byte < L::RB && kel < a.K) {
-                const uint8_t* src = static_cast<const uint8_t*>(a.A) + (static_cast<int64_t>(row) * a.K + kel) * 2;
+                const uint8_t* src = static_cast<const uint8_t*>(a.A) + (static_cast<int64_t>(m0 + row) * a.K + kel) * 2;
                 __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + row * L::RS + p * 1024), 16, 0, 0);
             }
         }
@@ -133,11 +139,11 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
             const bool ok = kbase + s < ksteps;
             const int64_t k = static_cast<int64_t>(kbase + s) * 32 + 8 * q;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
                 const int row = mt * 16 + mrow;
-                if (ok && row < a.M)
+                if (ok && row < mrows)
                     af[s][mt] = *reinterpret_cast<const AF*>(static_cast<const uint8_t*>(a.A) +
-                                                             (static_cast<int64_t>(row) * a.K + k) * AB);
+                                                             (static_cast<int64_t>(m0 + row) * a.K + k) * AB);
                 else
                     af[s][mt] = AF{};
             }
@@ -148,11 +154,11 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
     const float sa = (AT == AType::FP8) ? *a.s_a : 1.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int pair = wave + r * WAVES, jo = pair >> 2, mt = pair & 3;
+        const int pair = wave + r * WAVES, jo = pair / MT, mt = pair % MT;
         const int tile = skinny_tile<EPI, NT>(g, jo < JO ? jo : 0, a.N);
-        const int m = mt * 16 + mrow;
-        if (pair < PAIRS && tile < ntiles && m < a.M)
-            ein[r] = load_epi<WT, EPI>(a, m, tile * 16 + 4 * q, a.ksplit == 1);
+        const int row = mt * 16 + mrow;
+        if (pair < PAIRS && tile < ntiles && row < mrows)
+            ein[r] = load_epi<WT, EPI>(a, m0 + row, tile * 16 + 4 * q, a.ksplit == 1);
     }
     if constexpr (ALDS) {
         // every wave's direct-to-LDS loads have landed, then read fragments
@@ -162,9 +168,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
         for (int s = 0; s < S; ++s) {
             const bool ok = kbase + s < ksteps;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
                 const int row = mt * 16 + mrow;
-                if (ok && row < a.M)
+                if (ok && row < mrows)
                     af[s][mt] = *reinterpret_cast<const AF*>(lds + row * L::RS + ((wave * S + s) * 32 + 8 * q) * 2);
                 else
                     af[s][mt] = AF{};
@@ -172,15 +178,15 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
         }
     }
     // 4. MFMA
-    f32x4_t acc[NT][4];
+    f32x4_t acc[NT][MT];
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[j][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int mt = 0; mt < MT; ++mt) acc[j][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < S; ++s) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
             if (mt >= mt_count) break;
             const bf16x8_t bop = a_operand<AT>(af[s][mt]);
 #pragma unroll
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
             if (mt < mt_count) red[wave][j][mt][lane] = acc[j][mt];
     __syncthreads();
     auto total = [&](int j, int mt) {
@@ -206,47 +212,48 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
     };
     auto finish = [&](int r, int jo, int mt, f32x4_t v, f32x4_t u) {
         const int tile = skinny_tile<EPI, NT>(g, jo, a.N);
-        const int m = mt * 16 + mrow;
-        if (tile >= ntiles || m >= a.M) return;
-        if constexpr (EPI == Epi::PLAIN) store_plain<AT, WT>(a, m, tile * 16 + 4 * q, v, ein[r], sa);
-        else store_gelu(a, m, tile * 16 + 4 * q, v, u, ein[r]);
+        const int row = mt * 16 + mrow;
+        if (tile >= ntiles || row >= mrows) return;
+        if constexpr (EPI == Epi::PLAIN) store_plain<AT, WT>(a, m0 + row, tile * 16 + 4 * q, v, ein[r], sa);
+        else store_gelu(a, m0 + row, tile * 16 + 4 * q, v, u, ein[r]);
     };
     constexpr int JU = (EPI == Epi::PLAIN) ? 0 : NT / 2;     // offset of the matching up tile
     if (a.ksplit == 1) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int pair = wave + r * WAVES, jo = pair >> 2, mt = pair & 3;
+            const int pair = wave + r * WAVES, jo = pair / MT, mt = pair % MT;
             if (pair >= PAIRS || mt >= mt_count) continue;
             finish(r, jo, mt, total(jo, mt), JU ? total(jo + JU, mt) : f32x4_t{});
         }
         return;
     }
-    // 6. cross-workgroup split-K.  Partial layout [split][group][NT][4 mt][64 lanes]
+    // 6. cross-workgroup split-K.  Partial layout [split][m split][group][NT][MT][64 lanes]
     //    of f32x4; every wave stores and later finishes its own fragments.
     const Coherent part(a.part, a.part_bytes);
+    const int slot = mh * a.groups + g;
     auto off = [&](int sp, int j, int mt) {
-        return static_cast<uint32_t>((((static_cast<int64_t>(sp) * a.groups + g) * NT + j) * 4 + mt) * 64 + lane) * 16u;
+        return static_cast<uint32_t>((((static_cast<int64_t>(sp) * a.msplit * a.groups + slot) * NT + j) * MT + mt) * 64 + lane) * 16u;
     };
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int pair = wave + r * WAVES, jo = pair >> 2, mt = pair & 3;
+        const int pair = wave + r * WAVES, jo = pair / MT, mt = pair % MT;
         if (pair >= PAIRS || mt >= mt_count) continue;
         part.store(off(split, jo, mt), total(jo, mt));
         if (JU) part.store(off(split, jo + JU, mt), total(jo + JU, mt));
     }
-    if (!splitk_arrive_last(a.tickets, g, a.ksplit)) return;
+    if (!splitk_arrive_last(a.tickets, slot, a.ksplit)) return;
     // the residual was not prefetched (only the last workgroup needs it)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int pair = wave + r * WAVES, jo = pair >> 2, mt = pair & 3;
+        const int pair = wave + r * WAVES, jo = pair / MT, mt = pair % MT;
         const int tile = skinny_tile<EPI, NT>(g, jo < JO ? jo : 0, a.N);
-        const int m = mt * 16 + mrow;
-        if (EPI == Epi::PLAIN && a.resid && pair < PAIRS && tile < ntiles && m < a.M)
-            ein[r].resid = *reinterpret_cast<const uint2*>(a.resid + static_cast<int64_t>(m) * a.N + tile * 16 + 4 * q);
+        const int row = mt * 16 + mrow;
+        if (EPI == Epi::PLAIN && a.resid && pair < PAIRS && tile < ntiles && row < mrows)
+            ein[r].resid = *reinterpret_cast<const uint2*>(a.resid + static_cast<int64_t>(m0 + row) * a.N + tile * 16 + 4 * q);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int pair = wave + r * WAVES, jo = pair >> 2, mt = pair & 3;
+        const int pair = wave + r * WAVES, jo = pair / MT, mt = pair % MT;
         if (pair >= PAIRS || mt >= mt_count) continue;
         f32x4_t v = part.load(off(0, jo, mt));
         f32x4_t u = JU ? part.load(off(0, jo + JU, mt)) : f32x4_t{};
@@ -256,29 +263,32 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
         }
         finish(r, jo, mt, v, u);
     }
-    splitk_reset(a.tickets, g);
+    splitk_reset(a.tickets, slot);
 }
 
 // ------------------------------------------------------------- dispatch
 
-// Skinny tilings compiled in: (tiles per workgroup, K steps per wave, waves).
-#define VLA_SKINNY_CONFIGS(X) \
-    X(1, 1, 16) X(1, 2, 16) X(1, 4, 16) X(1, 2, 8) X(1, 4, 8) X(1, 8, 8) X(1, 8, 4) \
-    X(2, 1, 16) X(2, 2, 16) X(2, 2, 8) X(2, 4, 8) X(2, 4, 4) X(2, 8, 4)             \
-    X(4, 1, 8) X(4, 2, 8) X(4, 2, 4) X(4, 4, 4)
+// Skinny tilings compiled in: (tiles per workgroup, K steps per wave, waves,
+// 16-row activation tiles per workgroup).
+#define VLA_SKINNY_CONFIGS(X)                                                                        \
+    X(1, 1, 16, 4) X(1, 2, 16, 4) X(1, 4, 16, 4) X(1, 2, 8, 4) X(1, 4, 8, 4) X(1, 8, 8, 4) X(1, 8, 4, 4) \
+    X(2, 1, 16, 4) X(2, 2, 16, 4) X(2, 2, 8, 4) X(2, 4, 8, 4) X(2, 4, 4, 4) X(2, 8, 4, 4)                \
+    X(4, 1, 8, 4) X(4, 2, 8, 4) X(4, 2, 4, 4) X(4, 4, 4, 4)                                              \
+    X(1, 2, 8, 1) X(1, 4, 8, 1) X(1, 4, 16, 1) X(1, 8, 16, 1)                                            \
+    X(2, 2, 8, 1) X(2, 4, 8, 1) X(2, 4, 16, 1) X(2, 8, 16, 1)
 
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_skinny(const KArgs& ka, const GemmPlan& p, hipStream_t s) {
-    const dim3 grid(p.groups, p.ksplit);
-#define VLA_CASE(NT_, S_, W_)                                                                      \
-    if (p.nt == NT_ && p.steps == S_ && p.waves == W_) {                                           \
+    const dim3 grid(p.groups, p.ksplit, p.mblocks);
+#define VLA_CASE(NT_, S_, W_, MT_)                                                                 \
+    if (p.nt == NT_ && p.steps == S_ && p.waves == W_ && p.mt == MT_) {                            \
         if constexpr (EPI == Epi::GELU_MUL && NT_ < 2) {                                           \
             return hipErrorInvalidValue;                                                           \
-        } else if constexpr (AT == AType::BF16 && W_ * S_ <= 32) {                                 \
-            if (p.alds) skinny_gemm_kernel<AT, WT, EPI, NT_, S_, W_, true><<<grid, W_ * 64, 0, s>>>(ka); \
-            else skinny_gemm_kernel<AT, WT, EPI, NT_, S_, W_, false><<<grid, W_ * 64, 0, s>>>(ka);  \
+        } else if constexpr (AT == AType::BF16 && SkinnyLds<W_, S_, MT_>::BYTES <= 160 * 1024) {   \
+            if (p.alds) skinny_gemm_kernel<AT, WT, EPI, NT_, S_, W_, true, MT_><<<grid, W_ * 64, 0, s>>>(ka); \
+            else skinny_gemm_kernel<AT, WT, EPI, NT_, S_, W_, false, MT_><<<grid, W_ * 64, 0, s>>>(ka);  \
         } else {                                                                                   \
-            skinny_gemm_kernel<AT, WT, EPI, NT_, S_, W_, false><<<grid, W_ * 64, 0, s>>>(ka);      \
+            skinny_gemm_kernel<AT, WT, EPI, NT_, S_, W_, false, MT_><<<grid, W_ * 64, 0, s>>>(ka);      \
         }                                                                                          \
         return hipGetLastError();                                                                  \
     }
@@ -293,20 +303,22 @@ hipError_t launch_typed(const KArgs& ka, const GemmPlan& p, hipStream_t s) {
     return launch_wide<AT, WT, EPI>(ka, p, s);
 }
 
-// Skinny plan for a given tiling: groups of `nt` tiles, K chunks of
-// waves * steps MFMA steps.
-GemmPlan skinny_plan(int64_t N, int64_t K, Epi epi, int nt, int steps, int waves, bool alds = false) {
+// Skinny plan for a given tiling: groups of `nt` tiles, activation row
+// blocks of `mt` 16-row tiles, K chunks of waves * steps MFMA steps.
+GemmPlan skinny_plan(int64_t M, int64_t N, int64_t K, Epi epi, int nt, int steps, int waves, int mt,
+                     bool alds = false) {
     GemmPlan p{};
     p.kernel = 0;
-    p.alds = alds && waves * steps <= 32;
     p.nt = nt;
     p.steps = steps;
     p.waves = waves;
+    p.mt = mt;
+    p.alds = alds && static_cast<int64_t>(mt) * 16 * (static_cast<int64_t>(waves) * steps * 64 + 16) <= 160 * 1024;
     const int64_t tiles = N / 16, ksteps = K / 32;
     p.groups = static_cast<int>(std::max<int64_t>(1, epi == Epi::GELU_MUL ? (tiles / 2) / (nt / 2) : (tiles + nt - 1) / nt));
     p.ksplit = static_cast<int>((ksteps + static_cast<int64_t>(waves) * steps - 1) / (static_cast<int64_t>(waves) * steps));
-    p.mblocks = 1;
-    p.ok = p.ksplit == 1 || p.groups <= kMaxCounters;
+    p.mblocks = static_cast<int>((M + 16 * mt - 1) / (16 * mt));
+    p.ok = p.ksplit == 1 || static_cast<int64_t>(p.groups) * p.mblocks <= kMaxCounters;
     return p;
 }
 
@@ -317,15 +329,31 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
     const int64_t tiles = N / 16;
     if (M <= 64) {
         // One 16-column tile (a gate/up pair for the fused epilogue) per
-        // workgroup and K chunks of at most 32 MFMA steps (1024 K), split
-        // over workgroups only as far as needed to reach ~256 workgroups.
-        // Tilings measured on MI355X at M = 50: FP8 weights 8 waves x 4
-        // steps, BF16 weights 16 waves x 2 steps; bf16 activations staged
-        // through LDS (1.2-1.4 us faster per call than fragment loads).
+        // workgroup.  With at least ~256 such groups every workgroup takes
+        // all rows and K chunks of at most 32 MFMA steps (1024 K).  With
+        // fewer (the 4096 -> 1024 down-projection: 64 groups) the rows are
+        // split first, one 16-row tile per workgroup, which needs no
+        // exchange between workgroups (workgroups sharing a weight tile
+        // sit on the same XCD, grid x being a multiple of 8 there, so the
+        // tile streams from HBM once); K is split across workgroups only
+        // for what remains.  Tilings measured on MI355X at M = 50: FP8
+        // weights 8 waves x 4 steps, BF16 weights 16 waves x 2 steps;
+        // bf16 activations staged through LDS.
         const int nt = (epi == Epi::GELU_MUL) ? 2 : 1;
         const int64_t groups = std::max<int64_t>(1, (epi == Epi::GELU_MUL) ? tiles / 2 : tiles);
-        const int64_t want_split = groups >= 256 ? 1 : (256 + groups - 1) / groups;
-        const int64_t chunk = (ksteps + want_split - 1) / want_split;   // K steps per workgroup
+        const int64_t mt_total = (M + 15) / 16;
+        const int64_t want = groups >= 256 ? 1 : (256 + groups - 1) / groups;   // splits wanted
+        if (want > 1 && mt_total > 1) {
+            const int64_t ksplit = (want + mt_total - 1) / mt_total;
+            const int64_t chunk = (ksteps + ksplit - 1) / ksplit;               // K steps per workgroup
+            int steps, waves;
+            if (chunk <= 16) { waves = 8; steps = 2; }
+            else if (chunk <= 32) { waves = 8; steps = 4; }
+            else if (chunk <= 64) { waves = 16; steps = 4; }
+            else { waves = 16; steps = 8; }
+            return skinny_plan(M, N, K, epi, nt, steps, waves, 1, at == AType::BF16);
+        }
+        const int64_t chunk = (ksteps + want - 1) / want;   // K steps per workgroup
         int steps, waves;
         if (wt == WType::BF16) {
             waves = 16;
@@ -334,7 +362,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
             waves = 8;
             steps = chunk <= 16 ? 2 : 4;
         }
-        return skinny_plan(N, K, epi, nt, steps, waves, at == AType::BF16);
+        return skinny_plan(M, N, K, epi, nt, steps, waves, 4, at == AType::BF16);
     }
     // Wide kernel: 192-row blocks; 256-column tiles when they give enough
     // workgroups, else 128-column tiles and K split until ~256 workgroups
@@ -387,7 +415,7 @@ size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
     if (p.ksplit <= 1) return kCounterBytes;
     size_t part;
     if (p.kernel == 0)
-        part = static_cast<size_t>(p.ksplit) * p.groups * p.nt * 4 * 64 * 16;
+        part = static_cast<size_t>(p.ksplit) * p.mblocks * p.groups * p.nt * p.mt * 64 * 16;
     else
         part = wide_part_bytes(p);
     return kCounterBytes + part;
@@ -400,6 +428,7 @@ hipError_t launch_gemm_plan(const GemmProblem& pr, const GemmPlan& p, hipStream_
     ka.M = static_cast<int>(pr.M); ka.N = static_cast<int>(pr.N); ka.K = static_cast<int>(pr.K);
     ka.ksplit = p.ksplit;
     ka.groups = p.groups;
+    ka.msplit = p.mblocks;
     ka.tickets = static_cast<uint32_t*>(pr.ws);
     ka.part = reinterpret_cast<float*>(static_cast<uint8_t*>(pr.ws) + kCounterBytes);
     ka.part_bytes = static_cast<uint32_t>(gemm_ws_bytes(p, pr.M, pr.N) - kCounterBytes);

@@ -33,6 +33,7 @@ struct KArgs {
     int M, N, K;
     int ksplit;
     int groups;
+    int msplit;     // skinny kernel: activation row blocks (grid z)
 };
 
 // ------------------------------------------------------------- epilogue

@@ -51,7 +51,8 @@ struct GemmPlan {
     int wnw;        // wide: wavefronts along N (the rest are along M)
     int ksplit;     // number of K chunks across workgroups
     int groups;     // N groups (grid x)
-    int mblocks;    // M blocks (grid y of the wide kernel)
+    int mblocks;    // M blocks (wide: grid y of 192 rows; skinny: grid z of mt 16-row tiles)
+    int mt;         // skinny: 16-row activation tiles per workgroup
     bool alds;      // skinny: stage activations through LDS
     bool ok;        // false when the shape exceeds the split-K counter space
 };
