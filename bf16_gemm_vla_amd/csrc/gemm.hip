@@ -275,7 +275,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
     X(2, 1, 16, 4) X(2, 2, 16, 4) X(2, 2, 8, 4) X(2, 4, 8, 4) X(2, 4, 4, 4) X(2, 8, 4, 4)                \
     X(4, 1, 8, 4) X(4, 2, 8, 4) X(4, 2, 4, 4) X(4, 4, 4, 4)                                              \
     X(1, 2, 8, 1) X(1, 4, 8, 1) X(1, 4, 16, 1) X(1, 8, 16, 1)                                            \
-    X(2, 2, 8, 1) X(2, 4, 8, 1) X(2, 4, 16, 1) X(2, 8, 16, 1)
+    X(2, 2, 8, 1) X(2, 4, 8, 1) X(2, 4, 16, 1) X(2, 8, 16, 1)                                            \
+    X(2, 4, 8, 2) X(4, 4, 8, 2) X(4, 4, 8, 1) X(8, 4, 8, 1)
 
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_skinny(const KArgs& ka, const GemmPlan& p, hipStream_t s) {
@@ -362,6 +363,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
             waves = 8;
             steps = chunk <= 16 ? 2 : 4;
         }
+        // FP8 weights, plain epilogue, more than 32 rows: two 16-column tiles
+        // x two row halves per workgroup read 36% fewer bytes per CU than one
+        // tile x all rows (the 1024 -> 4096 up-projection: 5.4 -> 5.1 us)
+        if (wt == WType::FP8 && epi == Epi::PLAIN && mt_total > 2 && steps == 4)
+            return skinny_plan(M, N, K, epi, 2 * nt, steps, waves, 2, at == AType::BF16);
         return skinny_plan(M, N, K, epi, nt, steps, waves, 4, at == AType::BF16);
     }
     // Wide kernel: 192-row blocks; 256-column tiles when they give enough
