@@ -12,9 +12,11 @@
 // staged through LDS with direct global->LDS loads, and the epilogue's
 // scales/bias/residual are prefetched, so a workgroup has its whole share
 // in flight before the first MFMA; the waves split K and reduce through LDS
-// with one barrier.  When K is split across workgroups too, each workgroup
-// writes fp32 partials and counts its arrival; the last to arrive sums the
-// partials in split order (bitwise repeatable) and runs the epilogue.
+// with one barrier.  Workgroups split the output columns, then the
+// activation rows (blocks of 16-row tiles, no exchange needed), and only
+// then K: when K is split across workgroups, each workgroup writes fp32
+// partials and counts its arrival; the last to arrive sums the partials in
+// split order (bitwise repeatable) and runs the epilogue.
 #include <algorithm>
 
 #include "gemm_common.h"

@@ -296,7 +296,9 @@ void wide_gemm_kernel(KArgs a) {
     //      out first, interleaved with the first half of the MFMAs, and the
     //      next step's weight conversions fill the gaps of the second half.
     //      The stage's last step issues half of its MFMAs before the barrier,
-    //      so the matrix pipe is busy while the waves meet.
+    //      so the matrix pipe is busy while the waves meet.  MFMA blocks run
+    //      at raised wave priority, so a wave with MFMAs ready issues ahead of
+    //      its SIMD partner's memory work.
     constexpr int NM = C::NSUB * C::MSUB;        // MFMAs per step
     constexpr int HALF = NM / 2;
     F f0, f1;
@@ -311,7 +313,9 @@ void wide_gemm_kernel(KArgs a) {
             if (ks + 1 < C::NKS) {
                 __builtin_amdgcn_sched_barrier(0);
                 read_step(cur, ks + 1, of);
+                __builtin_amdgcn_s_setprio(1);
                 mfmas(cf, 0, NM);
+                __builtin_amdgcn_s_setprio(0);
                 convert(of);
 #pragma unroll
                 for (int j = 0; j < HALF; ++j) {
@@ -326,7 +330,9 @@ void wide_gemm_kernel(KArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(1);
                 mfmas(cf, 0, HALF);
+                __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * C::L));
                 __builtin_amdgcn_s_barrier();
@@ -334,7 +340,9 @@ void wide_gemm_kernel(KArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
                 read_step(bufs[(u + 1) % S], 0, of);
                 issue(kt_begin + i + S - 1, bufs[(u + S - 1) % S], i + S - 1 < nkt);
+                __builtin_amdgcn_s_setprio(1);
                 mfmas(cf, HALF, NM);
+                __builtin_amdgcn_s_setprio(0);
                 convert(of);
 #pragma unroll
                 for (int j = HALF; j < NM; ++j) {

@@ -58,10 +58,9 @@ struct GemmPlan {
 };
 
 // The first kCounterBytes of every GEMM workspace hold the split-K arrival
-// counters (one uint32 per output tile group), at the same place for every
-// shape, so one zero-filled workspace can serve calls of different shapes.
-// Its last 4 KiB are never written: an always-zero page that out-of-range
-// lanes of the wide kernel load from.
+// counters (one uint32 per skinny output group, three per wide output tile),
+// at the same place for every shape, so one zero-filled workspace can serve
+// calls of different shapes.  Its last 4 KiB are not used.
 constexpr size_t kCounterBytes = 65536;
 constexpr size_t kZeroPageOffset = kCounterBytes - 4096;
 constexpr int kMaxCounters = static_cast<int>(kZeroPageOffset / 4);
