@@ -8,6 +8,8 @@
 // reference quantizer bit for bit.
 #pragma clang fp contract(off)
 
+#include <algorithm>
+
 #include "vla_device.h"
 #include "vla_internal.h"
 
@@ -158,19 +160,31 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(const uint8_t* q, co
 // Activation quantization, pass 1: per-block absmax of 8-element chunks.
 constexpr int kActBlocks = 512;
 
+// Every thread keeps kActUnroll 16-byte loads in flight at a time.
+constexpr int kActUnroll = 4;
+
 __global__ __launch_bounds__(kThreads) void act_absmax_kernel(const uint16_t* __restrict__ A,
                                                               float* __restrict__ partial,
                                                               int64_t chunks) {
     __shared__ float red[kThreads / kWave];
     float m = 0.0f;
-    for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < chunks;
-         i += static_cast<int64_t>(gridDim.x) * kThreads) {
-        const uint4 v = *reinterpret_cast<const uint4*>(A + i * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * kActUnroll;
+    for (int64_t base = blockIdx.x * static_cast<int64_t>(kThreads) * kActUnroll + threadIdx.x; base < chunks;
+         base += stride) {
+        uint4 v[kActUnroll];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(w[j] & 0xFFFFu))));
-            m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(w[j] >> 16))));
+        for (int u = 0; u < kActUnroll; ++u) {
+            const int64_t i = base + u * kThreads;
+            v[u] = i < chunks ? *reinterpret_cast<const uint4*>(A + i * 8) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kActUnroll; ++u) {
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(w[j] & 0xFFFFu))));
+                m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(w[j] >> 16))));
+            }
         }
     }
     m = wave_max(m);
@@ -183,17 +197,70 @@ __global__ __launch_bounds__(kThreads) void act_absmax_kernel(const uint16_t* __
     }
 }
 
-// Pass 2: every block reduces the partial maxima (same order everywhere),
-// forms s_a, and encodes its share of chunks.
+// OCP E4M3 codes of fp32(x / sc) for the 8 bf16 values of one dword quad,
+// the quotient correctly rounded as IEEE division gives it.  With rcp =
+// RN(1/sc), q = RN(x * rcp) is within 2 fp32 ulps of RN(x / sc), and the
+// code only changes at the midpoints between E4M3 values (fp32 fraction
+// bits 19..0 == 0x80000 in the normal range), so the code of q is the code
+// of the exact quotient unless q lies within 3 ulps of a midpoint, below the
+// smallest normal E4M3 value (2^-6) but not zero, at/above 448, or is not
+// finite.  Such q take the exact division and the bit-level encoder; all
+// other q are zero or normal-range E4M3 values, which the hardware
+// conversion (round to nearest even, gfx950's OCP format, signed zero kept)
+// encodes two per instruction.
+__device__ __forceinline__ uint2 act_codes8(const uint32_t w[4], float sc, float rcp) {
+    float x[8], q[8];
+    bool slow[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        x[j] = __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+        q[j] = x[j] * rcp;
+        const uint32_t a = __float_as_uint(q[j]) & 0x7FFFFFFFu;
+        const bool out_of_range = (a - 0x3C800000u) >= (0x43E00000u - 0x3C800000u);   // not in [2^-6, 448)
+        const bool near_mid = ((a & 0xFFFFFu) - (0x80000u - 3u)) <= 6u;
+        slow[j] = (out_of_range && a != 0u) || near_mid;
+    }
+    uint32_t o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * h], q[4 * h + 1], 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * h + 2], q[4 * h + 3], v, true);
+        o[h] = static_cast<uint32_t>(v);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (__builtin_expect(slow[j], 0)) {
+            const uint32_t code = encode_e4m3<false>(__fdiv_rn(x[j], sc));
+            o[j >> 2] = (o[j >> 2] & ~(0xFFu << (8 * (j & 3)))) | (code << (8 * (j & 3)));
+        }
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+// Pass 2: every block loads its kActUnroll chunks per thread first, then
+// reduces the partial maxima (same order everywhere), forms s_a and encodes.
 __global__ __launch_bounds__(kThreads) void act_encode_kernel(const uint16_t* __restrict__ A,
                                                               const float* __restrict__ partial,
                                                               uint8_t* __restrict__ qa,
                                                               float* __restrict__ s_a,
-                                                              int64_t chunks, int nparts) {
+                                                              int64_t chunks) {
     __shared__ float s_sc;
+    uint4 v[kActUnroll];
+    const int64_t base = blockIdx.x * static_cast<int64_t>(kThreads) * kActUnroll + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kActUnroll; ++u) {
+        const int64_t i = base + u * kThreads;
+        v[u] = i < chunks ? *reinterpret_cast<const uint4*>(A + i * 8) : make_uint4(0, 0, 0, 0);
+    }
     if (threadIdx.x < kWave) {
+        // all partial maxima requested at once (one round trip, not one per load)
+        static_assert(kActBlocks % kWave == 0, "partials split evenly over one wave");
+        float p[kActBlocks / kWave];
+#pragma unroll
+        for (int i = 0; i < kActBlocks / kWave; ++i) p[i] = partial[threadIdx.x + i * kWave];
         float m = 0.0f;
-        for (int i = threadIdx.x; i < nparts; i += kWave) m = fmaxf(m, partial[i]);
+#pragma unroll
+        for (int i = 0; i < kActBlocks / kWave; ++i) m = fmaxf(m, p[i]);
         m = wave_max(m);
         if (threadIdx.x == 0) {
             const float sc = (m == 0.0f) ? 1.0f : __fdiv_rn(m, 448.0f);
@@ -203,18 +270,13 @@ __global__ __launch_bounds__(kThreads) void act_encode_kernel(const uint16_t* __
     }
     __syncthreads();
     const float sc = s_sc;
-    for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < chunks;
-         i += static_cast<int64_t>(gridDim.x) * kThreads) {
-        const uint4 v = *reinterpret_cast<const uint4*>(A + i * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o[2] = {0, 0};
+    const float rcp = __fdiv_rn(1.0f, sc);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint16_t h = static_cast<uint16_t>((w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-            const uint32_t code = encode_e4m3<false>(__fdiv_rn(bf16_to_f32(h), sc));
-            o[j >> 2] |= code << (8 * (j & 3));
-        }
-        *reinterpret_cast<uint2*>(qa + i * 8) = make_uint2(o[0], o[1]);
+    for (int u = 0; u < kActUnroll; ++u) {
+        const int64_t i = base + u * kThreads;
+        if (i >= chunks) continue;
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        *reinterpret_cast<uint2*>(qa + i * 8) = act_codes8(w, sc, rcp);
     }
 }
 
@@ -260,9 +322,9 @@ hipError_t launch_quantize_act(const uint16_t* A, uint8_t* qa, float* s_a, void*
     act_absmax_kernel<<<kActBlocks, kThreads, 0, s>>>(A, partial, chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t want = (chunks + kThreads - 1) / kThreads;
-    const unsigned grid = static_cast<unsigned>(want < 2048 ? (want > 0 ? want : 1) : 2048);
-    act_encode_kernel<<<grid, kThreads, 0, s>>>(A, partial, qa, s_a, chunks, kActBlocks);
+    const int64_t per_block = static_cast<int64_t>(kThreads) * kActUnroll;
+    const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, (chunks + per_block - 1) / per_block));
+    act_encode_kernel<<<grid, kThreads, 0, s>>>(A, partial, qa, s_a, chunks);
     return hipGetLastError();
 }
 

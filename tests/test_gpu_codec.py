@@ -120,6 +120,29 @@ def test_quantize_act_bit_exact(M, K):
     assert np.array_equal(qa.numpy(np.uint8).reshape(M, K), ref_q)
 
 
+@pytest.mark.parametrize("top", [0x4100, 0x3F00, 0x7F80])
+def test_quantize_act_every_bf16_value(top):
+    """Every finite bf16 value below `top` (both signs) in one tensor: the
+    codes must equal the oracle's IEEE-division codes bit for bit (the fast
+    reciprocal path decides every code away from E4M3 rounding midpoints)."""
+    pos = np.arange(0, top, dtype=np.uint16)
+    vals = np.concatenate([pos, pos | np.uint16(0x8000)])
+    K = 256
+    M = (vals.size + K - 1) // K
+    A = np.zeros(M * K, np.uint16)
+    A[:vals.size] = vals
+    A = A.reshape(M, K)
+    qa, sa = Guarded(M * K), Guarded(16)
+    ws = zeros_ws(vla.vla_quantize_act_workspace_bytes(M, K))
+    vla.vla_quantize_act(dev(A), qa.t, sa.t, ws, ws.numel(), M, K)
+    qa.check()
+    ref_q, ref_s = oracle.quantize_act(A)
+    assert sa.numpy(np.float32)[0] == ref_s
+    got = qa.numpy(np.uint8).reshape(M, K)
+    bad = got != ref_q
+    assert not bad.any(), f"{bad.sum()} codes differ, first input {hex(int(A[bad][0]))}"
+
+
 def test_quantize_act_all_zero():
     M, K = 8, 64
     A = np.zeros((M, K), np.uint16)
