@@ -46,6 +46,7 @@ SIGNATURES = {
     "vla_quantize_act_workspace_bytes": (SZ, [I64, I64]),
     "vla_quantize_act": (INT, [P, P, P, P, SZ, I64, I64, P]),
     "vla_gemm_workspace_bytes": (SZ, [I64, I64, I64, INT]),
+    "vla_gemm_supported": (INT, [I64, I64, I64, INT, INT, INT]),
     "vla_gemm_fp8w": (INT, [P, P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_gemm_bf16": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_gemm_fp8w_gelu_mul": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
@@ -122,6 +123,11 @@ def vla_quantize_act_workspace_bytes(M: int, K: int) -> int:
 
 def vla_gemm_workspace_bytes(M: int, N: int, K: int, wfmt: int) -> int:
     return load().vla_gemm_workspace_bytes(M, N, K, wfmt)
+
+
+def vla_gemm_supported(M: int, N: int, K: int, wfmt: int, fp8_act: bool = False, gelu_mul: bool = False) -> int:
+    """Status code (0 = supported) for a GEMM shape; host only, no device work."""
+    return load().vla_gemm_supported(M, N, K, wfmt, int(bool(fp8_act)), int(bool(gelu_mul)))
 
 
 def vla_mlp_chain_scratch_bytes(M: int, H: int, I: int) -> int:

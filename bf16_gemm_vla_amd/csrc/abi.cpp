@@ -62,8 +62,8 @@ int check_mnk(const char* fn, int64_t M, int64_t N, int64_t K) {
 
 int run_gemm(const char* fn, const vla::GemmProblem& pr, size_t ws_bytes, hipStream_t s) {
     const vla::GemmPlan p = vla::plan_gemm(pr.M, pr.N, pr.K, pr.atype, pr.wtype, pr.epi);
-    if (!p.ok)
-        return fail(VLA_ESHAPE, fn, "M=%lld N=%lld K=%lld needs more split-K counters than the workspace holds",
+    if (!vla::plan_dispatchable(p, pr.atype, pr.wtype, pr.epi))
+        return fail(VLA_ESHAPE, fn, "M=%lld N=%lld K=%lld exceeds the kernels' limits (split-K counters, 2 GiB operands)",
                     (long long)pr.M, (long long)pr.N, (long long)pr.K);
     const size_t need = vla::gemm_ws_bytes(p, pr.M, pr.N);
     if (ws_bytes < need)
@@ -261,6 +261,23 @@ size_t vla_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int wfmt) {
             if (b > best) best = b;
         }
     return best;
+}
+
+int vla_gemm_supported(int64_t M, int64_t N, int64_t K, int wfmt, int fp8_act, int gelu_mul) {
+    const char* fn = "vla_gemm_supported";
+    if (int rc = check_mnk(fn, M, N, K)) return rc;
+    if (wfmt != VLA_WFMT_BF16 && wfmt != VLA_WFMT_E4M3_OCP) return fail(VLA_EINVAL, fn, "wfmt=%d", wfmt);
+    const vla::AType at = fp8_act ? vla::AType::FP8 : vla::AType::BF16;
+    const vla::WType wt = (wfmt == VLA_WFMT_BF16) ? vla::WType::BF16 : vla::WType::FP8;
+    const vla::Epi epi = gelu_mul ? vla::Epi::GELU_MUL : vla::Epi::PLAIN;
+    if ((gelu_mul || fp8_act) && wt != vla::WType::FP8) return fail(VLA_EINVAL, fn, "fp8_act and gelu_mul need FP8 weights");
+    if (gelu_mul && fp8_act) return fail(VLA_EINVAL, fn, "gelu_mul takes bf16 activations");
+    if (gelu_mul && (N % 32) != 0) return fail(VLA_ESHAPE, fn, "gelu_mul needs N = 2I with I a multiple of 16");
+    const vla::GemmPlan p = vla::plan_gemm(M, N, K, at, wt, epi);
+    if (!vla::plan_dispatchable(p, at, wt, epi))
+        return fail(VLA_ESHAPE, fn, "M=%lld N=%lld K=%lld exceeds the kernels' limits", (long long)M, (long long)N,
+                    (long long)K);
+    return VLA_OK;
 }
 
 int vla_gemm_fp8w(const void* A, const float* s_a, const uint8_t* Wq, const float* s_w,

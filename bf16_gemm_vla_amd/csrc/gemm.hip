@@ -451,4 +451,14 @@ hipError_t launch_gemm(const GemmProblem& pr, hipStream_t s) {
     return launch_gemm_plan(pr, plan_gemm(pr.M, pr.N, pr.K, pr.atype, pr.wtype, pr.epi), s);
 }
 
+bool plan_dispatchable(const GemmPlan& p, AType at, WType wt, Epi epi) {
+    if (!p.ok) return false;
+    if (p.kernel != 0) return wide_dispatchable(p, at, wt, epi);
+#define VLA_CASE(NT_, S_, W_, MT_) \
+    if (p.nt == NT_ && p.steps == S_ && p.waves == W_ && p.mt == MT_) return !(epi == Epi::GELU_MUL && NT_ < 2);
+    VLA_SKINNY_CONFIGS(VLA_CASE)
+#undef VLA_CASE
+    return false;
+}
+
 }  // namespace vla

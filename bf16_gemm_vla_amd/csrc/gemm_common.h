@@ -181,5 +181,6 @@ __device__ __forceinline__ void splitk_reset(uint32_t* tickets, int slot) {
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStream_t s);
 size_t wide_part_bytes(const GemmPlan& p);
+bool wide_dispatchable(const GemmPlan& p, AType at, WType wt, Epi epi);
 
 }  // namespace vla

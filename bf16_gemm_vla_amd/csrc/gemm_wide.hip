@@ -559,6 +559,12 @@ size_t wide_part_bytes(const GemmPlan& p) {
     return static_cast<size_t>(p.ksplit) * p.mblocks * p.groups * (p.waves * 64) * (nsub * msub * 4) * 16;
 }
 
+// Wide tilings compiled in, per operand class: (BN, waves along N, K per stage).
+#define VLA_WIDE_GELU(X) X(256, 2, 64) X(256, 4, 64)
+#define VLA_WIDE_BF16W(X) X(128, 2, 64) X(128, 4, 64)
+#define VLA_WIDE_FP8A(X) X(256, 2, 64) X(128, 2, 64) X(128, 2, 128) X(128, 4, 128)
+#define VLA_WIDE_BF16A(X) X(256, 2, 64) X(128, 2, 64) X(256, 4, 64) X(128, 4, 64)
+
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStream_t s) {
     const dim3 grid(p.groups, p.mblocks, p.ksplit);
@@ -568,24 +574,34 @@ hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStrea
         return hipGetLastError();                                                       \
     }
     if constexpr (EPI == Epi::GELU_MUL) {
-        VLA_WIDE(256, 2, 64)
-        VLA_WIDE(256, 4, 64)
+        VLA_WIDE_GELU(VLA_WIDE)
     } else if constexpr (WT == WType::BF16) {
-        VLA_WIDE(128, 2, 64)
-        VLA_WIDE(128, 4, 64)
+        VLA_WIDE_BF16W(VLA_WIDE)
     } else if constexpr (AT == AType::FP8) {
-        VLA_WIDE(256, 2, 64)
-        VLA_WIDE(128, 2, 64)
-        VLA_WIDE(128, 2, 128)
-        VLA_WIDE(128, 4, 128)
+        VLA_WIDE_FP8A(VLA_WIDE)
     } else {
-        VLA_WIDE(256, 2, 64)
-        VLA_WIDE(128, 2, 64)
-        VLA_WIDE(256, 4, 64)
-        VLA_WIDE(128, 4, 64)
+        VLA_WIDE_BF16A(VLA_WIDE)
     }
 #undef VLA_WIDE
     return hipErrorInvalidValue;
+}
+
+bool wide_dispatchable(const GemmPlan& p, AType at, WType wt, Epi epi) {
+#define VLA_WIDE(BN_, WNW_, BK_) \
+    if (p.nt == BN_ && p.wnw == WNW_ && p.waves == 2 * WNW_ && p.steps == BK_) return true;
+    if (epi == Epi::GELU_MUL) {
+        if (at != AType::BF16 || wt != WType::FP8) return false;
+        VLA_WIDE_GELU(VLA_WIDE)
+    } else if (wt == WType::BF16) {
+        if (at != AType::BF16) return false;
+        VLA_WIDE_BF16W(VLA_WIDE)
+    } else if (at == AType::FP8) {
+        VLA_WIDE_FP8A(VLA_WIDE)
+    } else {
+        VLA_WIDE_BF16A(VLA_WIDE)
+    }
+#undef VLA_WIDE
+    return false;
 }
 
 template hipError_t launch_wide<AType::BF16, WType::FP8, Epi::PLAIN>(const gemm_detail::KArgs&, const GemmPlan&, hipStream_t);

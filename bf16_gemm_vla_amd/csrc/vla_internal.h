@@ -68,5 +68,7 @@ constexpr int kMaxCounters = static_cast<int>(kZeroPageOffset / 4);
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi);
 size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N);
 hipError_t launch_gemm(const GemmProblem& pr, hipStream_t s);
+// Whether the plan names a compiled kernel configuration (host only).
+bool plan_dispatchable(const GemmPlan& p, AType at, WType wt, Epi epi);
 
 }  // namespace vla

@@ -121,14 +121,21 @@ int vla_quantize_act(const uint16_t *A, uint8_t *qa, float *s_a, void *ws, size_
 
 /* Workspace for vla_gemm_fp8w / vla_gemm_bf16 / vla_gemm_fp8w_gelu_mul at
  * this shape (N = weight rows; for gelu_mul N = 2 I).  Its first 64 KiB
- * hold one arrival counter per output tile group (the same place for every
- * shape); the rest holds split-K partial sums.  The workspace must be
+ * hold the split-K arrival counters (the same place for every shape); the
+ * rest holds split-K partial sums.  The workspace must be
  * ZERO-FILLED before its first use; every completed call leaves the
  * counters at zero again, so one zeroed buffer (sized for the largest
  * shape) serves any number of later calls and graph replays, of any
  * shapes, that run one after another.  Calls that run concurrently must
  * not share a workspace. */
 size_t vla_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int wfmt);
+
+/* Host-only query, no device work: VLA_OK when a GEMM of this shape has a
+ * compiled kernel configuration (wfmt VLA_WFMT_BF16 or VLA_WFMT_E4M3_OCP;
+ * fp8_act: FP8 x FP8 with OCP activations; gelu_mul: the merged gate/up
+ * GEMM with N = 2I), else the status the GEMM call itself would return
+ * (EINVAL, ESHAPE). */
+int vla_gemm_supported(int64_t M, int64_t N, int64_t K, int wfmt, int fp8_act, int gelu_mul);
 
 /* Y = bf16( s[n] * sum_k A[m,k] * dec(Wq[n,k]) + bias[n] ), optionally
  * followed by Y = bf16(residual + Y).
@@ -145,7 +152,8 @@ size_t vla_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int wfmt);
  * y = acc * s_w[n] (FP8 x FP8: acc * (s_a * s_w[n])) + bias, rounded to
  * bf16 nearest-even; residual added in fp32 and rounded again.  The
  * summation order is fixed per shape, so repeated calls are bitwise equal.
- * Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP. */
+ * Errors: EINVAL, ESHAPE (also when M > 64 and A or Wq reaches 2 GiB: the
+ * wide kernel addresses them with 32-bit offsets), EALIGN, EWORKSPACE, EHIP. */
 int vla_gemm_fp8w(const void *A, const float *s_a, const uint8_t *Wq, const float *s_w,
                   const uint16_t *bias, const uint16_t *residual, uint16_t *Y, void *ws,
                   size_t ws_bytes, int64_t M, int64_t N, int64_t K, void *stream);

@@ -138,3 +138,31 @@ def test_chain_handle_state_machine(lib):
 def test_python_wrapper_raises(lib):
     with pytest.raises(RuntimeError, match="vla_gemm_bf16: unsupported shape"):
         vla.vla_gemm_bf16(A16, A16, None, None, A16, A16, 1 << 20, 50, 20, 128, stream=0)
+
+
+def test_every_planned_shape_has_a_compiled_kernel(lib):
+    """The planner only ever names kernel configurations the library holds:
+    skinny shapes of every row count, the wide encoder shapes and ragged
+    tiles, for every operand class."""
+    Ns = (16, 32, 48, 64, 96, 160, 272, 1024, 2048, 4096, 8192, 16384)
+    Ks = (32, 64, 96, 160, 1024, 1056, 2048, 4096, 16384)
+    Ms = tuple(range(1, 65)) + (65, 100, 129, 191, 192, 193, 571, 768, 1000)
+    for M in Ms:
+        for N in Ns:
+            for K in Ks:
+                assert vla.vla_gemm_supported(M, N, K, vla.VLA_WFMT_E4M3_OCP) == 0, (M, N, K, "w8a16")
+                assert vla.vla_gemm_supported(M, N, K, vla.VLA_WFMT_BF16) == 0, (M, N, K, "bf16")
+                assert vla.vla_gemm_supported(M, N, K, vla.VLA_WFMT_E4M3_OCP, fp8_act=True) == 0, (M, N, K, "fp8")
+                if N % 32 == 0:
+                    assert vla.vla_gemm_supported(M, N, K, vla.VLA_WFMT_E4M3_OCP, gelu_mul=True) == 0, (M, N, K, "gelu")
+
+
+def test_gemm_supported_rejects_bad_arguments(lib):
+    assert vla.vla_gemm_supported(0, 64, 64, 1) == vla.VLA_EINVAL
+    assert vla.vla_gemm_supported(4, 24, 64, 1) == vla.VLA_ESHAPE
+    assert vla.vla_gemm_supported(4, 64, 48, 1) == vla.VLA_ESHAPE
+    assert vla.vla_gemm_supported(4, 64, 64, 7) == vla.VLA_EINVAL
+    assert vla.vla_gemm_supported(4, 64, 64, vla.VLA_WFMT_BF16, fp8_act=True) == vla.VLA_EINVAL
+    assert vla.vla_gemm_supported(4, 48, 64, 1, gelu_mul=True) == vla.VLA_ESHAPE
+    # the wide kernel addresses operands with 32-bit offsets
+    assert vla.vla_gemm_supported(768, 1 << 20, 4096, 1) == vla.VLA_ESHAPE
