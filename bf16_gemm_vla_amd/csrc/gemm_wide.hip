@@ -393,6 +393,10 @@ void wide_gemm_kernel(KArgs a) {
             else ein[ns][rq] = EpiIn{};
         }
     const float sa = (AT == AType::FP8) ? *a.s_a : 1.0f;
+    // Wait for these loads here, once: gfx9 counts stores in vmcnt too, so a
+    // wait for them placed after the first output stores would also wait for
+    // every store issued so far.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
     // ---- epilogue.  acc[ns][ms] register r: row (output channel) 8*(r/4) + 4*(lane/32) + r%4
     //      of the 32-column sub-tile, activation row lane%32 of the 32-row sub-tile.
@@ -528,26 +532,31 @@ void wide_gemm_kernel(KArgs a) {
             }
         }
         __syncthreads();
+        // LDS rows -> 16-byte streaming stores (the output is not read again
+        // by this kernel).  Only calls with a residual load anything here, so
+        // the plain path issues stores back to back with no vmcnt wait.
+        auto store_pass = [&](auto WITH_RESID) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = tid; c < 64 * CPRO; c += C::THREADS) {
-            const int row = c / CPRO, ch = c % CPRO;
-            const int gm = m0 + (row >> 5) * 96 + ms * 32 + (row & 31);
-            const int n = g * OUT_W + ch * 8;
-            if (gm >= a.M || n >= outN) continue;
-            const uint8_t* src = ((row >> 5) ? pair1 : pair0) + (row & 31) * OSTRIDE + ch * 16;
-            uint4 v = *reinterpret_cast<const uint4*>(src);
-            if constexpr (EPI == Epi::PLAIN) {
-                if (a.resid) {
+            for (int c = tid; c < 64 * CPRO; c += C::THREADS) {
+                const int row = c / CPRO, ch = c % CPRO;
+                const int gm = m0 + (row >> 5) * 96 + ms * 32 + (row & 31);
+                const int n = g * OUT_W + ch * 8;
+                if (gm >= a.M || n >= outN) continue;
+                const uint8_t* src = ((row >> 5) ? pair1 : pair0) + (row & 31) * OSTRIDE + ch * 16;
+                uint4 v = *reinterpret_cast<const uint4*>(src);
+                if constexpr (decltype(WITH_RESID)::value) {
                     const uint4 r = *reinterpret_cast<const uint4*>(a.resid + static_cast<int64_t>(gm) * a.N + n);
                     v.x = add_resid2(v.x, r.x);
                     v.y = add_resid2(v.y, r.y);
                     v.z = add_resid2(v.z, r.z);
                     v.w = add_resid2(v.w, r.w);
                 }
+                __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w},
+                                            reinterpret_cast<u32x4_t*>(a.Y + static_cast<int64_t>(gm) * outN + n));
             }
-            // streaming store: the output is not read again by this kernel
-            __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(a.Y + static_cast<int64_t>(gm) * outN + n));
-        }
+        };
+        if (EPI == Epi::PLAIN && a.resid) store_pass(std::true_type{});
+        else store_pass(std::false_type{});
     }
 }
 
