@@ -105,19 +105,22 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
     const int ntiles = a.N >> 4;
     const int mrow = lane & 15, q = lane >> 4;
 
-    // 1. all weight fragments of this wave in flight
-    WF wf[S][NT];
+    // Loads, in this order: the epilogue inputs of the fragments this wave
+    // finishes, the activation chunk (straight into LDS, ALDS), then exactly
+    // S*NT weight-fragment loads (out-of-range ones read fragment 0 and are
+    // zeroed).  vmcnt retires in order, so waiting until only the weight
+    // loads are outstanding means the activations have landed: the barrier
+    // and the LDS operand reads then overlap the weights' HBM latency.
+    // 1. epilogue inputs
+    EpiIn ein[R];
+    const float sa = (AT == AType::FP8) ? *a.s_a : 1.0f;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const bool ok = kbase + s < ksteps;
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int tile = skinny_tile<EPI, NT>(g, j, a.N);
-            const int64_t fi = static_cast<int64_t>(tile) * ksteps + kbase + s;
-            const uint8_t* p = static_cast<const uint8_t*>(a.W) + (fi * 64 + lane) * WB;
-            if (ok && tile < ntiles) wf[s][j] = *reinterpret_cast<const WF*>(p);
-            else wf[s][j] = WF{};
-        }
+    for (int r = 0; r < R; ++r) {
+        const int pair = wave + r * WAVES, jo = pair / MT, mt = pair % MT;
+        const int tile = skinny_tile<EPI, NT>(g, jo < JO ? jo : 0, a.N);
+        const int row = mt * 16 + mrow;
+        if (pair < PAIRS && tile < ntiles && row < mrows)
+            ein[r] = load_epi<WT, EPI>(a, m0 + row, tile * 16 + 4 * q, a.ksplit == 1);
     }
     // 2. activation fragments: row m0 + mt*16 + lane%16, 8 K values at 8*(lane/16)
     AF af[S][MT];
@@ -151,21 +154,30 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
             }
         }
     }
-    // 3. epilogue inputs of the fragments this wave finishes (overlaps the loads)
-    EpiIn ein[R];
-    const float sa = (AT == AType::FP8) ? *a.s_a : 1.0f;
+    // 3. all weight fragments of this wave in flight
+    WF wf[S][NT];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int pair = wave + r * WAVES, jo = pair / MT, mt = pair % MT;
-        const int tile = skinny_tile<EPI, NT>(g, jo < JO ? jo : 0, a.N);
-        const int row = mt * 16 + mrow;
-        if (pair < PAIRS && tile < ntiles && row < mrows)
-            ein[r] = load_epi<WT, EPI>(a, m0 + row, tile * 16 + 4 * q, a.ksplit == 1);
+    for (int s = 0; s < S; ++s) {
+        const bool ok = kbase + s < ksteps;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int tile = skinny_tile<EPI, NT>(g, j, a.N);
+            const bool valid = ok && tile < ntiles;
+            const int64_t fi = valid ? static_cast<int64_t>(tile) * ksteps + kbase + s : 0;
+            const WF w = *reinterpret_cast<const WF*>(static_cast<const uint8_t*>(a.W) + (fi * 64 + lane) * WB);
+            wf[s][j] = valid ? w : WF{};
+        }
     }
     if constexpr (ALDS) {
-        // every wave's direct-to-LDS loads have landed, then read fragments
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // the activations (and epilogue inputs) have landed once at most the
+        // S*NT weight loads are outstanding; then read the LDS fragments
+        constexpr int NW = S * NT;
+        static_assert(NW <= 63, "the weight loads fit the vmcnt field");
+        __builtin_amdgcn_s_waitcnt((NW & 15) | ((NW >> 4) << 14) | 0x0F70);
+        // a bare barrier: __syncthreads() would add a release fence that
+        // waits for the weight loads too
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const bool ok = kbase + s < ksteps;

@@ -531,7 +531,11 @@ void wide_gemm_kernel(KArgs a) {
                 }
             }
         }
-        __syncthreads();
+        // LDS writes done, then a bare barrier: __syncthreads() would add a
+        // release fence that waits for the previous pass's global stores
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         // LDS rows -> 16-byte streaming stores (the output is not read again
         // by this kernel).  Only calls with a residual load anything here, so
         // the plain path issues stores back to back with no vmcnt wait.
