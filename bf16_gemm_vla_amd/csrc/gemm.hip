@@ -409,13 +409,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
             p.groups = static_cast<int>((tiles + 7) / 8);
         }
     }
-    if (at == AType::FP8) {
-        p.waves = (p.nt == 256) ? 4 : 8;
-        p.steps = (p.nt == 256) ? 64 : 128;    // K values per pipeline stage
-    } else {
-        p.waves = 8;
-        p.steps = 64;
-    }
+    p.waves = 8;
+    p.steps = (at == AType::FP8 && p.nt == 128) ? 128 : 64;   // K values per pipeline stage
     p.wnw = p.waves / 2;
     const int64_t kt_total = (K + p.steps - 1) / p.steps;
     const int64_t base = static_cast<int64_t>(p.groups) * p.mblocks;

@@ -1,9 +1,9 @@
 // Wide GEMM (M > 64) for gfx950.
 //
 // Output tile 192 (rows of A) x BN (weight rows, 256 or 128) per workgroup
-// of 4 waves, one per SIMD, arranged 2 x 2; each wave owns a 96 x BN/2
-// tile (3 x BN/64 accumulators of 32 x 32).  MFMA shapes with the full
-// gfx950 rate: v_mfma_f32_32x32x16_bf16 for bf16 activations (FP8 weights
+// of 8 waves, two per SIMD, arranged 2 (rows) x 4 (columns); each wave
+// owns a 96 x BN/4 tile (3 x BN/128 accumulators of 32 x 32).  MFMA shapes
+// with the full gfx950 rate: v_mfma_f32_32x32x16_bf16 for bf16 activations (FP8 weights
 // are converted to bf16 exactly in registers) and the scaled
 // v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit E8M0 scales) for
 // FP8 x FP8.  The packed weight tile is the MFMA "A" operand (32 output
@@ -11,11 +11,11 @@
 // accumulator holds runs of 4 consecutive output channels of one row.
 //
 // Operands move global -> LDS with buffer loads that write LDS directly
-// (16 bytes per lane, 1 KiB per wave instruction), 64 K values per stage,
-// in a ring of four stage buffers:
-//  * activations row-major, 128 (bf16) or 64 (FP8) bytes of K per row, the
-//    16-byte chunks of each row XOR-swizzled so the 32-row operand reads hit
-//    distinct banks;
+// (16 bytes per lane, 1 KiB per wave instruction), 64 K values per stage
+// (128 for FP8 x FP8 on 128-column tiles), in a ring of four stage buffers:
+//  * activations row-major, 128 bytes of K per row (64 for FP8 on
+//    256-column tiles), the 16-byte chunks of each row XOR-swizzled so the
+//    32-row operand reads hit distinct banks;
 //  * weights in their packed fragment order, one 1 KiB (FP8) or 2 KiB
 //    (bf16) block per 16-row tile; FP8 blocks of odd tiles have their
 //    128-byte halves swapped, so the two 16-row halves of a 32-row operand
@@ -57,15 +57,20 @@ struct WideCfg {
     static constexpr int WTB = (BK / 32) * 64 * WLB;            // W bytes per 16-row tile per stage
     static constexpr int A_BYTES = kWideBM * ARB;
     static constexpr int W_BYTES = (BN / 16) * WTB;
-    static constexpr int STAGE = A_BYTES + W_BYTES;
     static constexpr int A_LOADS = A_BYTES / 1024;
+    // activation load slots per stage, rounded up to a multiple of the wave
+    // count: the extra slots load nothing (offsets outside the resource) into
+    // a pad of the stage buffer, so every wave still issues the same loads
+    static constexpr int A_SLOTS = (A_LOADS + WAVES - 1) / WAVES * WAVES;
+    static constexpr int A_REGION = A_SLOTS * 1024;
+    static constexpr int STAGE = A_REGION + W_BYTES;
     static constexpr int W_LOADS = W_BYTES / 1024;
-    static constexpr int LA = A_LOADS / WAVES;                  // activation loads per wave per stage
-    static constexpr int L = (A_LOADS + W_LOADS) / WAVES;       // loads per wave per stage
+    static constexpr int LA = A_SLOTS / WAVES;                  // activation slots per wave per stage
+    static constexpr int L = LA + W_LOADS / WAVES;              // loads per wave per stage
     static constexpr int MSUB = 3;                              // 96-row wave tile
     static constexpr int WN = BN / WNW;                         // wave tile width
     static constexpr int NSUB = WN / 32;
-    static_assert(A_LOADS % WAVES == 0 && W_LOADS % WAVES == 0, "loads split evenly over the waves");
+    static_assert(A_BYTES % 1024 == 0 && W_LOADS % WAVES == 0, "loads split evenly over the waves");
     static_assert(kWideStages * STAGE <= 160 * 1024, "the stage ring fits the LDS");
     static_assert(L <= 15, "the partial vmcnt wait fits its field");
 };
@@ -155,8 +160,9 @@ void wide_gemm_kernel(KArgs a) {
 
     // ---- per-lane source offsets of this wave's L loads per stage (without
     //      the stage term) and the K position each covers (ragged-K mask).
-    //      Load t of wave w is instruction q = w + 4t of the stage; it fills
-    //      LDS bytes q*1024 .. +1023 of the stage buffer (A first, then W).
+    //      Load t of wave w is instruction q = w + WAVES*t of the stage; it
+    //      fills LDS bytes q*1024 .. +1023 of the stage buffer (A slots
+    //      first, then W).
     uint32_t voff[C::L], voffT[C::L];   // voffT: the same for the ragged last K tile
     const int krem = a.K - (kt_total - 1) * BK;         // K values in the last K tile
 #pragma unroll
@@ -167,10 +173,10 @@ void wide_gemm_kernel(KArgs a) {
             const int row = q * C::RPI + lane / C::CPR, pos = lane % C::CPR;
             const int c = (C::CPR == 8) ? (pos ^ ((row >> 1) & 7)) : (pos ^ ((row >> 2) & 3));
             const int gm = m0 + row;
-            voff[t] = gm < a.M ? static_cast<uint32_t>((gm * a.K) * C::AB + c * 16) : kOOB;
+            voff[t] = (q < C::A_LOADS && gm < a.M) ? static_cast<uint32_t>((gm * a.K) * C::AB + c * 16) : kOOB;
             in_tail = c * (16 / C::AB) < krem;
         } else {
-            const int j = q - C::A_LOADS;
+            const int j = q - C::A_SLOTS;
             constexpr int PER_TILE = C::WTB / 1024;
             const int tt = j / PER_TILE, h = j % PER_TILE;
             const int gt = wide_wtile<EPI, BN, C::WN>(g, tt, a.N);
@@ -205,11 +211,11 @@ void wide_gemm_kernel(KArgs a) {
     const int aoff = (wm * 96 + l32) * C::ARB;
     int woff;
     if constexpr (WT == WType::BF16)
-        woff = C::A_BYTES + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 16 + g2 * 256;
+        woff = C::A_REGION + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 16 + g2 * 256;
     else if constexpr (AT == AType::BF16)
-        woff = C::A_BYTES + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 8 + (g2 ^ oddW) * 128;
+        woff = C::A_REGION + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 8 + (g2 ^ oddW) * 128;
     else
-        woff = C::A_BYTES + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 8 + g2 * 512;
+        woff = C::A_REGION + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 8 + g2 * 512;
 
     auto read_step = [&](const uint8_t* buf, int ks, F& f) __attribute__((always_inline)) {
         if constexpr (AT == AType::BF16) {
@@ -573,10 +579,10 @@ size_t wide_part_bytes(const GemmPlan& p) {
 }
 
 // Wide tilings compiled in, per operand class: (BN, waves along N, K per stage).
-#define VLA_WIDE_GELU(X) X(256, 2, 64) X(256, 4, 64)
-#define VLA_WIDE_BF16W(X) X(128, 2, 64) X(128, 4, 64)
-#define VLA_WIDE_FP8A(X) X(256, 2, 64) X(128, 2, 64) X(128, 2, 128) X(128, 4, 128)
-#define VLA_WIDE_BF16A(X) X(256, 2, 64) X(128, 2, 64) X(256, 4, 64) X(128, 4, 64)
+#define VLA_WIDE_GELU(X) X(256, 4, 64)
+#define VLA_WIDE_BF16W(X) X(128, 4, 64)
+#define VLA_WIDE_FP8A(X) X(256, 4, 64) X(128, 4, 128)
+#define VLA_WIDE_BF16A(X) X(256, 4, 64) X(128, 4, 64)
 
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStream_t s) {
