@@ -164,9 +164,22 @@ def main():
     achieved = bytes_step / (ms_graph * 1e-3 / args.steps) / 1e9
     floor_buf = torch.zeros(1, device=dev)
     floor_us = time_graph(lambda i: floor_buf.fill_(1.0), args.steps) * 1000.0 / args.steps
+    # streaming-read floor: one launch that only reads one call's 4 MiB of
+    # packed weights (same cold rotation as the GEMM pair), best launch size
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    read_us = {}
+    for blocks in (256, 512, 1024, 2048):
+        def rd(i, blocks=blocks):
+            q = (qs_up if i % 2 == 0 else qs_dn)[(i // 2) % copies]
+            vla.vla_probe_stream_read(q, q.numel(), sink, blocks)
+        read_us[blocks] = time_graph(rd, 2 * args.steps) * 1000.0 / (2 * args.steps)
+    best_blocks = min(read_us, key=read_us.get)
     extra = {
         "us_per_call_eager": round(ms_eager * 1000.0 / (2 * args.steps), 3),
         "graph_launch_floor_us": round(floor_us, 3),
+        "stream_read_4MiB_us": round(read_us[best_blocks], 3),
+        "stream_read_4MiB_GBps": round(q_up.numel() / (read_us[best_blocks] * 1e-6) / 1e9, 1),
+        "stream_read_blocks": best_blocks,
         "weight_copies": copies,
     }
 
@@ -270,6 +283,11 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
             out[f"{name}_{tag}_frac"] = round(tf / peak, 4)
         ms = time_graph(actq, 20)
         out[f"{name}_act_quant_us"] = round(ms * 1000.0 / 20, 2)
+
+        def actq_static(i):   # frozen scale (the one just calibrated): one pass, no absmax
+            vla.vla_quantize_act_static(A, sa, qa, Mw, k)
+        ms = time_graph(actq_static, 20)
+        out[f"{name}_act_quant_static_us"] = round(ms * 1000.0 / 20, 2)
 
     log("secondary: 18-layer chain")
     L = 18

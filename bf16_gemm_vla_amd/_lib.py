@@ -45,6 +45,8 @@ SIGNATURES = {
     "vla_reencode_fnuz_to_ocp": (INT, [P, P, P, P, I64, I64, INT, P]),
     "vla_quantize_act_workspace_bytes": (SZ, [I64, I64]),
     "vla_quantize_act": (INT, [P, P, P, P, SZ, I64, I64, P]),
+    "vla_quantize_act_static": (INT, [P, P, P, I64, I64, P]),
+    "vla_probe_stream_read": (INT, [P, SZ, P, INT, P]),
     "vla_gemm_workspace_bytes": (SZ, [I64, I64, I64, INT]),
     "vla_gemm_supported": (INT, [I64, I64, I64, INT, INT, INT]),
     "vla_gemm_fp8w": (INT, [P, P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
@@ -155,6 +157,16 @@ def vla_reencode_fnuz_to_ocp(q_fnuz, s_fnuz, q_ocp, s_ocp, N, K, layout, stream=
 def vla_quantize_act(A, qa, s_a, ws, ws_bytes, M, K, stream=None):
     _check(load().vla_quantize_act(_ptr(A), _ptr(qa), _ptr(s_a), _ptr(ws), ws_bytes, M, K,
                                    _stream(stream)), "vla_quantize_act")
+
+
+def vla_probe_stream_read(src, nbytes, sink, blocks, stream=None):
+    _check(load().vla_probe_stream_read(_ptr(src), nbytes, _ptr(sink), blocks, _stream(stream)),
+           "vla_probe_stream_read")
+
+
+def vla_quantize_act_static(A, s_a, qa, M, K, stream=None):
+    _check(load().vla_quantize_act_static(_ptr(A), _ptr(s_a), _ptr(qa), M, K, _stream(stream)),
+           "vla_quantize_act_static")
 
 
 # ------------------------------------------------------------------- GEMM

@@ -239,6 +239,7 @@ int vla_quantize_act(const uint16_t* A, uint8_t* qa, float* s_a, void* ws, size_
                      int64_t M, int64_t K, void* stream) {
     const char* fn = "vla_quantize_act";
     if (int rc = check_mnk(fn, M, 16, K)) return rc;
+    if (M * K > (int64_t(1) << 40)) return fail(VLA_ESHAPE, fn, "M*K=%lld too large", (long long)(M * K));
     REQUIRE_PTR(A);
     REQUIRE_PTR(qa);
     REQUIRE_PTR(s_a);
@@ -246,6 +247,27 @@ int vla_quantize_act(const uint16_t* A, uint8_t* qa, float* s_a, void* ws, size_
     const size_t need = vla::quantize_act_ws_bytes(M, K);
     if (ws_bytes < need) return fail(VLA_EWORKSPACE, fn, "workspace %zu bytes < required %zu", ws_bytes, need);
     hipError_t e = vla::launch_quantize_act(A, qa, s_a, ws, M, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
+}
+
+int vla_quantize_act_static(const uint16_t* A, const float* s_a, uint8_t* qa, int64_t M, int64_t K, void* stream) {
+    const char* fn = "vla_quantize_act_static";
+    if (int rc = check_mnk(fn, M, 16, K)) return rc;
+    if (M * K > (int64_t(1) << 40)) return fail(VLA_ESHAPE, fn, "M*K=%lld too large", (long long)(M * K));
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(s_a);
+    REQUIRE_PTR(qa);
+    hipError_t e = vla::launch_quantize_act_static(A, s_a, qa, M, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
+}
+
+int vla_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, void* stream) {
+    const char* fn = "vla_probe_stream_read";
+    REQUIRE_PTR(src);
+    REQUIRE_PTR(sink);
+    if (bytes == 0 || bytes % 16 != 0) return fail(VLA_ESHAPE, fn, "bytes=%zu must be a positive multiple of 16", bytes);
+    if (blocks <= 0 || blocks > 65536) return fail(VLA_EINVAL, fn, "blocks=%d outside 1..65536", blocks);
+    hipError_t e = vla::launch_stream_read(src, bytes, sink, blocks, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
 }
 

@@ -239,6 +239,8 @@ __device__ __forceinline__ uint2 act_codes8(const uint32_t w[4], float sc, float
 
 // Pass 2: every block loads its kActUnroll chunks per thread first, then
 // reduces the partial maxima (same order everywhere), forms s_a and encodes.
+// STATIC: s_a is a given (calibrated) scale, read instead of formed.
+template <bool STATIC>
 __global__ __launch_bounds__(kThreads) void act_encode_kernel(const uint16_t* __restrict__ A,
                                                               const float* __restrict__ partial,
                                                               uint8_t* __restrict__ qa,
@@ -252,7 +254,9 @@ __global__ __launch_bounds__(kThreads) void act_encode_kernel(const uint16_t* __
         const int64_t i = base + u * kThreads;
         v[u] = i < chunks ? *reinterpret_cast<const uint4*>(A + i * 8) : make_uint4(0, 0, 0, 0);
     }
-    if (threadIdx.x < kWave) {
+    if constexpr (STATIC) {
+        if (threadIdx.x == 0) s_sc = *s_a;
+    } else if (threadIdx.x < kWave) {
         // all partial maxima requested at once (one round trip, not one per load)
         static_assert(kActBlocks % kWave == 0, "partials split evenly over one wave");
         float p[kActBlocks / kWave];
@@ -324,7 +328,16 @@ hipError_t launch_quantize_act(const uint16_t* A, uint8_t* qa, float* s_a, void*
     if (e != hipSuccess) return e;
     const int64_t per_block = static_cast<int64_t>(kThreads) * kActUnroll;
     const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, (chunks + per_block - 1) / per_block));
-    act_encode_kernel<<<grid, kThreads, 0, s>>>(A, partial, qa, s_a, chunks);
+    act_encode_kernel<false><<<grid, kThreads, 0, s>>>(A, partial, qa, s_a, chunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_act_static(const uint16_t* A, const float* s_a, uint8_t* qa, int64_t M, int64_t K,
+                                      hipStream_t s) {
+    const int64_t chunks = M * K / 8;
+    const int64_t per_block = static_cast<int64_t>(kThreads) * kActUnroll;
+    const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, (chunks + per_block - 1) / per_block));
+    act_encode_kernel<true><<<grid, kThreads, 0, s>>>(A, nullptr, qa, const_cast<float*>(s_a), chunks);
     return hipGetLastError();
 }
 

@@ -117,6 +117,34 @@ size_t vla_quantize_act_workspace_bytes(int64_t M, int64_t K);
 int vla_quantize_act(const uint16_t *A, uint8_t *qa, float *s_a, void *ws, size_t ws_bytes,
                      int64_t M, int64_t K, void *stream);
 
+/* The same encoding under a calibrated, frozen scale: qa = encode_ocp(fp32(A / s_a))
+ * with s_a given ("FlashRT: an inference engine for real-time robot control",
+ * section 3.2: the first real input sets the FP8 activation scales; section
+ * 7.1: the calibrated scales are captured into the graph).  One pass, no
+ * absmax, no workspace; vla_quantize_act's s_a output is one way to calibrate.
+ *   A   device bf16 M x K;  s_a device float[1], read by the kernel (any fp32
+ *       value: values of |A / s_a| >= 448 saturate to +-448, NaN gives 0x7F
+ *       or 0xFF, exactly as the encoder rules state);  qa device uint8 M x K.
+ * Shape rules as vla_quantize_act (K a multiple of 32); pointers 16-byte
+ * aligned, else VLA_EALIGN. */
+int vla_quantize_act_static(const uint16_t *A, const float *s_a, uint8_t *qa, int64_t M, int64_t K,
+                            void *stream);
+
+/* ----------------------------------------------------------- measurement */
+
+/* Streaming-read probe: one launch of `blocks` workgroups of 256 threads
+ * reads `bytes` from src (16-byte loads, four in flight per thread) and
+ * keeps nothing.  It is the floor under a weight-streaming GEMM call that
+ * reads the same bytes ("Real-time VLA inference on AMD hardware", section
+ * "FP8 helps the encoder and hurts the decoder": the decoder GEMMs are bound
+ * by streaming their weights).
+ *   src   device, 16-byte aligned, `bytes` readable (a positive multiple of 16,
+ *         else VLA_ESHAPE);
+ *   sink  device uint32[1], 16-byte aligned; written only in the rare case
+ *         that the XOR of a thread's data equals a fixed constant;
+ *   blocks 1..65536, else VLA_EINVAL. */
+int vla_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blocks, void *stream);
+
 /* ------------------------------------------------------------------ GEMM */
 
 /* Workspace for vla_gemm_fp8w / vla_gemm_bf16 / vla_gemm_fp8w_gelu_mul at

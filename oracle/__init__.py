@@ -67,6 +67,7 @@ def _load():
                 "orc_bf16_to_f64": (None, [P, I64, P]),
                 "orc_quantize_rows": (None, [P, I64, I64, INT, P, P]),
                 "orc_quantize_act": (None, [P, I64, I64, P, P]),
+                "orc_quantize_act_static": (None, [P, I64, I64, ctypes.c_float, P]),
                 "orc_reencode_fnuz_to_ocp": (None, [P, P, I64, I64, P, P]),
                 "orc_pack": (None, [P, P, I64, I64, INT, INT]),
                 "orc_unpack": (None, [P, P, I64, I64, INT, INT]),
@@ -148,6 +149,15 @@ def quantize_act(A_bits):
     s = np.empty(1, np.float32)
     _load().orc_quantize_act(_p(A), M, K, _p(qa), _p(s))
     return qa, np.float32(s[0])
+
+
+def quantize_act_static(A_bits, s_a):
+    """OCP codes of bf16 A (uint16 bits, M x K) under a given fp32 scale s_a."""
+    A = _c(A_bits, np.uint16)
+    M, K = A.shape
+    qa = np.empty((M, K), np.uint8)
+    _load().orc_quantize_act_static(_p(A), M, K, ctypes.c_float(float(np.float32(s_a))), _p(qa))
+    return qa
 
 
 def reencode_fnuz_to_ocp(q, s):

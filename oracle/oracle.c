@@ -18,6 +18,9 @@
  *       representation", section "Packing around the instruction" (the
  *       view/permute packing expression and its axis labels), section
  *       "Merging gate and up", section "Fusing the BF16 decoder boundary".
+ *  [FR] "FlashRT: an inference engine for real-time robot control"
+ *       (itsolotime.com), sections 3.2 and 7.1: activation scales are
+ *       calibrated once on real data, then frozen into the captured graph.
  *  [P3] "Deploying DeepSeek-V4-Flash on AMD MI300X" (lehuy.net), section
  *       "The FP8 dialect problem": the dialects share the bit layout, the
  *       exponent bias differs by one, FNUZ = finite, NaN, unsigned zero
@@ -194,6 +197,20 @@ void orc_quantize_act(const uint16_t *A, int64_t M, int64_t K, uint8_t *qa, floa
     *s_a = sc;
     for (int64_t i = 0; i < M * K; ++i) {
         float v = (float)orc_bf16_value(A[i]) / sc;
+        qa[i] = orc_fp8_encode(v, ORC_OCP);
+    }
+}
+
+/* Activation quantization with a calibrated, frozen per-tensor scale:
+ *   qa = enc_ocp(fp32(A / s_a)), s_a given.  [FR] "FlashRT: an inference
+ * engine for real-time robot control", section 3.2 (lazy calibration: the
+ * first real input sets the FP8 activation scales) and section 7.1 (the
+ * calibrated scales are captured into the graph).  The scale is taken as
+ * given: any fp32 value, the division and encoder rules then decide. */
+void orc_quantize_act_static(const uint16_t *A, int64_t M, int64_t K, float s_a, uint8_t *qa)
+{
+    for (int64_t i = 0; i < M * K; ++i) {
+        float v = (float)orc_bf16_value(A[i]) / s_a;
         qa[i] = orc_fp8_encode(v, ORC_OCP);
     }
 }

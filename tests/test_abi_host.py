@@ -104,6 +104,15 @@ def test_codec_errors(lib):
     assert rc_of("vla_pack_fp8", A16, A16 + 64, 64, 128, None) == vla.VLA_EINVAL        # overlap
     assert rc_of("vla_reencode_fnuz_to_ocp", A16, A16, A16 + 16, A16, 64, 128, 1, None) == vla.VLA_EINVAL
     assert rc_of("vla_quantize_act", A16, A16, A16, A16, 0, 50, 1024, None) == vla.VLA_EWORKSPACE
+    assert rc_of("vla_quantize_act_static", A16, None, A16, 50, 1024, None) == vla.VLA_EINVAL
+    assert rc_of("vla_probe_stream_read", A16, 1 << 22, A16, 0, None) == vla.VLA_EINVAL
+    assert rc_of("vla_probe_stream_read", A16, (1 << 22) + 8, A16, 256, None) == vla.VLA_ESHAPE
+    assert rc_of("vla_probe_stream_read", A16 + 8, 1 << 22, A16, 256, None) == vla.VLA_EALIGN
+    assert rc_of("vla_probe_stream_read", None, 1 << 22, A16, 256, None) == vla.VLA_EINVAL
+    assert rc_of("vla_quantize_act_static", A16, A16 + 4, A16, 50, 1024, None) == vla.VLA_EALIGN
+    assert rc_of("vla_quantize_act_static", A16, A16, A16, 50, 1000, None) == vla.VLA_ESHAPE
+    assert rc_of("vla_quantize_act_static", A16, A16, A16, 0, 1024, None) == vla.VLA_EINVAL
+    assert rc_of("vla_quantize_act_static", A16, A16, A16, 1 << 24, 1 << 20, None) == vla.VLA_ESHAPE
 
 
 def test_chain_errors(lib):

@@ -143,6 +143,65 @@ def test_quantize_act_every_bf16_value(top):
     assert not bad.any(), f"{bad.sum()} codes differ, first input {hex(int(A[bad][0]))}"
 
 
+def gpu_act_static(A, s):
+    M, K = A.shape
+    qa, sa = Guarded(M * K), Guarded(16)
+    sa.t[:4].copy_(torch.from_numpy(np.array([s], np.float32).view(np.uint8)))
+    vla.vla_quantize_act_static(dev(A), sa.t, qa.t, M, K)
+    qa.check()
+    return qa.numpy(np.uint8).reshape(M, K)
+
+
+@pytest.mark.parametrize("M,K", [(4, 128), (50, 1024), (768, 2048), (3, 32)])
+@pytest.mark.parametrize("scale_mul", [1.0, 0.25, 3.0])
+def test_quantize_act_static_bit_exact(M, K, scale_mul):
+    A = synthetic.activations(M, K, 4400 + M)
+    _, s_dyn = oracle.quantize_act(A)
+    s = np.float32(s_dyn * np.float32(scale_mul))
+    assert np.array_equal(gpu_act_static(A, s), oracle.quantize_act_static(A, s))
+
+
+@pytest.mark.parametrize("s", [1.0, 2.0 ** -7, 3.0e-3, 0.0, float("inf")])
+def test_quantize_act_static_every_bf16_value(s):
+    """Every bf16 bit pattern (both signs, infinities and NaNs included) under
+    a frozen scale, including the degenerate scales 0 and inf."""
+    A = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16).reshape(256, 256)
+    got = gpu_act_static(A, np.float32(s))
+    ref = oracle.quantize_act_static(A, np.float32(s))
+    # where the quotient is NaN (NaN in, 0/0, inf/inf) IEEE 754 leaves the
+    # sign of the result open, so any NaN code (0x7F, 0xFF) is accepted
+    nan = (ref & 0x7F) == 0x7F
+    assert ((got[nan] & 0x7F) == 0x7F).all()
+    bad = (got != ref) & ~nan
+    assert not bad.any(), f"{bad.sum()} codes differ, first input {hex(int(A[bad][0]))}"
+
+
+def test_quantize_act_static_reuses_calibrated_scale():
+    """Calibrate on one batch with vla_quantize_act, freeze its device scale,
+    encode another batch with it."""
+    M, K = 50, 1024
+    A0 = synthetic.activations(M, K, 4501)
+    A1 = synthetic.activations(M, K, 4502)
+    qa0, sa = Guarded(M * K), Guarded(16)
+    ws = zeros_ws(vla.vla_quantize_act_workspace_bytes(M, K))
+    vla.vla_quantize_act(dev(A0), qa0.t, sa.t, ws, ws.numel(), M, K)
+    qa1 = Guarded(M * K)
+    vla.vla_quantize_act_static(dev(A1), sa.t, qa1.t, M, K)
+    qa1.check()
+    s0 = oracle.quantize_act(A0)[1]
+    assert np.array_equal(qa1.numpy(np.uint8).reshape(M, K), oracle.quantize_act_static(A1, s0))
+
+
+@pytest.mark.parametrize("blocks", [1, 256, 1024])
+def test_probe_stream_read_runs(blocks):
+    """The probe reads every byte and writes nothing for all-zero data."""
+    src = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    sink = Guarded(16, fill=0xA5)
+    vla.vla_probe_stream_read(src, src.numel(), sink.t, blocks)
+    sink.check()
+    assert (sink.numpy(np.uint8) == 0xA5).all()
+
+
 def test_quantize_act_all_zero():
     M, K = 8, 64
     A = np.zeros((M, K), np.uint16)

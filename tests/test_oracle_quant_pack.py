@@ -75,6 +75,35 @@ def test_quantize_act_against_torch():
     assert ((qa & 0x7F) == 0x7E).any()
 
 
+@pytest.mark.parametrize("scale_mul", [1.0, 0.25, 3.0])
+def test_quantize_act_static_against_torch(scale_mul):
+    """A frozen scale: torch's float8_e4m3fn cast (round to nearest even) of
+    the IEEE quotient, clamped to +-448 first because the cast does not
+    saturate.  A scale of a quarter of the absmax scale saturates the tails."""
+    A = synthetic.activations(50, 1024, 504)
+    _, s_dyn = oracle.quantize_act(A)
+    s = np.float32(s_dyn * np.float32(scale_mul))
+    qa = oracle.quantize_act_static(A, s)
+    Af = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(torch.float32)
+    ref = torch.clamp(Af / torch.tensor(s, dtype=torch.float32), -448.0, 448.0)
+    assert np.array_equal(qa, ref.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    if scale_mul == 1.0:
+        assert np.array_equal(qa, oracle.quantize_act(A)[0])
+    if scale_mul < 1.0:
+        assert ((qa & 0x7F) == 0x7E).sum() > 100
+
+
+def test_quantize_act_static_special_values():
+    """Infinities saturate, NaN keeps its sign as 0x7F / 0xFF, -0 stays 0x80,
+    and a zero scale turns every finite non-zero value into a saturated code."""
+    A = np.array([[0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x8000, 0x0000, 0x3F80, 0xBF80] * 4], np.uint16)
+    q1 = oracle.quantize_act_static(A, np.float32(1.0))[0, :8]
+    assert list(q1) == [0x7E, 0xFE, 0x7F, 0xFF, 0x80, 0x00, 0x38, 0xB8]
+    q0 = oracle.quantize_act_static(A, np.float32(0.0))[0, :8]
+    assert list(q0[[0, 1, 6, 7]]) == [0x7E, 0xFE, 0x7E, 0xFE]
+    assert (q0[[2, 3, 4, 5]] & 0x7F).tolist() == [0x7F] * 4     # NaN in, and 0/0
+
+
 # ------------------------------------------------------------- re-encoder
 
 def _value(q, s, dialect):
