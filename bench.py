@@ -289,6 +289,18 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
         ms = time_graph(actq_static, 20)
         out[f"{name}_act_quant_static_us"] = round(ms * 1000.0 / 20, 2)
 
+    log("secondary: fused decoder boundary")
+    bx, by, bg, bs = (up_bits(t) for t in synthetic.boundary_inputs(M, H, M))
+    b_out = [torch.empty(M * H, dtype=torch.int16, device=dev) for _ in range(3)]
+
+    def boundary(i):
+        vla.vla_gate_residual_ada_norm(bx, by, bg, bs, True, 1e-6, b_out[0], b_out[1], b_out[2], M, H)
+    ms = time_graph(boundary, 256)
+    b_us = ms * 1000.0 / 256
+    b_bytes = (3 + 3) * M * H * 2 + 3 * M * H * 2          # reads x, out, gate, style; writes r, h, next gate
+    out["boundary_us"] = round(b_us, 3)
+    out["boundary_GBps"] = round(b_bytes / (b_us * 1e-6) / 1e9, 1)
+
     log("secondary: 18-layer chain")
     L = 18
     gate, up, down = synthetic.chain_weights(L, H, I)

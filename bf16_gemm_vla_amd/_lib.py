@@ -47,6 +47,7 @@ SIGNATURES = {
     "vla_quantize_act": (INT, [P, P, P, P, SZ, I64, I64, P]),
     "vla_quantize_act_static": (INT, [P, P, P, I64, I64, P]),
     "vla_probe_stream_read": (INT, [P, SZ, P, INT, P]),
+    "vla_gate_residual_ada_norm": (INT, [P, P, P, P, INT, ctypes.c_float, P, P, P, I64, I64, P]),
     "vla_gemm_workspace_bytes": (SZ, [I64, I64, I64, INT]),
     "vla_gemm_supported": (INT, [I64, I64, I64, INT, INT, INT]),
     "vla_gemm_fp8w": (INT, [P, P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
@@ -157,6 +158,14 @@ def vla_reencode_fnuz_to_ocp(q_fnuz, s_fnuz, q_ocp, s_ocp, N, K, layout, stream=
 def vla_quantize_act(A, qa, s_a, ws, ws_bytes, M, K, stream=None):
     _check(load().vla_quantize_act(_ptr(A), _ptr(qa), _ptr(s_a), _ptr(ws), ws_bytes, M, K,
                                    _stream(stream)), "vla_quantize_act")
+
+
+def vla_gate_residual_ada_norm(residual, out, gate, style, style_per_row, eps, residual_out, normalized,
+                               next_gate, M, D, stream=None):
+    _check(load().vla_gate_residual_ada_norm(_ptr(residual), _ptr(out), _ptr(gate), _ptr(style),
+                                             int(bool(style_per_row)), float(eps), _ptr(residual_out),
+                                             _ptr(normalized), _ptr(next_gate), M, D, _stream(stream)),
+           "vla_gate_residual_ada_norm")
 
 
 def vla_probe_stream_read(src, nbytes, sink, blocks, stream=None):

@@ -21,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["codec.hip", "gemm.hip", "gemm_wide.hip", "probe.hip", "abi.cpp"]
+SOURCES = ["codec.hip", "gemm.hip", "gemm_wide.hip", "boundary.hip", "probe.hip", "abi.cpp"]
 HIPFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

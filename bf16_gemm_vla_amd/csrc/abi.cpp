@@ -3,6 +3,7 @@
 // codec.hip and gemm.hip; nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -258,6 +259,44 @@ int vla_quantize_act_static(const uint16_t* A, const float* s_a, uint8_t* qa, in
     REQUIRE_PTR(s_a);
     REQUIRE_PTR(qa);
     hipError_t e = vla::launch_quantize_act_static(A, s_a, qa, M, K, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
+}
+
+int vla_gate_residual_ada_norm(const uint16_t* residual, const uint16_t* out, const uint16_t* gate,
+                               const uint16_t* style, int style_per_row, float eps, uint16_t* residual_out,
+                               uint16_t* normalized, uint16_t* next_gate, int64_t M, int64_t D, void* stream) {
+    const char* fn = "vla_gate_residual_ada_norm";
+    REQUIRE_PTR(residual);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(gate);
+    REQUIRE_PTR(style);
+    REQUIRE_PTR(residual_out);
+    REQUIRE_PTR(normalized);
+    OPTIONAL_PTR(next_gate);
+    if (M <= 0 || D <= 0) return fail(VLA_EINVAL, fn, "M=%lld D=%lld must be positive", (long long)M, (long long)D);
+    if (M > (int64_t(1) << 24)) return fail(VLA_ESHAPE, fn, "M=%lld too large", (long long)M);
+    if (!vla::boundary_width_ok(D)) return fail(VLA_ESHAPE, fn, "D=%lld must be a multiple of 4, at most 8192", (long long)D);
+    if (!std::isfinite(eps) || eps < 0.0f) return fail(VLA_EINVAL, fn, "eps must be finite and >= 0");
+    // residual_out may be residual itself; no other output may overlap anything
+    const size_t mat = static_cast<size_t>(M) * D * 2;
+    const size_t sty = static_cast<size_t>(style_per_row ? M : 1) * 3 * D * 2;
+    struct Range { const void* p; size_t n; };
+    const Range ins[4] = {{residual, mat}, {out, mat}, {gate, mat}, {style, sty}};
+    const Range outs[3] = {{residual_out, mat}, {normalized, mat}, {next_gate, next_gate ? mat : 0}};
+    auto overlap = [](const Range& x, const Range& y) {
+        const uint8_t *a = static_cast<const uint8_t*>(x.p), *b = static_cast<const uint8_t*>(y.p);
+        return x.n && y.n && a < b + y.n && b < a + x.n;
+    };
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlap(outs[i], ins[j]) && !(i == 0 && j == 0 && outs[i].p == ins[j].p))
+                return fail(VLA_EINVAL, fn, "output %d overlaps input %d", i, j);
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return fail(VLA_EINVAL, fn, "outputs %d and %d overlap", i, j);
+    }
+    hipError_t e = vla::launch_gate_residual_ada_norm(residual, out, gate, style, style_per_row ? 1 : 0, eps,
+                                                      residual_out, normalized, next_gate, M, D,
+                                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
 }
 

@@ -20,6 +20,10 @@ hipError_t launch_reencode(const uint8_t* q, const float* sc, uint8_t* q2, float
 size_t quantize_act_ws_bytes(int64_t M, int64_t K);
 hipError_t launch_quantize_act(const uint16_t* A, uint8_t* qa, float* s_a, void* ws, int64_t M,
                                int64_t K, hipStream_t s);
+hipError_t launch_gate_residual_ada_norm(const uint16_t* resid, const uint16_t* out, const uint16_t* gate,
+                                         const uint16_t* style, int style_per_row, float eps, uint16_t* r_out,
+                                         uint16_t* h_out, uint16_t* ng_out, int64_t M, int64_t D, hipStream_t s);
+bool boundary_width_ok(int64_t D);   // D a positive multiple of 4, at most 8192
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
 hipError_t launch_quantize_act_static(const uint16_t* A, const float* s_a, uint8_t* qa, int64_t M, int64_t K,
                                       hipStream_t s);

@@ -130,6 +130,33 @@ int vla_quantize_act(const uint16_t *A, uint8_t *qa, float *s_a, void *ws, size_
 int vla_quantize_act_static(const uint16_t *A, const float *s_a, uint8_t *qa, int64_t M, int64_t K,
                             void *stream);
 
+/* ------------------------------------------------------- decoder boundary */
+
+/* Fused decoder boundary ("Real-time VLA inference on AMD hardware",
+ * section "Fusing the BF16 decoder boundary"): the gated residual update
+ * followed by the adaptive RMS norm of its result, per row m and channel d:
+ *   residual_out = bf16(residual + out * gate)              (one rounding)
+ *   normalized   = bf16(r / sqrt(mean_d(r^2) + eps) * (1 + scale) + shift)
+ *   next_gate    = the style row's gate block (a copy)
+ * with r = residual_out and style rows holding three consecutive D-wide bf16
+ * blocks [scale | shift | next gate].  The page names the operation and its
+ * two steps; the modulation reading (scale, shift, gate per channel, no
+ * separate norm weight) is this library's.  residual_out is the correctly
+ * rounded sum bit for bit; normalized is computed in fp64 and rounded once.
+ *   residual, out, gate   device bf16 M x D (row-major);
+ *   style                 device bf16, M x 3D when style_per_row != 0, else
+ *                         one 3D row shared by every row;
+ *   eps                   finite, >= 0 (else VLA_EINVAL);
+ *   residual_out          device bf16 M x D; may be `residual` itself;
+ *   normalized            device bf16 M x D;
+ *   next_gate             device bf16 M x D, or NULL to skip the copy.
+ * No output may overlap an input or another output (residual_out ==
+ * residual excepted): VLA_EINVAL.  D a multiple of 4, at most 8192
+ * (VLA_ESHAPE); M in 1 .. 2^24; pointers 16-byte aligned (VLA_EALIGN). */
+int vla_gate_residual_ada_norm(const uint16_t *residual, const uint16_t *out, const uint16_t *gate,
+                               const uint16_t *style, int style_per_row, float eps, uint16_t *residual_out,
+                               uint16_t *normalized, uint16_t *next_gate, int64_t M, int64_t D, void *stream);
+
 /* ----------------------------------------------------------- measurement */
 
 /* Streaming-read probe: one launch of `blocks` workgroups of 256 threads

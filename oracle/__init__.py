@@ -76,6 +76,7 @@ def _load():
                 "orc_gelu_tanh": (ctypes.c_double, [ctypes.c_double]),
                 "orc_gelu_mul": (None, [P, P, I64, P]),
                 "orc_mlp_chain": (None, [P, P, P, P, P, INT, I64, I64, I64, P, P, P, P]),
+                "orc_gate_residual_ada_norm": (None, [P, P, P, P, INT, ctypes.c_float, I64, I64, P, P, P]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(lib, name)
@@ -254,3 +255,24 @@ def mlp_chain(x_in_bits, wgu, sgu, wd, sd, stages: bool = False):
     _load().orc_mlp_chain(_p(x), pgu, psg, pd, psd, L, M, H, I, _p(out), _p(gu), _p(act),
                           _p(xl))
     return (out, gu, act, xl) if stages else out
+
+
+# ------------------------------------------------------- decoder boundary
+
+def gate_residual_ada_norm(residual, out, gate, style, eps: float, style_per_row: bool = True):
+    """Fused decoder boundary on bf16 bit patterns (uint16): residual, out,
+    gate are M x D; style is M x 3D (per row) or 1 x 3D (shared), blocks
+    [scale | shift | next gate].  Returns (r, h, next_gate), each M x D."""
+    residual = _c(residual, np.uint16)
+    out = _c(out, np.uint16)
+    gate = _c(gate, np.uint16)
+    style = _c(style, np.uint16)
+    M, D = residual.shape
+    assert out.shape == (M, D) and gate.shape == (M, D)
+    assert style.shape == ((M if style_per_row else 1), 3 * D)
+    r = np.empty((M, D), np.uint16)
+    h = np.empty((M, D), np.uint16)
+    ng = np.empty((M, D), np.uint16)
+    _load().orc_gate_residual_ada_norm(_p(residual), _p(out), _p(gate), _p(style), int(bool(style_per_row)),
+                                       ctypes.c_float(float(np.float32(eps))), M, D, _p(r), _p(h), _p(ng))
+    return r, h, ng

@@ -384,3 +384,41 @@ void orc_mlp_chain(const uint16_t *x_in, const uint8_t *const *wgu, const float 
     memcpy(x_out, xb, sizeof(uint16_t) * M * H);
     free(x); free(wg); free(wdn); free(gu); free(act); free(dn); free(gb); free(ab); free(xb);
 }
+
+/* Fused decoder boundary, [P1] "Fusing the BF16 decoder boundary": the
+ * gated residual update followed by the adaptive RMS norm of its result,
+ *   r  = bf16(residual + out * gate)                       (one rounding)
+ *   h  = bf16(r / sqrt(mean_d(r^2) + eps) * (1 + scale) + shift)
+ *   ng = next gate (a bf16 copy),
+ * for bf16 M x D inputs residual, out, gate.  The pages name the operation
+ * and its two steps only; this reading takes the adaptive norm's style as
+ * the per-channel modulation (scale, shift, next gate), stored as three
+ * consecutive D-wide bf16 blocks per style row: one row per activation row
+ * (style_per_row != 0) or one row shared by all rows.  Everything is fp64;
+ * the mean is a plain ascending sum over d divided by D.  eps is the fp32
+ * value given, widened. */
+void orc_gate_residual_ada_norm(const uint16_t *residual, const uint16_t *out, const uint16_t *gate,
+                                const uint16_t *style, int style_per_row, float eps, int64_t M, int64_t D,
+                                uint16_t *r_out, uint16_t *h_out, uint16_t *ng_out)
+{
+    double *r = malloc(sizeof(double) * D);
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *st = style + (style_per_row ? m * 3 * D : 0);
+        double ss = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            int64_t i = m * D + d;
+            double v = orc_bf16_value(residual[i]) + orc_bf16_value(out[i]) * orc_bf16_value(gate[i]);
+            uint16_t rb = orc_bf16_round(v);
+            r_out[i] = rb;
+            r[d] = orc_bf16_value(rb);
+            ss += r[d] * r[d];
+        }
+        double inv = 1.0 / sqrt(ss / (double)D + (double)eps);
+        for (int64_t d = 0; d < D; ++d) {
+            double scale = orc_bf16_value(st[d]), shift = orc_bf16_value(st[D + d]);
+            h_out[m * D + d] = orc_bf16_round(r[d] * inv * (1.0 + scale) + shift);
+            ng_out[m * D + d] = st[2 * D + d];
+        }
+    }
+    free(r);
+}

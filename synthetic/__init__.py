@@ -12,6 +12,9 @@ Recipe (stated once, used everywhere):
     bit patterns).
   * weights: N(0, 0.02) drawn in fp32 (sigma = 0.02), one row per output
     channel (N x K).
+  * decoder boundary: residual and block output N(0, 1), gate and the
+    style rows (scale | shift | next gate) N(0, 0.1), all rounded to bf16
+    (the pages give no distributions; modulation outputs are taken small).
 The pages measure on camera observations of a public robotics benchmark and
 on trained checkpoints; neither is available here, and these Gaussian
 tensors of the same shapes stand in for them (no outliers).
@@ -60,6 +63,7 @@ IDS = {
     "wide.down.A": 22, "wide.down.W": 23,
     "dialect.W": 30,
     "chain.x": 40,
+    "boundary.residual": 50, "boundary.out": 51, "boundary.gate": 52, "boundary.style": 53,
     "chain.gate": 100,   # + layer
     "chain.up": 200,     # + layer
     "chain.down": 300,   # + layer
@@ -72,3 +76,17 @@ def chain_weights(L: int, H: int, I: int, seed: int = 0):
     up = [weights(I, H, IDS["chain.up"] + l, seed) for l in range(L)]
     down = [weights(H, I, IDS["chain.down"] + l, seed) for l in range(L)]
     return gate, up, down
+
+
+MODULATION_SIGMA = 0.1
+
+
+def boundary_inputs(M: int, D: int, style_rows: int, seed: int = 0):
+    """bf16 bit patterns for the fused decoder boundary: residual, out (M x D),
+    gate (M x D) and style (style_rows x 3D)."""
+    def draw(shape, tid, sigma):
+        x = rng(IDS[tid], seed).standard_normal(shape, dtype=np.float32) * np.float32(sigma)
+        return fp32_to_bf16_bits(x)
+    return (draw((M, D), "boundary.residual", 1.0), draw((M, D), "boundary.out", 1.0),
+            draw((M, D), "boundary.gate", MODULATION_SIGMA),
+            draw((style_rows, 3 * D), "boundary.style", MODULATION_SIGMA))

@@ -115,6 +115,29 @@ def test_codec_errors(lib):
     assert rc_of("vla_quantize_act_static", A16, A16, A16, 1 << 24, 1 << 20, None) == vla.VLA_ESHAPE
 
 
+def test_boundary_errors(lib):
+    mat = 50 * 1024 * 2
+    X, Y, G, S = A16, A16 + mat, A16 + 2 * mat, A16 + 3 * mat       # disjoint inputs
+    R, H, NG = A16 + 8 * mat, A16 + 9 * mat, A16 + 10 * mat          # disjoint outputs
+
+    def rc(*args):
+        return rc_of("vla_gate_residual_ada_norm", *args)
+    assert rc(X, Y, G, S, 1, 1e-6, R, H, NG, 0, 1024, None) == vla.VLA_EINVAL
+    assert rc(X, Y, G, S, 1, 1e-6, R, H, NG, 50, 1022, None) == vla.VLA_ESHAPE
+    assert rc(X, Y, G, S, 1, 1e-6, R, H, NG, 50, 8196, None) == vla.VLA_ESHAPE
+    assert rc(X, Y, G, S, 1, -1.0, R, H, NG, 50, 1024, None) == vla.VLA_EINVAL
+    assert rc(X, Y, G, S, 1, float("nan"), R, H, NG, 50, 1024, None) == vla.VLA_EINVAL
+    assert rc(None, Y, G, S, 1, 1e-6, R, H, NG, 50, 1024, None) == vla.VLA_EINVAL
+    assert rc(X + 8, Y, G, S, 1, 1e-6, R, H, NG, 50, 1024, None) == vla.VLA_EALIGN
+    assert rc(X, Y, G, S, 1, 1e-6, R, H, NG + 8, 50, 1024, None) == vla.VLA_EALIGN
+    assert rc(X, Y, G, S, 1, 1e-6, R, Y, NG, 50, 1024, None) == vla.VLA_EINVAL        # normalized over out
+    assert rc(X, Y, G, S, 1, 1e-6, R, H, S + 16, 50, 1024, None) == vla.VLA_EINVAL    # next_gate in style
+    assert rc(X, Y, G, S, 1, 1e-6, X + 16, H, NG, 50, 1024, None) == vla.VLA_EINVAL   # partial alias
+    assert rc(X, Y, G, S, 1, 1e-6, R, R + 16, NG, 50, 1024, None) == vla.VLA_EINVAL   # outputs overlap
+    # a shared style row is 3D wide: an output right after it is fine, inside it is not
+    assert rc(X, Y, G, S, 0, 1e-6, R, H, S + 16, 50, 1024, None) == vla.VLA_EINVAL
+
+
 def test_chain_errors(lib):
     arr = (ctypes.c_void_p * 2)(A16, A16)
     need = vla.vla_mlp_chain_scratch_bytes(50, 1024, 4096)
