@@ -66,18 +66,19 @@ __global__ __launch_bounds__(kBThreads) void gate_residual_ada_norm_kernel(BArgs
     const int64_t row = static_cast<int64_t>(blockIdx.x) * a.D;
     const uint16_t* st = a.style + (a.style_per_row ? static_cast<int64_t>(blockIdx.x) * 3 * a.D : 0);
 
+    // chunks past the row load chunk 0 (always present) and are never used,
+    // so every load is unconditional
     uint2 xv[CH], yv[CH], gv[CH], sc[CH], sh[CH], ng[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int64_t q = tid + static_cast<int64_t>(c) * kBThreads;
-        const bool ok = q < nq;
-        const uint2 z = make_uint2(0, 0);
-        xv[c] = ok ? *reinterpret_cast<const uint2*>(a.resid + row + 4 * q) : z;
-        yv[c] = ok ? *reinterpret_cast<const uint2*>(a.out + row + 4 * q) : z;
-        gv[c] = ok ? *reinterpret_cast<const uint2*>(a.gate + row + 4 * q) : z;
-        sc[c] = ok ? *reinterpret_cast<const uint2*>(st + 4 * q) : z;
-        sh[c] = ok ? *reinterpret_cast<const uint2*>(st + a.D + 4 * q) : z;
-        ng[c] = ok ? *reinterpret_cast<const uint2*>(st + 2 * a.D + 4 * q) : z;
+        const int64_t q0 = tid + static_cast<int64_t>(c) * kBThreads;
+        const int64_t q = q0 < nq ? q0 : 0;
+        xv[c] = *reinterpret_cast<const uint2*>(a.resid + row + 4 * q);
+        yv[c] = *reinterpret_cast<const uint2*>(a.out + row + 4 * q);
+        gv[c] = *reinterpret_cast<const uint2*>(a.gate + row + 4 * q);
+        sc[c] = *reinterpret_cast<const uint2*>(st + 4 * q);
+        sh[c] = *reinterpret_cast<const uint2*>(st + a.D + 4 * q);
+        ng[c] = *reinterpret_cast<const uint2*>(st + 2 * a.D + 4 * q);
     }
 
     // gated residual, one rounding per value; sum of squares of the rounded r
