@@ -192,6 +192,18 @@ def main():
         extra[f"{name}_GBps"] = round(alg_bytes_fp8w(*shp) / (ms * 1e-3 / args.steps) / 1e9, 1)
 
     if not args.no_extra:
+        # the pages' own decoder row count (10 rows), same weights and rotation
+        A10_up = up_bits(synthetic.activations(10, H, synthetic.IDS["skinny.up.A"]))
+        A10_dn = up_bits(synthetic.activations(10, I, synthetic.IDS["skinny.down.A"]))
+        ws10_bytes = max(vla.vla_gemm_workspace_bytes(10, I, H, 1), vla.vla_gemm_workspace_bytes(10, H, I, 1))
+        ws10 = torch.zeros(ws10_bytes, dtype=torch.uint8, device=dev)
+        for name, shp, qs, A, s in (("up", (10, I, H), qs_up, A10_up, s_up), ("down", (10, H, I), qs_dn, A10_dn, s_dn)):
+            def one10(i, shp=shp, qs=qs, A=A, s=s):
+                vla.vla_gemm_fp8w(A, None, qs[i % copies], s, None, None, Y_up, ws10, ws10_bytes, *shp)
+            ms = time_graph(one10, args.steps)
+            extra[f"m10_{name}_us"] = round(ms * 1000.0 / args.steps, 3)
+
+    if not args.no_extra:
         extra.update(secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, args))
 
     result = {
@@ -250,44 +262,44 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
         del qs
 
     log("secondary: wide GEMMs")
-    Mw = 768
-    for name, (n, k) in (("wide_up", (16384, 2048)), ("wide_down", (2048, 16384))):
-        A = up_bits(synthetic.activations(Mw, k, 910 + n))
-        q, s = quantize(synthetic.weights(n, k, 911 + n))
-        Y = torch.empty(Mw * n, dtype=torch.int16, device=dev)
-        wsb = vla.vla_gemm_workspace_bytes(Mw, n, k, 1)
-        ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
-        qa = torch.empty(Mw * k, dtype=torch.uint8, device=dev)
-        sa = torch.empty(1, dtype=torch.float32, device=dev)
-        wq_b = vla.vla_quantize_act_workspace_bytes(Mw, k)
-        wq = torch.zeros(wq_b, dtype=torch.uint8, device=dev)
-        flops = 2.0 * Mw * n * k
+    for Mw, prefix in ((768, "wide"), (571, "wide_m571")):
+        for name, (n, k) in ((prefix + "_up", (16384, 2048)), (prefix + "_down", (2048, 16384))):
+            A = up_bits(synthetic.activations(Mw, k, 910 + n))
+            q, s = quantize(synthetic.weights(n, k, 911 + n))
+            Y = torch.empty(Mw * n, dtype=torch.int16, device=dev)
+            wsb = vla.vla_gemm_workspace_bytes(Mw, n, k, 1)
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+            qa = torch.empty(Mw * k, dtype=torch.uint8, device=dev)
+            sa = torch.empty(1, dtype=torch.float32, device=dev)
+            wq_b = vla.vla_quantize_act_workspace_bytes(Mw, k)
+            wq = torch.zeros(wq_b, dtype=torch.uint8, device=dev)
+            flops = 2.0 * Mw * n * k
 
-        def w8a16(i):
-            vla.vla_gemm_fp8w(A, None, q, s, None, None, Y, ws, wsb, Mw, n, k)
+            def w8a16(i):
+                vla.vla_gemm_fp8w(A, None, q, s, None, None, Y, ws, wsb, Mw, n, k)
 
-        def actq(i):
-            vla.vla_quantize_act(A, qa, sa, wq, wq_b, Mw, k)
+            def actq(i):
+                vla.vla_quantize_act(A, qa, sa, wq, wq_b, Mw, k)
 
-        def fp8fp8(i):
-            vla.vla_gemm_fp8w(qa, sa, q, s, None, None, Y, ws, wsb, Mw, n, k)
+            def fp8fp8(i):
+                vla.vla_gemm_fp8w(qa, sa, q, s, None, None, Y, ws, wsb, Mw, n, k)
 
-        for tag, fn, peak in (("w8a16", w8a16, BF16_PEAK_TFLOPS), ("fp8xfp8", fp8fp8, FP8_PEAK_TFLOPS)):
-            if tag == "fp8xfp8":
-                actq(0)
-            ms = time_graph(fn, 20)
-            us = ms * 1000.0 / 20
-            tf = flops / (us * 1e-6) / 1e12
-            out[f"{name}_{tag}_us"] = round(us, 2)
-            out[f"{name}_{tag}_TFLOPs"] = round(tf, 1)
-            out[f"{name}_{tag}_frac"] = round(tf / peak, 4)
-        ms = time_graph(actq, 20)
-        out[f"{name}_act_quant_us"] = round(ms * 1000.0 / 20, 2)
+            for tag, fn, peak in (("w8a16", w8a16, BF16_PEAK_TFLOPS), ("fp8xfp8", fp8fp8, FP8_PEAK_TFLOPS)):
+                if tag == "fp8xfp8":
+                    actq(0)
+                ms = time_graph(fn, 20)
+                us = ms * 1000.0 / 20
+                tf = flops / (us * 1e-6) / 1e12
+                out[f"{name}_{tag}_us"] = round(us, 2)
+                out[f"{name}_{tag}_TFLOPs"] = round(tf, 1)
+                out[f"{name}_{tag}_frac"] = round(tf / peak, 4)
+            ms = time_graph(actq, 20)
+            out[f"{name}_act_quant_us"] = round(ms * 1000.0 / 20, 2)
 
-        def actq_static(i):   # frozen scale (the one just calibrated): one pass, no absmax
-            vla.vla_quantize_act_static(A, sa, qa, Mw, k)
-        ms = time_graph(actq_static, 20)
-        out[f"{name}_act_quant_static_us"] = round(ms * 1000.0 / 20, 2)
+            def actq_static(i):   # frozen scale (the one just calibrated): one pass, no absmax
+                vla.vla_quantize_act_static(A, sa, qa, Mw, k)
+            ms = time_graph(actq_static, 20)
+            out[f"{name}_act_quant_static_us"] = round(ms * 1000.0 / 20, 2)
 
     log("secondary: fused decoder boundary")
     bx, by, bg, bs = (up_bits(t) for t in synthetic.boundary_inputs(M, H, M))

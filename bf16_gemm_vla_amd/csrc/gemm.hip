@@ -358,6 +358,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
         const int64_t groups = std::max<int64_t>(1, (epi == Epi::GELU_MUL) ? tiles / 2 : tiles);
         const int64_t mt_total = (M + 15) / 16;
         const int64_t want = groups >= 256 ? 1 : (256 + groups - 1) / groups;   // splits wanted
+        // one 16-row tile and too few column groups, FP8 weights: no K split
+        // up to 128 MFMA steps (K = 4096) — one 16-wave workgroup per tile
+        // beats the cross-workgroup exchange (the 10-row 4096 -> 1024
+        // down-projection: 6.30 -> 5.31 us against four K splits)
+        if (want > 1 && mt_total == 1 && wt == WType::FP8 && epi == Epi::PLAIN && ksteps > 16 && ksteps <= 128)
+            return skinny_plan(M, N, K, epi, nt, ksteps <= 64 ? 4 : 8, 16, 1, at == AType::BF16);
         if (want > 1 && mt_total > 1) {
             const int64_t ksplit = (want + mt_total - 1) / mt_total;
             const int64_t chunk = (ksteps + ksplit - 1) / ksplit;               // K steps per workgroup
@@ -414,8 +420,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
     p.wnw = p.waves / 2;
     const int64_t kt_total = (K + p.steps - 1) / p.steps;
     const int64_t base = static_cast<int64_t>(p.groups) * p.mblocks;
+    // the largest K split that keeps the grid within one workgroup per CU
+    // (256) and at least 8 stages per split: a grid past 256 runs a second,
+    // partial wave of workgroups (571 rows, 2048 -> 16384: 66 -> 46 us for
+    // one split against two)
     int ks = 1;
-    while (base * ks < 256 && kt_total / (ks * 2) >= 8) ks *= 2;
+    while (base * (ks + 1) <= 256 && kt_total / (ks + 1) >= 8) ++ks;
     p.ksplit = ks;
     const int64_t a_bytes = M * K * (at == AType::FP8 ? 1 : 2);
     const int64_t w_bytes = N * K * (wt == WType::FP8 ? 1 : 2);

@@ -218,3 +218,40 @@ def test_wide_config_sampled(N, K, fp8_act):
     ref, yabs = oracle.gemm(a_val[rows], w.w)
     assert_gemm_close(y[rows], ref, yabs)
     assert np.isfinite(bf16_f64(y)).all()
+
+
+# ------------------------------------------------- the pages' own row counts
+
+@pytest.mark.parametrize("wfmt", [vla.VLA_WFMT_E4M3_OCP, vla.VLA_WFMT_BF16])
+@pytest.mark.parametrize("N,K,bias", [(4096, 1024, False), (1024, 4096, False), (8192, 1024, True)])
+def test_page_decoder_rows(wfmt, N, K, bias):
+    """The 10-row action decoder the pages time: up, down, and the merged
+    gate/up GEMM (10, 8192, 1024) with its bias epilogue."""
+    check(10, N, K, wfmt, 7000 + N // 16 + K // 32, bias=bias)
+
+
+@pytest.mark.parametrize("N,K", [(16384, 2048), (2048, 16384)])
+@pytest.mark.parametrize("fp8_act", [False, True])
+def test_page_encoder_rows(N, K, fp8_act):
+    """The 571-row encoder GEMMs the pages time (two full 192-row blocks and a
+    ragged 187-row one); sampled rows include the last ones."""
+    M = 571
+    print(f"encoder rows M={M} N={N} K={K} fp8_act={fp8_act}", flush=True)
+    A = synthetic.activations(M, K, 7100 + N // 1024)
+    w = Weights(synthetic.weights(N, K, 7101 + N // 1024), vla.VLA_WFMT_E4M3_OCP)
+    Ad = dev(A)
+    if fp8_act:
+        qa = torch.empty(M * K, dtype=torch.uint8, device="cuda")
+        sa = torch.empty(1, dtype=torch.float32, device="cuda")
+        wq = torch.zeros(vla.vla_quantize_act_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+        vla.vla_quantize_act(Ad, qa, sa, wq, wq.numel(), M, K)
+        y, _ = run_gemm(qa, w, M, s_a=sa)
+        ref_qa, ref_sa = oracle.quantize_act(A)
+        a_val = oracle.decode(ref_qa, OCP) * np.float64(ref_sa)
+    else:
+        y, _ = run_gemm(Ad, w, M)
+        a_val = bf16_f64(A)
+    rows = np.unique(np.concatenate([_sampled_rows(M, 16, 7200 + N), [383, 384, 569, 570]]))
+    ref, yabs = oracle.gemm(a_val[rows], w.w)
+    assert_gemm_close(y[rows], ref, yabs)
+    assert np.isfinite(bf16_f64(y)).all()
