@@ -429,8 +429,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
     p.ksplit = ks;
     const int64_t a_bytes = M * K * (at == AType::FP8 ? 1 : 2);
     const int64_t w_bytes = N * K * (wt == WType::FP8 ? 1 : 2);
-    // split-K arrival counters: one per 32-row slice (3) of every output tile
-    p.ok = base * 3 <= kMaxCounters && a_bytes < (int64_t(1) << 31) && w_bytes < (int64_t(1) << 31);
+    // split-K counters: kWideCounters per output tile
+    p.ok = base * kWideCounters <= kMaxCounters && a_bytes < (int64_t(1) << 31) && w_bytes < (int64_t(1) << 31);
     return p;
 }
 

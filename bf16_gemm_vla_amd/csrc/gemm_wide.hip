@@ -41,6 +41,7 @@ using namespace gemm_detail;
 constexpr int kWideBM = 192;
 constexpr int kWideStages = 4;
 constexpr uint32_t kOOB = 0x80000000u;   // voffset beyond every resource's range
+constexpr int kWideSpinMax = 1 << 20;     // polls before an owner gives up waiting (never reached)
 
 template <AType AT, WType WT, int BN, int WNW, int BK_>
 struct WideCfg {
@@ -151,6 +152,10 @@ void wide_gemm_kernel(KArgs a) {
     const int kt_begin = split * kt_per;
     const int kt_end = min(kt_total, kt_begin + kt_per);
     const int nkt = max(0, kt_end - kt_begin);
+    // split-K counters of this output tile: [0] workgroups started,
+    // [1] arrivals (+ slices handed to the last arrival), [2] workgroups done
+    uint32_t* const ctr = a.tickets + (static_cast<int64_t>(mb) * a.groups + g) * kWideCounters;
+    if (a.ksplit > 1 && tid == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // buffer resources bounded to A and W: loads past the end read zero
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
@@ -407,11 +412,15 @@ void wide_gemm_kernel(KArgs a) {
     // ---- epilogue.  acc[ns][ms] register r: row (output channel) 8*(r/4) + 4*(lane/32) + r%4
     //      of the 32-column sub-tile, activation row lane%32 of the 32-row sub-tile.
     //      The tile is finished in MSUB slices (slice ms = accumulators acc[*][ms]).
-    //      With K split over workgroups every slice has its own arrival counter:
-    //      each workgroup stores all its partials, then counts its arrival on
-    //      every slice at once, and finishes the slices it was last for, so the
-    //      reduction of a tile is spread over its workgroups.  Partials are
-    //      summed in split order, whoever finishes (bitwise repeatable).
+    //      With K split over workgroups, every workgroup stores its partials;
+    //      the workgroup of split s < MSUB owns slice s and finishes it itself,
+    //      waiting for the other splits' partials, but only if every split of
+    //      the tile had started when it decided (then all of them are running
+    //      and arrive without waiting on anything, so the wait ends); otherwise
+    //      it hands the slice to whichever workgroup arrives last, which also
+    //      takes slices without an owner.  The hand-over travels in the same
+    //      atomic as the arrival, so no fence is needed.  Partials are summed
+    //      in split order, whoever finishes (bitwise repeatable).
     constexpr int NACC = C::NSUB * C::MSUB * 4;
     uint32_t todo = (1u << C::MSUB) - 1;     // slices this workgroup outputs
     if (a.ksplit > 1) {
@@ -421,6 +430,9 @@ void wide_gemm_kernel(KArgs a) {
         const int64_t sstride = static_cast<int64_t>(gridDim.y) * a.groups * per;
         const Coherent part(a.part, a.part_bytes);
         auto off = [&](int sp, int f) { return static_cast<uint32_t>((sp * sstride + slot * per + f * C::THREADS + tid) * 16); };
+        // have all splits of the tile started?  (read while the stores drain)
+        uint32_t started = 0;
+        if (tid == 0) started = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int ns = 0; ns < C::NSUB; ++ns)
 #pragma unroll
@@ -431,20 +443,44 @@ void wide_gemm_kernel(KArgs a) {
                     part.store(off(split, (ns * C::MSUB + ms) * 4 + rq), f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]});
                 }
         // every wave's partial stores have completed (stores count in vmcnt),
-        // then the barrier orders them before the arrivals; the flags live in
+        // then the barrier orders them before the arrival; the flag lives in
         // stage buffer 0, which every wave has finished reading
         int* const flags = reinterpret_cast<int*>(lds0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid < C::MSUB) {
-            const uint32_t prev = __hip_atomic_fetch_add(a.tickets + slot * C::MSUB + tid, 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            flags[tid] = (prev == static_cast<uint32_t>(a.ksplit - 1)) ? 1 : 0;
+        if (tid == 0) {
+            const uint32_t ks = static_cast<uint32_t>(a.ksplit);
+            const int own = split < C::MSUB ? split : -1;
+            const bool wait_own = own >= 0 && started == ks;
+            const uint32_t add = 1u + ((own >= 0 && !wait_own) ? (1u << (16 + own)) : 0u);
+            const uint32_t prev = __hip_atomic_fetch_add(ctr + 1, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t mine = 0;
+            if ((prev & 0xFFFFu) == ks - 1) {
+                const uint32_t handed = (prev + add) >> 16;
+#pragma unroll
+                for (int ms = 0; ms < C::MSUB; ++ms)
+                    if (((handed >> ms) & 1u) || ms >= a.ksplit) mine |= 1u << ms;
+            }
+            if (wait_own) {
+                for (int it = 0; it < kWideSpinMax; ++it) {
+                    if ((__hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFFFFu) == ks) {
+                        mine |= 1u << own;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            // no counter of the tile is read after this point; the last
+            // workgroup past it clears them for the next call
+            if (__hip_atomic_fetch_add(ctr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ks - 1) {
+                __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ctr + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            flags[0] = static_cast<int>(mine);
         }
         __syncthreads();
-        todo = 0;
-#pragma unroll
-        for (int ms = 0; ms < C::MSUB; ++ms) todo |= flags[ms] ? (1u << ms) : 0u;
+        todo = static_cast<uint32_t>(flags[0]);
         if (todo == 0) return;
 #pragma unroll
         for (int ms = 0; ms < C::MSUB; ++ms) {
@@ -476,8 +512,6 @@ void wide_gemm_kernel(KArgs a) {
                 for (int rq = 0; rq < 4; ++rq)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[ns][ms][4 * rq + e] = sum[ns][rq][e];
-            if (tid == 0)
-                __hip_atomic_store(a.tickets + slot * C::MSUB + ms, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     // ---- output: one pass per 32-row sub-tile ms (64 rows: both wm halves).

@@ -65,12 +65,14 @@ struct GemmPlan {
 };
 
 // The first kCounterBytes of every GEMM workspace hold the split-K arrival
-// counters (one uint32 per skinny output group, three per wide output tile),
+// counters (one uint32 per skinny output group, kWideCounters per wide output
+// tile: workgroups started, arrivals with handed-over slices, workgroups done),
 // at the same place for every shape, so one zero-filled workspace can serve
 // calls of different shapes.  Its last 4 KiB are not used.
 constexpr size_t kCounterBytes = 65536;
 constexpr size_t kZeroPageOffset = kCounterBytes - 4096;
 constexpr int kMaxCounters = static_cast<int>(kZeroPageOffset / 4);
+constexpr int kWideCounters = 4;   // three used, one pad
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi);
 size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N);
