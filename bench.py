@@ -348,9 +348,39 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
         out["chain_us_per_replay_cold"] = round(float(np.median(cold)), 2)
         chain_bytes = L * (2 * I * H + 8 * I + H * I + 4 * H) + 2 * 2 * M * H
         out["chain_cold_GBps"] = round(chain_bytes / (np.median(cold) * 1e-6) / 1e9, 1)
-        del flush
     finally:
         vla.vla_mlp_chain_destroy(h)
+
+    log("secondary: 18-layer decoder-block chain (MLP + fused boundary per layer)")
+    dx, dh, dg, dstyle = synthetic.decoder_chain_inputs(L, M, H, M)
+    d_in = [up_bits(a) for a in (dx, dh, dg)]
+    d_style = [up_bits(s_) for s_ in dstyle]
+    d_out = [torch.empty(M * H, dtype=torch.int16, device=dev) for _ in range(3)]
+    dsb = vla.vla_decoder_chain_scratch_bytes(M, H, I)
+    dscratch = torch.zeros(dsb, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    h = vla.vla_decoder_chain_create(wgu, sgu, wd, sd, d_style, True, 1e-6, *d_in, *d_out, dscratch, dsb,
+                                     L, M, H, I, cs)
+    try:
+        for _ in range(5):
+            vla.vla_mlp_chain_replay(h, cs)
+        cs.synchronize()
+        warm, cold = [], []
+        for i in range(40):
+            if i % 2 == 1:
+                flush.fill_(i & 0xFF)
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cs)
+            vla.vla_mlp_chain_replay(h, cs)
+            e1.record(cs)
+            cs.synchronize()
+            (cold if i % 2 == 1 else warm).append(e0.elapsed_time(e1) * 1000.0)
+        out["decoder_chain_us_per_replay_warm"] = round(float(np.median(warm)), 2)
+        out["decoder_chain_us_per_replay_cold"] = round(float(np.median(cold)), 2)
+    finally:
+        vla.vla_mlp_chain_destroy(h)
+    del flush
 
     log("secondary: dialect conversion 16384 x 2048")
     N, K = 16384, 2048

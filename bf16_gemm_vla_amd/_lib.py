@@ -57,6 +57,11 @@ SIGNATURES = {
     "vla_mlp_chain_enqueue": (INT, [P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P]),
     "vla_mlp_chain_create": (INT, [P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P, P]),
     "vla_mlp_chain_replay": (INT, [P, P]),
+    "vla_decoder_chain_scratch_bytes": (SZ, [I64, I64, I64]),
+    "vla_decoder_chain_enqueue": (INT, [P, P, P, P, P, INT, ctypes.c_float, P, P, P, P, P, P, P, SZ, INT, I64, I64,
+                                        I64, P]),
+    "vla_decoder_chain_create": (INT, [P, P, P, P, P, INT, ctypes.c_float, P, P, P, P, P, P, P, SZ, INT, I64, I64,
+                                       I64, P, P]),
     "vla_mlp_chain_destroy": (INT, [P]),
 }
 
@@ -220,6 +225,37 @@ def vla_mlp_chain_create(wgu, sgu, wd, sd, x_in, x_out, scratch, scratch_bytes, 
                                        _ptr_array(sd), _ptr(x_in), _ptr(x_out), _ptr(scratch),
                                        scratch_bytes, L, M, H, I, _stream(capture_stream),
                                        ctypes.byref(out)), "vla_mlp_chain_create")
+    return out.value
+
+
+def vla_decoder_chain_scratch_bytes(M: int, H: int, I: int) -> int:
+    return load().vla_decoder_chain_scratch_bytes(M, H, I)
+
+
+def _decoder_args(wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out, gate_out,
+                  scratch, scratch_bytes, L, M, H, I):
+    return (_ptr_array(wgu), _ptr_array(sgu), _ptr_array(wd), _ptr_array(sd), _ptr_array(style),
+            int(bool(style_per_row)), float(eps), _ptr(x_in), _ptr(h_in), _ptr(gate_in), _ptr(x_out),
+            _ptr(h_out), _ptr(gate_out), _ptr(scratch), scratch_bytes, L, M, H, I)
+
+
+def vla_decoder_chain_enqueue(wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
+                              gate_out, scratch, scratch_bytes, L, M, H, I, stream=None):
+    _check(load().vla_decoder_chain_enqueue(*_decoder_args(wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in,
+                                                           gate_in, x_out, h_out, gate_out, scratch, scratch_bytes,
+                                                           L, M, H, I), _stream(stream)),
+           "vla_decoder_chain_enqueue")
+
+
+def vla_decoder_chain_create(wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
+                             gate_out, scratch, scratch_bytes, L, M, H, I, capture_stream):
+    """Returns the chain handle (an opaque int); replay / destroy it with the
+    gated-MLP chain calls."""
+    out = ctypes.c_void_p()
+    _check(load().vla_decoder_chain_create(*_decoder_args(wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in,
+                                                          gate_in, x_out, h_out, gate_out, scratch, scratch_bytes,
+                                                          L, M, H, I), _stream(capture_stream),
+                                           ctypes.byref(out)), "vla_decoder_chain_create")
     return out.value
 
 

@@ -161,6 +161,152 @@ int enqueue_chain(const char* fn, const uint8_t* const* wgu, const float* const*
     return VLA_OK;
 }
 
+// Decoder-block chain scratch: x | h | gate (two, alternating) | down output |
+// act | GEMM workspace.
+struct DecoderLayout {
+    size_t x_off, h_off, g_off[2], d_off, act_off, ws_off, total, ws_bytes;
+};
+
+DecoderLayout decoder_layout(int64_t M, int64_t H, int64_t I) {
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t mh = up(static_cast<size_t>(M) * H * 2);
+    DecoderLayout c{};
+    c.x_off = 0;
+    c.h_off = mh;
+    c.g_off[0] = 2 * mh;
+    c.g_off[1] = 3 * mh;
+    c.d_off = 4 * mh;
+    c.act_off = 5 * mh;
+    c.ws_off = c.act_off + up(static_cast<size_t>(M) * I * 2);
+    const ChainLayout cl = chain_layout(M, H, I);
+    c.ws_bytes = cl.ws_bytes;
+    c.total = c.ws_off + c.ws_bytes;
+    return c;
+}
+
+int check_decoder(const char* fn, const uint8_t* const* wgu, const float* const* sgu, const uint8_t* const* wd,
+                  const float* const* sd, const uint16_t* const* style, int style_per_row, float eps,
+                  const uint16_t* x_in, const uint16_t* h_in, const uint16_t* gate_in, uint16_t* x_out,
+                  uint16_t* h_out, uint16_t* gate_out, void* scratch, size_t scratch_bytes, int L, int64_t M,
+                  int64_t H, int64_t I) {
+    if (!wgu || !sgu || !wd || !sd || !style) return fail(VLA_EINVAL, fn, "pointer arrays must not be NULL");
+    if (L <= 0) return fail(VLA_EINVAL, fn, "L=%d must be positive", L);
+    if (int rc = check_mnk(fn, M, 2 * I, H)) return rc;
+    if (int rc = check_nk(fn, H, I)) return rc;
+    if (I % 16 != 0) return fail(VLA_ESHAPE, fn, "I=%lld is not a multiple of 16", (long long)I);
+    if (!vla::boundary_width_ok(H)) return fail(VLA_ESHAPE, fn, "H=%lld must be at most 8192", (long long)H);
+    if (!std::isfinite(eps) || eps < 0.0f) return fail(VLA_EINVAL, fn, "eps must be finite and >= 0");
+    REQUIRE_PTR(x_in);
+    REQUIRE_PTR(h_in);
+    REQUIRE_PTR(gate_in);
+    REQUIRE_PTR(x_out);
+    REQUIRE_PTR(h_out);
+    REQUIRE_PTR(gate_out);
+    REQUIRE_PTR(scratch);
+    for (int l = 0; l < L; ++l) {
+        if (!wgu[l] || !sgu[l] || !wd[l] || !sd[l] || !style[l]) return fail(VLA_EINVAL, fn, "layer %d has a NULL pointer", l);
+        if (!aligned16(wgu[l]) || !aligned16(sgu[l]) || !aligned16(wd[l]) || !aligned16(sd[l]) || !aligned16(style[l]))
+            return fail(VLA_EALIGN, fn, "layer %d pointer not 16-byte aligned", l);
+    }
+    const DecoderLayout c = decoder_layout(M, H, I);
+    if (scratch_bytes < c.total)
+        return fail(VLA_EWORKSPACE, fn, "scratch %zu bytes < required %zu", scratch_bytes, c.total);
+    const size_t mat = static_cast<size_t>(M) * H * 2;
+    const size_t sty = static_cast<size_t>(style_per_row ? M : 1) * 3 * H * 2;
+    auto overlap = [](const void* x, size_t nx, const void* y, size_t ny) {
+        const uint8_t *a = static_cast<const uint8_t*>(x), *b = static_cast<const uint8_t*>(y);
+        return a < b + ny && b < a + nx;
+    };
+    const void* outs[3] = {x_out, h_out, gate_out};
+    const void* ins[3] = {x_in, h_in, gate_in};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], mat, outs[j], mat)) return fail(VLA_EINVAL, fn, "outputs %d and %d overlap", i, j);
+        for (int j = 0; j < 3; ++j)
+            if (overlap(outs[i], mat, ins[j], mat)) return fail(VLA_EINVAL, fn, "output %d overlaps input %d", i, j);
+        if (overlap(outs[i], mat, scratch, c.total)) return fail(VLA_EINVAL, fn, "output %d overlaps scratch", i);
+        for (int l = 0; l < L; ++l)
+            if (overlap(outs[i], mat, style[l], sty)) return fail(VLA_EINVAL, fn, "output %d overlaps style %d", i, l);
+    }
+    for (int j = 0; j < 3; ++j)
+        if (overlap(ins[j], mat, scratch, c.total)) return fail(VLA_EINVAL, fn, "input %d overlaps scratch", j);
+    return VLA_OK;
+}
+
+int enqueue_decoder(const char* fn, const uint8_t* const* wgu, const float* const* sgu, const uint8_t* const* wd,
+                    const float* const* sd, const uint16_t* const* style, int style_per_row, float eps,
+                    const uint16_t* x_in, const uint16_t* h_in, const uint16_t* gate_in, uint16_t* x_out,
+                    uint16_t* h_out, uint16_t* gate_out, void* scratch, int L, int64_t M, int64_t H, int64_t I,
+                    hipStream_t s) {
+    const DecoderLayout c = decoder_layout(M, H, I);
+    uint8_t* base = static_cast<uint8_t*>(scratch);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(base + c.x_off);
+    uint16_t* hs = reinterpret_cast<uint16_t*>(base + c.h_off);
+    uint16_t* gs[2] = {reinterpret_cast<uint16_t*>(base + c.g_off[0]), reinterpret_cast<uint16_t*>(base + c.g_off[1])};
+    uint16_t* dbuf = reinterpret_cast<uint16_t*>(base + c.d_off);
+    uint16_t* act = reinterpret_cast<uint16_t*>(base + c.act_off);
+    void* ws = base + c.ws_off;
+    const uint16_t *x = x_in, *h = h_in, *g = gate_in;
+    for (int l = 0; l < L; ++l) {
+        vla::GemmProblem gp{};
+        gp.A = h; gp.W = wgu[l]; gp.s_w = sgu[l]; gp.Y = act; gp.ws = ws;
+        gp.M = M; gp.N = 2 * I; gp.K = H;
+        gp.atype = vla::AType::BF16; gp.wtype = vla::WType::FP8; gp.epi = vla::Epi::GELU_MUL;
+        if (int rc = run_gemm(fn, gp, c.ws_bytes, s)) return rc;
+        vla::GemmProblem dp{};
+        dp.A = act; dp.W = wd[l]; dp.s_w = sd[l]; dp.Y = dbuf; dp.ws = ws;
+        dp.M = M; dp.N = H; dp.K = I;
+        dp.atype = vla::AType::BF16; dp.wtype = vla::WType::FP8; dp.epi = vla::Epi::PLAIN;
+        if (int rc = run_gemm(fn, dp, c.ws_bytes, s)) return rc;
+        const bool last = l == L - 1;
+        uint16_t* xo = last ? x_out : xs;        // in place from the second layer on
+        uint16_t* ho = last ? h_out : hs;        // this layer's GEMM has read h already
+        uint16_t* go = last ? gate_out : gs[l & 1];
+        hipError_t e = vla::launch_gate_residual_ada_norm(x, dbuf, g, style[l], style_per_row ? 1 : 0, eps, xo, ho, go,
+                                                          M, H, s);
+        if (e != hipSuccess) return hip_fail(fn, "boundary launch", e);
+        x = xo; h = ho; g = go;
+    }
+    return VLA_OK;
+}
+
+// Capture `enqueue` on capture_stream into a graph and instantiate it.
+template <class F>
+int capture_chain(const char* fn, void* capture_stream, int L, vla_mlp_chain** out, F&& enqueue) {
+    hipStream_t s = static_cast<hipStream_t>(capture_stream);
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed);
+    if (e != hipSuccess) return hip_fail(fn, "hipStreamBeginCapture", e);
+    int rc = enqueue(s);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(s, &graph);
+    if (rc != VLA_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+    }
+    if (e != hipSuccess) return hip_fail(fn, "hipStreamEndCapture", e);
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        return hip_fail(fn, "hipGraphInstantiate", e);
+    }
+    vla_mlp_chain* h = new (std::nothrow) vla_mlp_chain;
+    if (!h) {
+        (void)hipGraphExecDestroy(exec);
+        (void)hipGraphDestroy(graph);
+        return fail(VLA_EINVAL, fn, "out of host memory");
+    }
+    h->graph = graph;
+    h->exec = exec;
+    h->layers = L;
+    {
+        std::lock_guard<std::mutex> lk(g_chain_mu);
+        g_chains.insert(h);
+    }
+    *out = h;
+    return VLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -428,38 +574,45 @@ int vla_mlp_chain_create(const uint8_t* const* wgu, const float* const* sgu,
     *out = nullptr;
     if (!capture_stream) return fail(VLA_EINVAL, fn, "capture_stream must not be the null stream");
     if (int rc = check_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, scratch_bytes, L, M, H, I)) return rc;
-    hipStream_t s = static_cast<hipStream_t>(capture_stream);
-    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed);
-    if (e != hipSuccess) return hip_fail(fn, "hipStreamBeginCapture", e);
-    int rc = enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I, s);
-    hipGraph_t graph = nullptr;
-    e = hipStreamEndCapture(s, &graph);
-    if (rc != VLA_OK) {
-        if (graph) (void)hipGraphDestroy(graph);
+    return capture_chain(fn, capture_stream, L, out, [&](hipStream_t s) {
+        return enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I, s);
+    });
+}
+
+size_t vla_decoder_chain_scratch_bytes(int64_t M, int64_t H, int64_t I) {
+    if (M <= 0 || H <= 0 || I <= 0) return 0;
+    return decoder_layout(M, H, I).total;
+}
+
+int vla_decoder_chain_enqueue(const uint8_t* const* wgu, const float* const* sgu, const uint8_t* const* wd,
+                              const float* const* sd, const uint16_t* const* style, int style_per_row, float eps,
+                              const uint16_t* x_in, const uint16_t* h_in, const uint16_t* gate_in, uint16_t* x_out,
+                              uint16_t* h_out, uint16_t* gate_out, void* scratch, size_t scratch_bytes, int L,
+                              int64_t M, int64_t H, int64_t I, void* stream) {
+    const char* fn = "vla_decoder_chain_enqueue";
+    if (int rc = check_decoder(fn, wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
+                               gate_out, scratch, scratch_bytes, L, M, H, I))
         return rc;
-    }
-    if (e != hipSuccess) return hip_fail(fn, "hipStreamEndCapture", e);
-    hipGraphExec_t exec = nullptr;
-    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    if (e != hipSuccess) {
-        (void)hipGraphDestroy(graph);
-        return hip_fail(fn, "hipGraphInstantiate", e);
-    }
-    vla_mlp_chain* h = new (std::nothrow) vla_mlp_chain;
-    if (!h) {
-        (void)hipGraphExecDestroy(exec);
-        (void)hipGraphDestroy(graph);
-        return fail(VLA_EINVAL, fn, "out of host memory");
-    }
-    h->graph = graph;
-    h->exec = exec;
-    h->layers = L;
-    {
-        std::lock_guard<std::mutex> lk(g_chain_mu);
-        g_chains.insert(h);
-    }
-    *out = h;
-    return VLA_OK;
+    return enqueue_decoder(fn, wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
+                           gate_out, scratch, L, M, H, I, static_cast<hipStream_t>(stream));
+}
+
+int vla_decoder_chain_create(const uint8_t* const* wgu, const float* const* sgu, const uint8_t* const* wd,
+                             const float* const* sd, const uint16_t* const* style, int style_per_row, float eps,
+                             const uint16_t* x_in, const uint16_t* h_in, const uint16_t* gate_in, uint16_t* x_out,
+                             uint16_t* h_out, uint16_t* gate_out, void* scratch, size_t scratch_bytes, int L,
+                             int64_t M, int64_t H, int64_t I, void* capture_stream, vla_mlp_chain** out) {
+    const char* fn = "vla_decoder_chain_create";
+    if (!out) return fail(VLA_EINVAL, fn, "out is NULL");
+    *out = nullptr;
+    if (!capture_stream) return fail(VLA_EINVAL, fn, "capture_stream must not be the null stream");
+    if (int rc = check_decoder(fn, wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
+                               gate_out, scratch, scratch_bytes, L, M, H, I))
+        return rc;
+    return capture_chain(fn, capture_stream, L, out, [&](hipStream_t s) {
+        return enqueue_decoder(fn, wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
+                               gate_out, scratch, L, M, H, I, s);
+    });
 }
 
 int vla_mlp_chain_replay(vla_mlp_chain* chain, void* stream) {

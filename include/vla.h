@@ -282,6 +282,47 @@ int vla_mlp_chain_replay(vla_mlp_chain *chain, void *stream);
  * destroying NULL is a no-op returning VLA_OK. */
 int vla_mlp_chain_destroy(vla_mlp_chain *chain);
 
+/* ---------------------------------------------------- decoder-block chain */
+
+/* L action-decoder MLP blocks closed by the fused decoder boundary
+ * ("Real-time VLA inference on AMD hardware", sections "Merging gate and
+ * up" and "Fusing the BF16 decoder boundary"): per layer l, from the
+ * residual x, the normalized input h and the gate g (each M x H bf16),
+ *   act       = gelu_mul(h @ [Wgate_l; Wup_l]^T)    (vla_gemm_fp8w_gelu_mul)
+ *   d         = bf16(act @ Wdown_l^T)               (vla_gemm_fp8w)
+ *   (x, h, g) = vla_gate_residual_ada_norm(x, d, g, style_l, eps)
+ * three kernels per layer, recorded once as a HIP graph like the gated-MLP
+ * chain.  The final x, h and g are the outputs.
+ *   wgu, sgu, wd, sd  as for the gated-MLP chain.
+ *   style        host array of L device pointers: bf16 (style_per_row ? M : 1)
+ *                x 3H, [scale | shift | next gate] (see the boundary).
+ *   eps          finite, >= 0.
+ *   x_in, h_in, gate_in     device bf16 M x H inputs (read only).
+ *   x_out, h_out, gate_out  device bf16 M x H outputs; none may overlap
+ *                another output, an input, a style array or scratch.
+ *   scratch      device, vla_decoder_chain_scratch_bytes(M, H, I) bytes,
+ *                ZERO-FILLED before first use (it embeds a GEMM workspace);
+ *                the inputs must not overlap it.
+ * H and I multiples of 32, H at most 8192.  The handle from
+ * vla_decoder_chain_create is replayed and destroyed with
+ * vla_mlp_chain_replay / vla_mlp_chain_destroy. */
+size_t vla_decoder_chain_scratch_bytes(int64_t M, int64_t H, int64_t I);
+
+int vla_decoder_chain_enqueue(const uint8_t *const *wgu, const float *const *sgu,
+                              const uint8_t *const *wd, const float *const *sd,
+                              const uint16_t *const *style, int style_per_row, float eps,
+                              const uint16_t *x_in, const uint16_t *h_in, const uint16_t *gate_in,
+                              uint16_t *x_out, uint16_t *h_out, uint16_t *gate_out, void *scratch,
+                              size_t scratch_bytes, int L, int64_t M, int64_t H, int64_t I, void *stream);
+
+int vla_decoder_chain_create(const uint8_t *const *wgu, const float *const *sgu,
+                             const uint8_t *const *wd, const float *const *sd,
+                             const uint16_t *const *style, int style_per_row, float eps,
+                             const uint16_t *x_in, const uint16_t *h_in, const uint16_t *gate_in,
+                             uint16_t *x_out, uint16_t *h_out, uint16_t *gate_out, void *scratch,
+                             size_t scratch_bytes, int L, int64_t M, int64_t H, int64_t I,
+                             void *capture_stream, vla_mlp_chain **out);
+
 #ifdef __cplusplus
 }
 #endif

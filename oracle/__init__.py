@@ -77,6 +77,8 @@ def _load():
                 "orc_gelu_mul": (None, [P, P, I64, P]),
                 "orc_mlp_chain": (None, [P, P, P, P, P, INT, I64, I64, I64, P, P, P, P]),
                 "orc_gate_residual_ada_norm": (None, [P, P, P, P, INT, ctypes.c_float, I64, I64, P, P, P]),
+                "orc_decoder_chain": (None, [P, P, P, P, P, P, P, P, I64, INT, ctypes.c_float, INT, I64, I64, I64,
+                                             P, P, P]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(lib, name)
@@ -276,3 +278,27 @@ def gate_residual_ada_norm(residual, out, gate, style, eps: float, style_per_row
     _load().orc_gate_residual_ada_norm(_p(residual), _p(out), _p(gate), _p(style), int(bool(style_per_row)),
                                        ctypes.c_float(float(np.float32(eps))), M, D, _p(r), _p(h), _p(ng))
     return r, h, ng
+
+
+def decoder_chain(x_in, h_in, g_in, wgu, sgu, wd, sd, styles, eps: float, style_per_row: bool = True):
+    """Decoder-block chain on row-major OCP codes: per layer the merged
+    gate/up GEMM with GELU*mul, the down GEMM, then the fused boundary.
+    x_in, h_in, g_in: M x H bf16 bits; styles: L arrays of (M or 1) x 3H.
+    Returns (x_out, h_out, g_out)."""
+    x = _c(x_in, np.uint16)
+    h = _c(h_in, np.uint16)
+    g = _c(g_in, np.uint16)
+    M, H = x.shape
+    L = len(wgu)
+    I = wgu[0].shape[0] // 2
+    keep = [_c(w, np.uint8) for w in wgu] + [_c(w, np.uint8) for w in wd]
+    keep_s = [_c(v, np.float32) for v in sgu] + [_c(v, np.float32) for v in sd]
+    rows = M if style_per_row else 1
+    st = np.ascontiguousarray(np.stack([_c(s, np.uint16).reshape(rows, 3 * H) for s in styles]))
+    assert st.shape == (L, rows, 3 * H)
+    arr = lambda xs: (ctypes.c_void_p * len(xs))(*[a.ctypes.data for a in xs])
+    xo, ho, go = (np.empty((M, H), np.uint16) for _ in range(3))
+    _load().orc_decoder_chain(_p(x), _p(h), _p(g), arr(keep[:L]), arr(keep_s[:L]), arr(keep[L:]),
+                              arr(keep_s[L:]), _p(st), rows * 3 * H, int(bool(style_per_row)),
+                              ctypes.c_float(float(np.float32(eps))), L, M, H, I, _p(xo), _p(ho), _p(go))
+    return xo, ho, go

@@ -422,3 +422,61 @@ void orc_gate_residual_ada_norm(const uint16_t *residual, const uint16_t *out, c
     }
     free(r);
 }
+
+/* Decoder-block chain: the gated-MLP chain with the fused decoder boundary
+ * closing every layer ([P1] "Merging gate and up", "Fusing the BF16 decoder
+ * boundary").  State per layer: residual x, normalized input h, gate g (all
+ * M x H bf16).  For l = 0 .. L-1:
+ *   gu  = bf16(h @ [Wgate; Wup]_l^T)            (merged GEMM, rounded once)
+ *   act = bf16(gelu_tanh(g_part) * u_part)
+ *   d   = bf16(act @ Wdown_l^T)
+ *   (x, h, g) = gate_residual_ada_norm(x, d, g, style_l, eps)
+ * style_l: (style_per_row ? M : 1) x 3H bf16 per layer, consecutive layers
+ * `style_stride` elements apart.  Outputs the final x, h, g. */
+void orc_decoder_chain(const uint16_t *x_in, const uint16_t *h_in, const uint16_t *g_in,
+                       const uint8_t *const *wgu, const float *const *sgu, const uint8_t *const *wd,
+                       const float *const *sd, const uint16_t *style, int64_t style_stride, int style_per_row,
+                       float eps, int L, int64_t M, int64_t H, int64_t I,
+                       uint16_t *x_out, uint16_t *h_out, uint16_t *g_out)
+{
+    double *hv = malloc(sizeof(double) * M * H);
+    double *wg = malloc(sizeof(double) * 2 * I * H);
+    double *wdn = malloc(sizeof(double) * H * I);
+    double *gu = malloc(sizeof(double) * M * 2 * I);
+    double *act = malloc(sizeof(double) * M * I);
+    double *dn = malloc(sizeof(double) * M * H);
+    uint16_t *gb = malloc(sizeof(uint16_t) * M * 2 * I);
+    uint16_t *ab = malloc(sizeof(uint16_t) * M * I);
+    uint16_t *db = malloc(sizeof(uint16_t) * M * H);
+    uint16_t *x = malloc(sizeof(uint16_t) * M * H);
+    uint16_t *h = malloc(sizeof(uint16_t) * M * H);
+    uint16_t *g = malloc(sizeof(uint16_t) * M * H);
+    uint16_t *x2 = malloc(sizeof(uint16_t) * M * H);
+    uint16_t *h2 = malloc(sizeof(uint16_t) * M * H);
+    uint16_t *g2 = malloc(sizeof(uint16_t) * M * H);
+    memcpy(x, x_in, sizeof(uint16_t) * M * H);
+    memcpy(h, h_in, sizeof(uint16_t) * M * H);
+    memcpy(g, g_in, sizeof(uint16_t) * M * H);
+    for (int l = 0; l < L; ++l) {
+        orc_bf16_to_f64(h, M * H, hv);
+        orc_dequant_rows(wgu[l], sgu[l], 2 * I, H, ORC_OCP, wg);
+        orc_dequant_rows(wd[l], sd[l], H, I, ORC_OCP, wdn);
+        orc_gemm(hv, wg, NULL, M, 2 * I, H, gu, NULL);
+        orc_bf16_round_array(gu, M * 2 * I, gb);
+        for (int64_t m = 0; m < M; ++m)
+            orc_gelu_mul(gb + m * 2 * I, gb + m * 2 * I + I, I, ab + m * I);
+        orc_bf16_to_f64(ab, M * I, act);
+        orc_gemm(act, wdn, NULL, M, H, I, dn, NULL);
+        orc_bf16_round_array(dn, M * H, db);
+        orc_gate_residual_ada_norm(x, db, g, style + (int64_t)l * style_stride, style_per_row, eps, M, H,
+                                   x2, h2, g2);
+        memcpy(x, x2, sizeof(uint16_t) * M * H);
+        memcpy(h, h2, sizeof(uint16_t) * M * H);
+        memcpy(g, g2, sizeof(uint16_t) * M * H);
+    }
+    memcpy(x_out, x, sizeof(uint16_t) * M * H);
+    memcpy(h_out, h, sizeof(uint16_t) * M * H);
+    memcpy(g_out, g, sizeof(uint16_t) * M * H);
+    free(hv); free(wg); free(wdn); free(gu); free(act); free(dn); free(gb); free(ab); free(db);
+    free(x); free(h); free(g); free(x2); free(h2); free(g2);
+}

@@ -64,6 +64,8 @@ IDS = {
     "dialect.W": 30,
     "chain.x": 40,
     "boundary.residual": 50, "boundary.out": 51, "boundary.gate": 52, "boundary.style": 53,
+    "decoder.x": 60, "decoder.h": 61, "decoder.gate": 62,
+    "decoder.style": 400,   # + layer
     "chain.gate": 100,   # + layer
     "chain.up": 200,     # + layer
     "chain.down": 300,   # + layer
@@ -90,3 +92,15 @@ def boundary_inputs(M: int, D: int, style_rows: int, seed: int = 0):
     return (draw((M, D), "boundary.residual", 1.0), draw((M, D), "boundary.out", 1.0),
             draw((M, D), "boundary.gate", MODULATION_SIGMA),
             draw((style_rows, 3 * D), "boundary.style", MODULATION_SIGMA))
+
+
+def decoder_chain_inputs(L: int, M: int, H: int, style_rows: int, seed: int = 0):
+    """bf16 bit patterns for the decoder-block chain: residual x and normalized
+    input h ~ N(0, 1), gate ~ N(0, 0.1) (M x H), and one style array
+    (style_rows x 3H, N(0, 0.1)) per layer."""
+    def draw(shape, tid, sigma):
+        x = rng(tid, seed).standard_normal(shape, dtype=np.float32) * np.float32(sigma)
+        return fp32_to_bf16_bits(x)
+    return (draw((M, H), IDS["decoder.x"], 1.0), draw((M, H), IDS["decoder.h"], 1.0),
+            draw((M, H), IDS["decoder.gate"], MODULATION_SIGMA),
+            [draw((style_rows, 3 * H), IDS["decoder.style"] + l, MODULATION_SIGMA) for l in range(L)])

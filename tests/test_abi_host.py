@@ -138,6 +138,35 @@ def test_boundary_errors(lib):
     assert rc(X, Y, G, S, 0, 1e-6, R, H, S + 16, 50, 1024, None) == vla.VLA_EINVAL
 
 
+def test_decoder_chain_errors(lib):
+    arr = (ctypes.c_void_p * 2)(A16, A16)
+    M, H, I = 50, 1024, 4096
+    need = vla.vla_decoder_chain_scratch_bytes(M, H, I)
+    assert need > vla.vla_mlp_chain_scratch_bytes(M, H, I)
+    mat = M * H * 2
+    XI, HI, GI = 1 << 33, (1 << 33) + mat, (1 << 33) + 2 * mat          # inputs
+    XO, HO, GO = 1 << 34, (1 << 34) + mat, (1 << 34) + 2 * mat          # outputs
+    SC = 1 << 35
+
+    def rc(style=arr, per_row=1, eps=1e-6, xo=XO, ho=HO, go=GO, scratch=SC, nbytes=need, L=2, Hh=H):
+        return rc_of("vla_decoder_chain_enqueue", arr, arr, arr, arr, style, per_row, eps, XI, HI, GI, xo, ho, go,
+                     scratch, nbytes, L, M, Hh, I, None)
+    assert rc(style=None) == vla.VLA_EINVAL
+    assert rc(L=0) == vla.VLA_EINVAL
+    assert rc(eps=-1.0) == vla.VLA_EINVAL
+    assert rc(nbytes=need - 1) == vla.VLA_EWORKSPACE
+    assert rc(ho=HI + 16) == vla.VLA_EINVAL                     # output over an input
+    assert rc(go=XO + 16) == vla.VLA_EINVAL                     # outputs overlap
+    assert rc(xo=SC + 64) == vla.VLA_EINVAL                     # output in scratch
+    assert rc(style=(ctypes.c_void_p * 2)(A16, A16 + 8)) == vla.VLA_EALIGN
+    assert rc(style=(ctypes.c_void_p * 2)(A16, None)) == vla.VLA_EINVAL
+    assert rc(style=(ctypes.c_void_p * 2)(A16, XO - 64)) == vla.VLA_EINVAL    # output over a style array
+    assert rc(Hh=1040) == vla.VLA_ESHAPE
+    out = ctypes.c_void_p()
+    assert rc_of("vla_decoder_chain_create", arr, arr, arr, arr, arr, 1, 1e-6, XI, HI, GI, XO, HO, GO, SC, need, 2,
+                 M, H, I, None, ctypes.byref(out)) == vla.VLA_EINVAL
+
+
 def test_chain_errors(lib):
     arr = (ctypes.c_void_p * 2)(A16, A16)
     need = vla.vla_mlp_chain_scratch_bytes(50, 1024, 4096)

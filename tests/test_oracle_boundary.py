@@ -105,3 +105,59 @@ def test_rows_are_independent():
     part = oracle.gate_residual_ada_norm(x[3:7], y[3:7], g[3:7], st[3:7], 1e-6)
     for u, v in zip(full, part):
         assert np.array_equal(u[3:7], v)
+
+
+# ------------------------------------------------------ decoder-block chain
+
+def _chain_layer_weights(L, H, I, seed):
+    gate, up, down = synthetic.chain_weights(L, H, I, seed)
+    wgu, sgu, wd, sd = [], [], [], []
+    for l in range(L):
+        q, s = oracle.quantize_rows(np.concatenate([gate[l], up[l]]), oracle.OCP)
+        wgu.append(q); sgu.append(s)
+        q, s = oracle.quantize_rows(down[l], oracle.OCP)
+        wd.append(q); sd.append(s)
+    return wgu, sgu, wd, sd
+
+
+def test_decoder_chain_one_layer_is_the_stage_composition():
+    """One layer = merged GEMM, bf16, GELU*mul, down GEMM, bf16, boundary —
+    each stage an oracle function pinned on its own."""
+    L, M, H, I = 1, 6, 64, 128
+    wgu, sgu, wd, sd = _chain_layer_weights(L, H, I, 3)
+    x, h, g, st = synthetic.decoder_chain_inputs(L, M, H, M)
+    got = oracle.decoder_chain(x, h, g, wgu, sgu, wd, sd, st, 1e-6)
+    gu, _ = oracle.gemm(oracle.bf16_value(h), oracle.dequant_rows(wgu[0], sgu[0]))
+    gub = oracle.bf16_round(gu)
+    act = oracle.gelu_mul(gub[:, :I], gub[:, I:])
+    d, _ = oracle.gemm(oracle.bf16_value(act), oracle.dequant_rows(wd[0], sd[0]))
+    want = oracle.gate_residual_ada_norm(x, oracle.bf16_round(d), g, st[0], 1e-6)
+    for u, v in zip(got, want):
+        assert np.array_equal(u, v)
+
+
+def test_decoder_chain_layers_compose():
+    L, M, H, I = 3, 5, 64, 96
+    wgu, sgu, wd, sd = _chain_layer_weights(L, H, I, 4)
+    x, h, g, st = synthetic.decoder_chain_inputs(L, M, H, 1)
+    full = oracle.decoder_chain(x, h, g, wgu, sgu, wd, sd, st, 1e-6, style_per_row=False)
+    cur = (x, h, g)
+    for l in range(L):
+        cur = oracle.decoder_chain(*cur, wgu[l:l + 1], sgu[l:l + 1], wd[l:l + 1], sd[l:l + 1], st[l:l + 1], 1e-6,
+                                   style_per_row=False)
+    for u, v in zip(full, cur):
+        assert np.array_equal(u, v)
+
+
+def test_decoder_chain_zero_down_weights_keep_the_residual():
+    """All-zero down weights: d = 0, so the residual passes through bit for bit
+    and the next input is the adaptive norm of the unchanged residual."""
+    L, M, H, I = 2, 4, 64, 64
+    wgu, sgu, _, _ = _chain_layer_weights(L, H, I, 5)
+    wd = [np.zeros((H, I), np.uint8) for _ in range(L)]
+    sd = [np.ones(H, np.float32) for _ in range(L)]
+    x, h, g, st = synthetic.decoder_chain_inputs(L, M, H, M)
+    xo, ho, go = oracle.decoder_chain(x, h, g, wgu, sgu, wd, sd, st, 1e-6)
+    assert np.array_equal(xo, x)
+    _, h_ref, g_ref = oracle.gate_residual_ada_norm(x, np.zeros_like(x), g, st[-1], 1e-6)
+    assert np.array_equal(ho, h_ref) and np.array_equal(go, g_ref)
