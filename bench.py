@@ -63,6 +63,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 8 times (scale reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--wide-only", action="store_true",
+                    help="only run the M = 768 encoder GEMMs (W8A16 and FP8 x FP8, both shapes, 8 calls "
+                         "each; the workload of the wide-kernel counter runs) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -99,6 +102,25 @@ def main():
         s = torch.empty(N, dtype=torch.float32, device=dev) if wfmt != vla.VLA_WFMT_BF16 else None
         vla.vla_quantize_pack(up_bits(W), q, s, N, K, wfmt, vla.VLA_LAYOUT_MFMA)
         return q, s
+
+    if args.wide_only:
+        Mw = 768
+        for n, k in ((16384, 2048), (2048, 16384)):
+            A = up_bits(synthetic.activations(Mw, k, 910 + n))
+            q, s = quantize(synthetic.weights(n, k, 911 + n))
+            qa = torch.empty(Mw * k, dtype=torch.uint8, device=dev)
+            sa = torch.empty(1, dtype=torch.float32, device=dev)
+            wq = torch.zeros(vla.vla_quantize_act_workspace_bytes(Mw, k), dtype=torch.uint8, device=dev)
+            vla.vla_quantize_act(A, qa, sa, wq, wq.numel(), Mw, k)
+            Y = torch.empty(Mw * n, dtype=torch.int16, device=dev)
+            wsb = vla.vla_gemm_workspace_bytes(Mw, n, k, 1)
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+            for Ap, sap in ((A, None), (qa, sa)):
+                for _ in range(8):
+                    vla.vla_gemm_fp8w(Ap, sap, q, s, None, None, Y, ws, wsb, Mw, n, k)
+                torch.cuda.synchronize()
+        print(json.dumps({"wide_only": "done"}))
+        return
 
     # ---------------------------------------------------------- headline
     log("building skinny workload")
