@@ -214,6 +214,31 @@ def main():
         extra[f"{name}_GBps"] = round(alg_bytes_fp8w(*shp) / (ms * 1e-3 / args.steps) / 1e9, 1)
 
     if not args.no_extra:
+        # MXFP4 weights (E2M1 + an E8M0 scale per 32 values: 0.53 of the FP8
+        # bytes), same shapes, activations and cold rotation over >= 1 GiB
+        def quantize_mx(W):
+            n_, k_ = W.shape
+            q = torch.empty(vla.vla_packed_bytes(n_, k_, vla.VLA_WFMT_MXFP4), dtype=torch.uint8, device=dev)
+            vla.vla_quantize_pack(up_bits(W), q, None, n_, k_, vla.VLA_WFMT_MXFP4, vla.VLA_LAYOUT_MFMA)
+            return q
+        mq_up, mq_dn = quantize_mx(W_up), quantize_mx(W_dn)
+        mcopies = max(1, (1 << 30) // (mq_up.numel() + mq_dn.numel())) if args.cache == "cold" else 1
+        mqs = {"up": [mq_up] + [mq_up.clone() for _ in range(mcopies - 1)],
+               "down": [mq_dn] + [mq_dn.clone() for _ in range(mcopies - 1)]}
+        wsm_bytes = max(vla.vla_gemm_workspace_bytes(*UP, vla.VLA_WFMT_MXFP4),
+                        vla.vla_gemm_workspace_bytes(*DOWN, vla.VLA_WFMT_MXFP4))
+        wsm = torch.zeros(wsm_bytes, dtype=torch.uint8, device=dev)
+        for name, shp, A, Y in (("up", UP, A_up, Y_up), ("down", DOWN, A_dn, Y_dn)):
+            def onem(i, name=name, shp=shp, A=A, Y=Y):
+                vla.vla_gemm_mxfp4w(A, mqs[name][i % mcopies], None, None, Y, wsm, wsm_bytes, *shp)
+            ms = time_graph(onem, args.steps)
+            us = ms * 1000.0 / args.steps
+            n_, k_ = shp[1], shp[2]
+            mx_bytes = n_ * k_ // 2 + n_ * k_ // 32 + 2 * shp[0] * k_ + 2 * shp[0] * n_
+            extra[f"mxfp4_{name}_us"] = round(us, 3)
+            extra[f"mxfp4_{name}_GBps"] = round(mx_bytes / (us * 1e-6) / 1e9, 1)
+        del mqs
+
         # the pages' own decoder row count (10 rows), same weights and rotation
         A10_up = up_bits(synthetic.activations(10, H, synthetic.IDS["skinny.up.A"]))
         A10_dn = up_bits(synthetic.activations(10, I, synthetic.IDS["skinny.down.A"]))

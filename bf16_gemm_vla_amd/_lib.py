@@ -27,6 +27,7 @@ VLA_ESTATE = 6
 VLA_WFMT_BF16 = 0
 VLA_WFMT_E4M3_OCP = 1
 VLA_WFMT_E4M3_FNUZ = 2
+VLA_WFMT_MXFP4 = 3
 VLA_LAYOUT_ROWMAJOR = 0
 VLA_LAYOUT_MFMA = 1
 
@@ -52,6 +53,7 @@ SIGNATURES = {
     "vla_gemm_supported": (INT, [I64, I64, I64, INT, INT, INT]),
     "vla_gemm_fp8w": (INT, [P, P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_gemm_bf16": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
+    "vla_gemm_mxfp4w": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_gemm_fp8w_gelu_mul": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_mlp_chain_scratch_bytes": (SZ, [I64, I64, I64]),
     "vla_mlp_chain_enqueue": (INT, [P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P]),
@@ -194,6 +196,11 @@ def vla_gemm_fp8w(A, s_a, Wq, s_w, bias, residual, Y, ws, ws_bytes, M, N, K, str
 def vla_gemm_bf16(A, Wq, bias, residual, Y, ws, ws_bytes, M, N, K, stream=None):
     _check(load().vla_gemm_bf16(_ptr(A), _ptr(Wq), _ptr(bias), _ptr(residual), _ptr(Y),
                                 _ptr(ws), ws_bytes, M, N, K, _stream(stream)), "vla_gemm_bf16")
+
+
+def vla_gemm_mxfp4w(A, Wq, bias, residual, Y, ws, ws_bytes, M, N, K, stream=None):
+    _check(load().vla_gemm_mxfp4w(_ptr(A), _ptr(Wq), _ptr(bias), _ptr(residual), _ptr(Y), _ptr(ws), ws_bytes,
+                                  M, N, K, _stream(stream)), "vla_gemm_mxfp4w")
 
 
 def vla_gemm_fp8w_gelu_mul(A, Wgu, s_gu, act, gu, ws, ws_bytes, M, I, K, stream=None):

@@ -328,17 +328,25 @@ const char* vla_last_error(void) { return g_err; }
 
 size_t vla_packed_bytes(int64_t N, int64_t K, int wfmt) {
     if (N <= 0 || K <= 0) return 0;
+    if (wfmt == VLA_WFMT_MXFP4)
+        return static_cast<size_t>(N) * K / 2 + static_cast<size_t>(N) * vla::mxfp4_scale_row_bytes(K);
     return static_cast<size_t>(N) * static_cast<size_t>(K) * (wfmt == VLA_WFMT_BF16 ? 2 : 1);
 }
 
 int vla_quantize_pack(const float* W, void* Wq, float* scales, int64_t N, int64_t K, int wfmt,
                       int layout, void* stream) {
     const char* fn = "vla_quantize_pack";
-    if (wfmt < VLA_WFMT_BF16 || wfmt > VLA_WFMT_E4M3_FNUZ) return fail(VLA_EINVAL, fn, "unknown wfmt %d", wfmt);
+    if (wfmt < VLA_WFMT_BF16 || wfmt > VLA_WFMT_MXFP4) return fail(VLA_EINVAL, fn, "unknown wfmt %d", wfmt);
     if (layout != VLA_LAYOUT_ROWMAJOR && layout != VLA_LAYOUT_MFMA) return fail(VLA_EINVAL, fn, "unknown layout %d", layout);
     if (int rc = check_nk(fn, N, K)) return rc;
     REQUIRE_PTR(W);
     REQUIRE_PTR(Wq);
+    if (wfmt == VLA_WFMT_MXFP4) {
+        if (scales != nullptr) return fail(VLA_EINVAL, fn, "scales must be NULL for MXFP4 (they are packed into Wq)");
+        if (layout != VLA_LAYOUT_MFMA) return fail(VLA_EINVAL, fn, "MXFP4 is packed in VLA_LAYOUT_MFMA only");
+        hipError_t e = vla::launch_mxfp4_quantize_pack(W, static_cast<uint8_t*>(Wq), N, K, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
+    }
     if (wfmt == VLA_WFMT_BF16) {
         if (scales != nullptr) return fail(VLA_EINVAL, fn, "scales must be NULL for BF16");
     } else {
@@ -458,6 +466,8 @@ int vla_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int blo
 
 size_t vla_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int wfmt) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
+    if (wfmt == VLA_WFMT_MXFP4)
+        return vla::gemm_ws_bytes(vla::plan_gemm(M, N, K, vla::AType::BF16, vla::WType::FP4, vla::Epi::PLAIN), M, N);
     const vla::WType wt = (wfmt == VLA_WFMT_BF16) ? vla::WType::BF16 : vla::WType::FP8;
     size_t best = 0;
     const vla::AType ats[2] = {vla::AType::BF16, vla::AType::FP8};
@@ -473,11 +483,14 @@ size_t vla_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int wfmt) {
 int vla_gemm_supported(int64_t M, int64_t N, int64_t K, int wfmt, int fp8_act, int gelu_mul) {
     const char* fn = "vla_gemm_supported";
     if (int rc = check_mnk(fn, M, N, K)) return rc;
-    if (wfmt != VLA_WFMT_BF16 && wfmt != VLA_WFMT_E4M3_OCP) return fail(VLA_EINVAL, fn, "wfmt=%d", wfmt);
+    if (wfmt != VLA_WFMT_BF16 && wfmt != VLA_WFMT_E4M3_OCP && wfmt != VLA_WFMT_MXFP4)
+        return fail(VLA_EINVAL, fn, "wfmt=%d", wfmt);
     const vla::AType at = fp8_act ? vla::AType::FP8 : vla::AType::BF16;
-    const vla::WType wt = (wfmt == VLA_WFMT_BF16) ? vla::WType::BF16 : vla::WType::FP8;
+    const vla::WType wt = (wfmt == VLA_WFMT_BF16) ? vla::WType::BF16
+                          : (wfmt == VLA_WFMT_MXFP4 ? vla::WType::FP4 : vla::WType::FP8);
     const vla::Epi epi = gelu_mul ? vla::Epi::GELU_MUL : vla::Epi::PLAIN;
     if ((gelu_mul || fp8_act) && wt != vla::WType::FP8) return fail(VLA_EINVAL, fn, "fp8_act and gelu_mul need FP8 weights");
+    if (wt == vla::WType::FP4 && M > 64) return fail(VLA_ESHAPE, fn, "MXFP4 weights: M <= 64 only");
     if (gelu_mul && fp8_act) return fail(VLA_EINVAL, fn, "gelu_mul takes bf16 activations");
     if (gelu_mul && (N % 32) != 0) return fail(VLA_ESHAPE, fn, "gelu_mul needs N = 2I with I a multiple of 16");
     const vla::GemmPlan p = vla::plan_gemm(M, N, K, at, wt, epi);
@@ -525,6 +538,26 @@ int vla_gemm_bf16(const uint16_t* A, const uint16_t* Wq, const uint16_t* bias,
     p.M = M; p.N = N; p.K = K;
     p.atype = vla::AType::BF16;
     p.wtype = vla::WType::BF16;
+    p.epi = vla::Epi::PLAIN;
+    return run_gemm(fn, p, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int vla_gemm_mxfp4w(const uint16_t* A, const uint8_t* Wq, const uint16_t* bias, const uint16_t* residual,
+                    uint16_t* Y, void* ws, size_t ws_bytes, int64_t M, int64_t N, int64_t K, void* stream) {
+    const char* fn = "vla_gemm_mxfp4w";
+    if (int rc = check_mnk(fn, M, N, K)) return rc;
+    if (M > 64) return fail(VLA_ESHAPE, fn, "M=%lld: MXFP4 weights run in the skinny kernel only (M <= 64)", (long long)M);
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(Wq);
+    OPTIONAL_PTR(bias);
+    OPTIONAL_PTR(residual);
+    REQUIRE_PTR(Y);
+    REQUIRE_PTR(ws);
+    vla::GemmProblem p{};
+    p.A = A; p.W = Wq; p.bias = bias; p.resid = residual; p.Y = Y; p.ws = ws;
+    p.M = M; p.N = N; p.K = K;
+    p.atype = vla::AType::BF16;
+    p.wtype = vla::WType::FP4;
     p.epi = vla::Epi::PLAIN;
     return run_gemm(fn, p, ws_bytes, static_cast<hipStream_t>(stream));
 }

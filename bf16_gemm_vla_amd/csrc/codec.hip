@@ -88,6 +88,72 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(const float* __
     }
 }
 
+// MXFP4 (OCP Microscaling Formats v1.0): nearest E2M1 code of |v|, ties to
+// the even code (mantissa bit 0), |v| >= 6 saturating; the sign bit is
+// taken from v (so -0 stays 0x8).  Magnitudes: 0, .5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ uint32_t encode_e2m1(float v) {
+    const float a = fabsf(v);
+    uint32_t c;
+    if (a <= 0.25f) c = 0;
+    else if (a < 0.75f) c = 1;
+    else if (a <= 1.25f) c = 2;
+    else if (a < 1.75f) c = 3;
+    else if (a <= 2.5f) c = 4;
+    else if (a < 3.5f) c = 5;
+    else if (a <= 5.0f) c = 6;
+    else c = 7;
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// MXFP4 quantize + pack, one workgroup per 16-row tile, one thread per
+// 32-value block (one output channel x one 32-wide K step, which is exactly
+// one packed MFMA fragment row).  Shared exponent floor(log2 max|w|) - 2,
+// clamped to E8M0's range (an all-zero block takes 0); codes of w * 2^-e
+// (exact: a power-of-two scale).  Codes go two per byte (even position in
+// the low nibble) in the FP8 fragment order; the E8M0 scale bytes follow all
+// codes, row-major with rows padded to P = K/32 rounded up to 8 bytes (pad
+// bytes 127): byte N*K/2 + n * P + k0, so a wave's consecutive K steps of one
+// row are one aligned load.
+__global__ __launch_bounds__(kThreads) void mxfp4_quantize_pack_kernel(const float* __restrict__ W,
+                                                                       uint8_t* __restrict__ Wq, int64_t N,
+                                                                       int64_t K) {
+    const int64_t n0 = blockIdx.x;
+    const int64_t ksteps = K >> 5;
+    const int64_t P = mxfp4_scale_row_bytes(K);
+    uint8_t* const sc_base = Wq + N * K / 2;
+    for (int64_t b = threadIdx.x; b < P * 16; b += kThreads) {
+        const int64_t k0 = b >> 4;
+        const int n1 = static_cast<int>(b & 15);
+        if (k0 >= ksteps) {   // row padding
+            sc_base[(n0 * 16 + n1) * P + k0] = 127;
+            continue;
+        }
+        const float* src = W + (n0 * 16 + n1) * K + k0 * 32;
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 f = *reinterpret_cast<const float4*>(src + 4 * i);
+            v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+        // floor(log2 m) from the exponent field; a subnormal m clamps to -127
+        const int ebits = static_cast<int>((__float_as_uint(m) >> 23) & 0xFFu);
+        const int se = (m == 0.0f) ? 0 : (ebits == 0 ? -127 : max(-127, ebits - 127 - 2));
+        const float inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);   // 2^-se, a normal float
+#pragma unroll
+        for (int k1 = 0; k1 < 4; ++k1) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w |= encode_e2m1(v[8 * k1 + i] * inv) << (4 * i);
+            const int64_t slot = (n0 * ksteps + k0) * 64 + 16 * k1 + n1;
+            *reinterpret_cast<uint32_t*>(Wq + slot * 4) = w;
+        }
+        sc_base[(n0 * 16 + n1) * P + k0] = static_cast<uint8_t>(127 + se);
+    }
+}
+
 // Row-major FP8 -> MFMA layout: one thread per 8-byte slot.
 __global__ __launch_bounds__(kThreads) void pack_fp8_kernel(const uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ qp, int64_t N,
@@ -300,6 +366,11 @@ hipError_t launch_quantize_pack(const float* W, void* Wq, float* scales, int64_t
             quantize_pack_kernel<VLA_WFMT_E4M3_FNUZ><<<grid, kThreads, 0, s>>>(W, Wq, scales, K, layout);
             break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_quantize_pack(const float* W, uint8_t* Wq, int64_t N, int64_t K, hipStream_t s) {
+    mxfp4_quantize_pack_kernel<<<static_cast<unsigned>(N / 16), kThreads, 0, s>>>(W, Wq, N, K);
     return hipGetLastError();
 }
 

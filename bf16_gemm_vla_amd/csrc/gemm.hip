@@ -34,6 +34,8 @@ template <>
 struct WFragT<WType::FP8> { using type = u32x2_t; };
 template <>
 struct WFragT<WType::BF16> { using type = u32x4_t; };
+template <>
+struct WFragT<WType::FP4> { using type = uint32_t; };
 
 template <AType AT>
 struct AFragT;
@@ -82,7 +84,7 @@ template <AType AT, WType WT, Epi EPI, int NT, int S, int WAVES, bool ALDS, int 
 __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
     using WF = typename WFragT<WT>::type;
     using AF = typename AFragT<AT>::type;
-    constexpr int WB = (WT == WType::FP8) ? 8 : 16;   // weight bytes per lane per fragment
+    constexpr int WB = (WT == WType::FP8) ? 8 : (WT == WType::FP4 ? 4 : 16);   // weight bytes per lane per fragment
     constexpr int AB = (AT == AType::FP8) ? 1 : 2;    // activation bytes per element
     constexpr int JO = (EPI == Epi::PLAIN) ? NT : NT / 2;   // output tiles per group
     constexpr int PAIRS = JO * MT;                           // (output tile, m-tile) fragments
@@ -154,8 +156,39 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
             }
         }
     }
-    // 3. all weight fragments of this wave in flight
+    // 3. all weight fragments of this wave in flight.  MXFP4: first the E8M0
+    //    scales of the lane's row for the wave's S K steps, one aligned load
+    //    per tile (rows of P bytes after the N*K/2 code bytes; kbase is a
+    //    multiple of S, which divides 8, so the load stays inside the row)
     WF wf[S][NT];
+    float wsc[S][NT];
+    if constexpr (WT == WType::FP4) {
+        static_assert(S == 1 || S == 2 || S == 4 || S == 8, "scale loads of 1, 2, 4 or 8 bytes");
+        const int64_t P = mxfp4_scale_row_bytes(a.K);
+        const uint8_t* const wscale = static_cast<const uint8_t*>(a.W) + static_cast<int64_t>(a.N) * a.K / 2;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int tile = skinny_tile<EPI, NT>(g, j, a.N);
+            const bool valid = tile < ntiles && kbase < ksteps;
+            const uint8_t* p = wscale + (valid ? (static_cast<int64_t>(tile) * 16 + (lane & 15)) * P + kbase : 0);
+            uint32_t b[2] = {0, 0};
+            if constexpr (S == 8) {
+                const uint2 v = *reinterpret_cast<const uint2*>(p);
+                b[0] = v.x; b[1] = v.y;
+            } else if constexpr (S == 4) {
+                b[0] = *reinterpret_cast<const uint32_t*>(p);
+            } else if constexpr (S == 2) {
+                b[0] = *reinterpret_cast<const uint16_t*>(p);
+            } else {
+                b[0] = *p;
+            }
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const uint32_t e = (b[s >> 2] >> (8 * (s & 3))) & 0xFFu;
+                wsc[s][j] = (valid && kbase + s < ksteps) ? e8m0_to_f32(e) : 0.0f;
+            }
+        }
+    }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const bool ok = kbase + s < ksteps;
@@ -170,9 +203,11 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
     }
     if constexpr (ALDS) {
         // the activations (and epilogue inputs) have landed once at most the
-        // S*NT weight loads are outstanding; then read the LDS fragments
-        constexpr int NW = S * NT;
-        static_assert(NW <= 63, "the weight loads fit the vmcnt field");
+        // S*NT weight loads (and the NT scale loads) are outstanding; then
+        // read the LDS fragments.  Capped at the field's 63: a lower count
+        // only waits for a few more loads.
+        constexpr int NW0 = S * NT + (WT == WType::FP4 ? NT : 0);
+        constexpr int NW = NW0 < 63 ? NW0 : 63;
         __builtin_amdgcn_s_waitcnt((NW & 15) | ((NW >> 4) << 14) | 0x0F70);
         // a bare barrier: __syncthreads() would add a release fence that
         // waits for the weight loads too
@@ -205,7 +240,10 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
             const bf16x8_t bop = a_operand<AT>(af[s][mt]);
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w_operand<WT>(wf[s][j]), bop, acc[j][mt], 0, 0, 0);
+                if constexpr (WT == WType::FP4)
+                    acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4_to_bf16x8(wf[s][j], wsc[s][j]), bop, acc[j][mt], 0, 0, 0);
+                else
+                    acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w_operand<WT>(wf[s][j]), bop, acc[j][mt], 0, 0, 0);
         }
     }
     if constexpr (ALDS) __syncthreads();   // activation reads done before LDS is reused
@@ -315,7 +353,8 @@ hipError_t launch_skinny(const KArgs& ka, const GemmPlan& p, hipStream_t s) {
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_typed(const KArgs& ka, const GemmPlan& p, hipStream_t s) {
     if (p.kernel == 0) return launch_skinny<AT, WT, EPI>(ka, p, s);
-    return launch_wide<AT, WT, EPI>(ka, p, s);
+    if constexpr (WT == WType::FP4) return hipErrorInvalidValue;   // no wide MXFP4 kernel
+    else return launch_wide<AT, WT, EPI>(ka, p, s);
 }
 
 // Skinny plan for a given tiling: groups of `nt` tiles, activation row
@@ -358,11 +397,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
         const int64_t groups = std::max<int64_t>(1, (epi == Epi::GELU_MUL) ? tiles / 2 : tiles);
         const int64_t mt_total = (M + 15) / 16;
         const int64_t want = groups >= 256 ? 1 : (256 + groups - 1) / groups;   // splits wanted
+        // MXFP4 weights take the FP8 tilings (fewer weight bytes per fragment)
         // one 16-row tile and too few column groups, FP8 weights: no K split
         // up to 128 MFMA steps (K = 4096) — one 16-wave workgroup per tile
         // beats the cross-workgroup exchange (the 10-row 4096 -> 1024
         // down-projection: 6.30 -> 5.31 us against four K splits)
-        if (want > 1 && mt_total == 1 && wt == WType::FP8 && epi == Epi::PLAIN && ksteps > 16 && ksteps <= 128)
+        if (want > 1 && mt_total == 1 && wt != WType::BF16 && epi == Epi::PLAIN && ksteps > 16 && ksteps <= 128)
             return skinny_plan(M, N, K, epi, nt, ksteps <= 64 ? 4 : 8, 16, 1, at == AType::BF16);
         if (want > 1 && mt_total > 1) {
             const int64_t ksplit = (want + mt_total - 1) / mt_total;
@@ -386,9 +426,15 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
         // FP8 weights, plain epilogue, more than 32 rows: two 16-column tiles
         // x two row halves per workgroup read 36% fewer bytes per CU than one
         // tile x all rows (the 1024 -> 4096 up-projection: 5.4 -> 5.1 us)
-        if (wt == WType::FP8 && epi == Epi::PLAIN && mt_total > 2 && steps == 4)
+        if (wt != WType::BF16 && epi == Epi::PLAIN && mt_total > 2 && steps == 4)
             return skinny_plan(M, N, K, epi, 2 * nt, steps, waves, 2, at == AType::BF16);
         return skinny_plan(M, N, K, epi, nt, steps, waves, 4, at == AType::BF16);
+    }
+    if (wt == WType::FP4) {   // MXFP4 weights: the skinny kernel only
+        GemmPlan p{};
+        p.kernel = 1;
+        p.ok = false;
+        return p;
     }
     // Wide kernel: 192-row blocks; 256-column tiles when they give enough
     // workgroups, else 128-column tiles and K split until ~256 workgroups
@@ -460,6 +506,7 @@ hipError_t launch_gemm_plan(const GemmProblem& pr, const GemmPlan& p, hipStream_
 
     if (pr.epi == Epi::GELU_MUL) return launch_typed<AType::BF16, WType::FP8, Epi::GELU_MUL>(ka, p, s);
     if (pr.wtype == WType::BF16) return launch_typed<AType::BF16, WType::BF16, Epi::PLAIN>(ka, p, s);
+    if (pr.wtype == WType::FP4) return launch_typed<AType::BF16, WType::FP4, Epi::PLAIN>(ka, p, s);
     if (pr.atype == AType::FP8) return launch_typed<AType::FP8, WType::FP8, Epi::PLAIN>(ka, p, s);
     return launch_typed<AType::BF16, WType::FP8, Epi::PLAIN>(ka, p, s);
 }

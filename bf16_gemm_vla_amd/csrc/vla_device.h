@@ -106,6 +106,25 @@ __device__ __forceinline__ bf16x8_t ocp8_to_bf16x8(u32x2_t w) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// E8M0 block scale -> fp32 2^(e - 127) (e = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+// Eight E2M1 codes (one dword, element i in bits 4i..4i+3) times a block
+// scale -> eight bf16 as an MFMA operand.  Exact: an E2M1 value times a
+// power of two in bf16's range is a bf16 value; gfx950 converts a byte (two
+// codes, low nibble first) to a pair of scaled bf16 in one instruction.
+__device__ __forceinline__ bf16x8_t fp4_to_bf16x8(uint32_t w, float scale) {
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    const u32x4_t v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                       __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // --------------------------------------------------------- wave reductions

@@ -14,6 +14,9 @@ namespace vla {
 // ---------------------------------------------------------------- codec
 hipError_t launch_quantize_pack(const float* W, void* Wq, float* scales, int64_t N, int64_t K,
                                 int wfmt, int layout, hipStream_t s);
+// MXFP4 block-scale bytes per weight row: K/32 rounded up to 8.
+constexpr int64_t mxfp4_scale_row_bytes(int64_t K) { return ((K >> 5) + 7) & ~int64_t(7); }
+hipError_t launch_mxfp4_quantize_pack(const float* W, uint8_t* Wq, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_pack_fp8(const uint8_t* q, uint8_t* qp, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_reencode(const uint8_t* q, const float* sc, uint8_t* q2, float* sc2, int64_t N,
                            int64_t K, int layout, hipStream_t s);
@@ -30,7 +33,7 @@ hipError_t launch_quantize_act_static(const uint16_t* A, const float* s_a, uint8
 
 // ----------------------------------------------------------------- GEMM
 enum class AType { BF16 = 0, FP8 = 1 };
-enum class WType { BF16 = 0, FP8 = 1 };
+enum class WType { BF16 = 0, FP8 = 1, FP4 = 2 };   // FP4: MXFP4 (E2M1 + E8M0 per 32 K)
 enum class Epi { PLAIN = 0, GELU_MUL = 1 };
 
 struct GemmProblem {

@@ -51,6 +51,7 @@ extern "C" {
 #define VLA_WFMT_BF16 0
 #define VLA_WFMT_E4M3_OCP 1   /* OCP E4M3: bias 7, max 448, NaN S.1111.111, no inf */
 #define VLA_WFMT_E4M3_FNUZ 2  /* E4M3 FNUZ: bias 8, max 240, NaN 0x80 only, no -0, no inf */
+#define VLA_WFMT_MXFP4 3      /* OCP MX FP4: E2M1 codes + one E8M0 scale per 32 values of K */
 
 /* Weight layouts. */
 #define VLA_LAYOUT_ROWMAJOR 0
@@ -70,7 +71,8 @@ const char *vla_last_error(void);
 
 /* --------------------------------------------------------- weight codecs */
 
-/* Bytes of an N x K weight in format `wfmt` (either layout). */
+/* Bytes of an N x K weight in format `wfmt` (either layout; MXFP4: codes
+ * and block scales, N*K/2 + N*P with P = K/32 rounded up to 8). */
 size_t vla_packed_bytes(int64_t N, int64_t K, int wfmt);
 
 /* Quantize (FP8) or round (BF16) an fp32 weight and lay it out.
@@ -83,6 +85,16 @@ size_t vla_packed_bytes(int64_t N, int64_t K, int wfmt);
  * FP8: scales[n] = fp32(max_k |W[n,k]| / 448) (OCP) or / 240 (FNUZ), 1 for an
  * all-zero row; code = encode(fp32(W[n,k] / scales[n])), IEEE division,
  * round to nearest even, saturating at +-max.  BF16: round to nearest even.
+ * MXFP4 (OCP Microscaling Formats v1.0; 4-bit weights as in "FlashRT: an
+ * inference engine for real-time robot control", section 7.2, here in the
+ * MX form gfx950 converts in hardware): per block of 32 values of K in one
+ * row, shared exponent e = floor(log2 max|w|) - 2 clamped to [-127, 127]
+ * (0 for an all-zero block), code = nearest E2M1 of w * 2^-e (ties to the
+ * even code, saturating at +-6); only VLA_LAYOUT_MFMA, scales must be NULL:
+ * Wq holds the codes in the FP8 fragment order, two per byte (even position
+ * in the low nibble), N*K/2 bytes, then the E8M0 bytes (127 + e) row-major,
+ * each row padded to P = K/32 rounded up to 8 bytes (pad bytes 127): byte
+ * N*K/2 + n * P + k/32.
  * W must be finite.  Errors: EINVAL, ESHAPE, EALIGN, EHIP. */
 int vla_quantize_pack(const float *W, void *Wq, float *scales, int64_t N, int64_t K, int wfmt,
                       int layout, void *stream);
@@ -230,6 +242,18 @@ int vla_gemm_bf16(const uint16_t *A, const uint16_t *Wq, const uint16_t *bias,
  *   act   device bf16 M x I output.
  *   gu    device bf16 M x 2I output of [g, u], or NULL.
  * I must be a multiple of 16.  Workspace: vla_gemm_workspace_bytes(M, 2I, K, OCP). */
+/* As vla_gemm_fp8w with MXFP4 weights (bf16 activations, no per-channel
+ * scale: each 32-value block of a weight row carries its E8M0 scale):
+ *   Y = bf16(A @ (dec(q) * 2^(e - 127))^T + bias) (+ residual, as above)
+ * 4-bit weights ("FlashRT: an inference engine for real-time robot
+ * control", section 7.2) in the OCP MX form; the kernel converts each code
+ * to bf16 with its block scale in one gfx950 instruction per pair, exactly,
+ * and streams half the bytes of FP8.  The skinny kernel only: M <= 64, else
+ * VLA_ESHAPE.  Wq from vla_quantize_pack(..., VLA_WFMT_MXFP4, VLA_LAYOUT_MFMA);
+ * workspace vla_gemm_workspace_bytes(M, N, K, VLA_WFMT_MXFP4). */
+int vla_gemm_mxfp4w(const uint16_t *A, const uint8_t *Wq, const uint16_t *bias, const uint16_t *residual,
+                    uint16_t *Y, void *ws, size_t ws_bytes, int64_t M, int64_t N, int64_t K, void *stream);
+
 int vla_gemm_fp8w_gelu_mul(const uint16_t *A, const uint8_t *Wgu, const float *s_gu,
                            uint16_t *act, uint16_t *gu, void *ws, size_t ws_bytes, int64_t M,
                            int64_t I, int64_t K, void *stream);

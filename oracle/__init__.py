@@ -77,6 +77,10 @@ def _load():
                 "orc_gelu_mul": (None, [P, P, I64, P]),
                 "orc_mlp_chain": (None, [P, P, P, P, P, INT, I64, I64, I64, P, P, P, P]),
                 "orc_gate_residual_ada_norm": (None, [P, P, P, P, INT, ctypes.c_float, I64, I64, P, P, P]),
+                "orc_fp4_decode": (ctypes.c_double, [ctypes.c_uint8]),
+                "orc_fp4_encode": (ctypes.c_uint8, [ctypes.c_double]),
+                "orc_mxfp4_quantize_rows": (None, [P, I64, I64, P, P]),
+                "orc_mxfp4_dequant_rows": (None, [P, P, I64, I64, P]),
                 "orc_decoder_chain": (None, [P, P, P, P, P, P, P, P, I64, INT, ctypes.c_float, INT, I64, I64, I64,
                                              P, P, P]),
             }
@@ -302,3 +306,36 @@ def decoder_chain(x_in, h_in, g_in, wgu, sgu, wd, sd, styles, eps: float, style_
                               arr(keep_s[L:]), _p(st), rows * 3 * H, int(bool(style_per_row)),
                               ctypes.c_float(float(np.float32(eps))), L, M, H, I, _p(xo), _p(ho), _p(go))
     return xo, ho, go
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def fp4_decode_table() -> np.ndarray:
+    """Values of the 16 E2M1 codes."""
+    lib = _load()
+    return np.array([lib.orc_fp4_decode(c) for c in range(16)], np.float64)
+
+
+def fp4_encode(x) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(x, np.float64)
+    return np.array([lib.orc_fp4_encode(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def mxfp4_quantize_rows(W):
+    """fp32 W (N x K) -> (codes N x K uint8 in the low nibble, E8M0 scales N x K/32)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, K // 32), np.uint8)
+    _load().orc_mxfp4_quantize_rows(_p(W), N, K, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mxfp4_dequant_rows(codes, scales) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    N, K = codes.shape
+    out = np.empty((N, K), np.float64)
+    _load().orc_mxfp4_dequant_rows(_p(codes), _p(scales), N, K, _p(out))
+    return out

@@ -480,3 +480,76 @@ void orc_decoder_chain(const uint16_t *x_in, const uint16_t *h_in, const uint16_
     free(hv); free(wg); free(wdn); free(gu); free(act); free(dn); free(gb); free(ab); free(db);
     free(x); free(h); free(g); free(x2); free(h2); free(g2);
 }
+
+/* ------------------------------------------------------------ MXFP4 */
+
+/* MXFP4 (OCP Microscaling Formats v1.0): E2M1 elements (sign, 2 exponent
+ * bits with bias 1, 1 mantissa bit; no inf or NaN; magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6) sharing one E8M0 scale 2^(e - 127) per block of 32
+ * consecutive values.  Used here for 4-bit weights, one block = 32 values of
+ * K in one output channel (the pages' 4-bit encoder weights, [FR] section
+ * 7.2, are NVFP4; gfx950 converts MX formats in hardware). */
+double orc_fp4_decode(uint8_t c)
+{
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* Nearest E2M1 code of x (finite), ties to the even code (mantissa bit 0),
+ * |x| >= 6 saturating to +-6; the sign of zero is kept. */
+uint8_t orc_fp4_encode(double x)
+{
+    uint8_t sign = signbit(x) ? 8 : 0;
+    double a = fabs(x);
+    if (a >= 6.0) return sign | 7;   /* saturate (no inf in E2M1) */
+    uint8_t best = 0;
+    double best_err = a;
+    for (uint8_t c = 1; c < 8; ++c) {
+        double err = fabs(orc_fp4_decode(c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return sign | best;
+}
+
+/* Per-block quantization of fp32 W (N x K, K a multiple of 32): for each
+ * block of 32 values of one row, the shared exponent is
+ * floor(log2(max |w|)) - 2 (2 = the largest exponent of E2M1), clamped to
+ * E8M0's range [-127, 127]; an all-zero block takes exponent 0.  Codes are
+ * enc(fp32(w / 2^shared)).  codes: N x K (one code per byte, low nibble),
+ * scales: N x K/32 E8M0 bytes (127 + shared). */
+void orc_mxfp4_quantize_rows(const float *W, int64_t N, int64_t K, uint8_t *codes, uint8_t *scales)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const float *w = W + n * K + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                if (fabsf(w[i]) > amax) amax = fabsf(w[i]);
+            int se = 0;
+            if (amax > 0.0f) {
+                int e2;
+                (void)frexp((double)amax, &e2);   /* amax = f * 2^e2, f in [0.5, 1) */
+                se = (e2 - 1) - 2;
+                if (se < -127) se = -127;
+                if (se > 127) se = 127;
+            }
+            scales[n * (K / 32) + b] = (uint8_t)(127 + se);
+            for (int i = 0; i < 32; ++i) {
+                float v = (float)ldexp((double)w[i], -se);   /* exact: a power-of-two scale */
+                codes[n * K + b * 32 + i] = orc_fp4_encode((double)v);
+            }
+        }
+    }
+}
+
+/* Dequantize MXFP4 codes + E8M0 scales to fp64 (exact). */
+void orc_mxfp4_dequant_rows(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K, double *out)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = ldexp(orc_fp4_decode(codes[n * K + k]), (int)scales[n * (K / 32) + k / 32] - 127);
+}
