@@ -237,7 +237,6 @@ def main():
             mx_bytes = n_ * k_ // 2 + n_ * k_ // 32 + 2 * shp[0] * k_ + 2 * shp[0] * n_
             extra[f"mxfp4_{name}_us"] = round(us, 3)
             extra[f"mxfp4_{name}_GBps"] = round(mx_bytes / (us * 1e-6) / 1e9, 1)
-        del mqs
 
         # the pages' own decoder row count (10 rows), same weights and rotation
         A10_up = up_bits(synthetic.activations(10, H, synthetic.IDS["skinny.up.A"]))
@@ -249,6 +248,14 @@ def main():
                 vla.vla_gemm_fp8w(A, None, qs[i % copies], s, None, None, Y_up, ws10, ws10_bytes, *shp)
             ms = time_graph(one10, args.steps)
             extra[f"m10_{name}_us"] = round(ms * 1000.0 / args.steps, 3)
+            wsm10_bytes = vla.vla_gemm_workspace_bytes(*shp, vla.VLA_WFMT_MXFP4)
+            wsm10 = torch.zeros(wsm10_bytes, dtype=torch.uint8, device=dev)
+
+            def one10m(i, name=name, shp=shp, A=A, wsm10=wsm10, wsm10_bytes=wsm10_bytes):
+                vla.vla_gemm_mxfp4w(A, mqs[name][i % mcopies], None, None, Y_up, wsm10, wsm10_bytes, *shp)
+            ms = time_graph(one10m, args.steps)
+            extra[f"m10_mxfp4_{name}_us"] = round(ms * 1000.0 / args.steps, 3)
+        del mqs
 
     if not args.no_extra:
         extra.update(secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, args))
