@@ -255,3 +255,38 @@ def test_page_encoder_rows(N, K, fp8_act):
     ref, yabs = oracle.gemm(a_val[rows], w.w)
     assert_gemm_close(y[rows], ref, yabs)
     assert np.isfinite(bf16_f64(y)).all()
+
+
+def test_concurrent_streams_with_separate_workspaces():
+    """Split-K GEMMs of different shapes on two streams at once, each with its
+    own workspace, give the same bits as the same calls run one after the
+    other (the arrival counters live in each call's workspace)."""
+    shapes = [(10, 1024, 4096), (768, 2048, 16384)]
+    data = []
+    for i, (M, N, K) in enumerate(shapes):
+        A = dev(synthetic.activations(M, K, 9900 + i))
+        w = Weights(synthetic.weights(N, K, 9910 + i), vla.VLA_WFMT_E4M3_OCP)
+        ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, N, K, w.wfmt))
+        data.append((A, w, ws, M, N, K))
+
+    def call(d, Y, stream=None):
+        A, w, ws, M, N, K = d
+        vla.vla_gemm_fp8w(A, None, w.q, w.s, None, None, Y, ws, ws.numel(), M, N, K, stream=stream)
+    seq = []
+    for d in data:
+        Y = torch.empty(d[3] * d[4], dtype=torch.int16, device="cuda")
+        call(d, Y)
+        seq.append(Y)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty(d[3] * d[4], dtype=torch.int16, device="cuda") for _ in range(4)] for d in data]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for r in range(4):
+        for i, d in enumerate(data):
+            call(d, outs[i][r], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in range(len(data)):
+        for r in range(4):
+            assert torch.equal(outs[i][r], seq[i])
+        assert int(host(data[i][2][:61440]).view(np.uint32).sum()) == 0
