@@ -290,3 +290,47 @@ def test_concurrent_streams_with_separate_workspaces():
         for r in range(4):
             assert torch.equal(outs[i][r], seq[i])
         assert int(host(data[i][2][:61440]).view(np.uint32).sum()) == 0
+
+
+def test_graph_replays_equal_eager():
+    """Split-K skinny and wide GEMMs (and the fused gate/up GEMM) captured in
+    one HIP graph: every replay, with other eager work and synchronizations
+    between replays, equals the eager results bit for bit."""
+    calls = []
+    for i, (M, N, K) in enumerate([(10, 1024, 4096), (50, 1024, 4096), (768, 2048, 16384), (300, 256, 4096)]):
+        A = dev(synthetic.activations(M, K, 9950 + i))
+        w = Weights(synthetic.weights(N, K, 9960 + i), vla.VLA_WFMT_E4M3_OCP)
+        ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, N, K, w.wfmt))
+        Y = torch.empty(M * N, dtype=torch.int16, device="cuda")
+        calls.append(lambda A=A, w=w, ws=ws, Y=Y, M=M, N=N, K=K: vla.vla_gemm_fp8w(
+            A, None, w.q, w.s, None, None, Y, ws, ws.numel(), M, N, K))
+        calls[-1].Y = Y
+    M, I, K = 50, 4096, 1024
+    Ag = dev(synthetic.activations(M, K, 9970))
+    wg = Weights(synthetic.weights(2 * I, K, 9971), vla.VLA_WFMT_E4M3_OCP)
+    wsg = zeros_ws(vla.vla_gemm_workspace_bytes(M, 2 * I, K, 1))
+    act = torch.empty(M * I, dtype=torch.int16, device="cuda")
+    calls.append(lambda: vla.vla_gemm_fp8w_gelu_mul(Ag, wg.q, wg.s, act, None, wsg, wsg.numel(), M, I, K))
+    calls[-1].Y = act
+
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    eager = [c.Y.clone() for c in calls]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        for c in calls:
+            c()
+    for r in range(3):
+        for c in calls:
+            c.Y.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for c, e in zip(calls, eager):
+            assert torch.equal(c.Y, e), f"replay {r} differs"
+        del junk
