@@ -212,6 +212,9 @@ def main():
         ms = time_graph(one, args.steps)
         extra[f"{name}_us"] = round(ms * 1000.0 / args.steps, 3)
         extra[f"{name}_GBps"] = round(alg_bytes_fp8w(*shp) / (ms * 1e-3 / args.steps) / 1e9, 1)
+    # a call's time against the best time of a launch that only streams its
+    # 4 MiB of weights (same cold rotation): the share of the single-call floor reached
+    extra["read_floor_over_call"] = round(read_us[best_blocks] / (0.5 * (extra["up_us"] + extra["down_us"])), 3)
 
     if not args.no_extra:
         # MXFP4 weights (E2M1 + an E8M0 scale per 32 values: 0.53 of the FP8

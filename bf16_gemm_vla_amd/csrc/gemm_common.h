@@ -149,9 +149,8 @@ struct Coherent {
 // Coherent::store.  Returns true in the one workgroup that arrives last for
 // `slot`; that workgroup then reads every partial with Coherent::load and
 // must call splitk_reset when done.
-// `flag` is one int of LDS that no wave touches between the two barriers.
-__device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, int ksplit, int* flag) {
-    int& s_last = *flag;
+__device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, int ksplit) {
+    __shared__ int s_last;
     // wait until this wave's partial stores have completed (gfx9 counts
     // stores in vmcnt); the barrier then orders every wave's stores before
     // the arrival below
@@ -163,11 +162,6 @@ __device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, 
     }
     __syncthreads();
     return s_last != 0;
-}
-
-__device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, int ksplit) {
-    __shared__ int s_flag;
-    return splitk_arrive_last(tickets, slot, ksplit, &s_flag);
 }
 
 __device__ __forceinline__ void splitk_reset(uint32_t* tickets, int slot) {
