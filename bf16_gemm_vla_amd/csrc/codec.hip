@@ -26,6 +26,81 @@ __device__ __forceinline__ int64_t slot_offset(int layout, int64_t n0, int64_t s
     return (n0 * 16 + n1) * K + k0 * 32 + k1 * 8;                     // row-major
 }
 
+// Codes of fp32(v / sc) for eight fp32 values, the quotient correctly
+// rounded as IEEE division gives it, with rcp = RN(1 / sc): q = RN(v * rcp)
+// is within 2 ulps of RN(v / sc), and the code only changes at midpoints
+// between E4M3 values (fraction bits 19..0 == 0x80000 in the normal range),
+// so unless q lies within 3 ulps of a midpoint, below the smallest normal
+// value (but not zero) or is not finite, the code of q is the code of the
+// exact quotient.  Those codes come from the hardware conversion (nearest
+// even, signed zero kept), two per instruction, of q clamped to the largest
+// finite value the conversion gets right, since the encoder saturates:
+//   OCP:  |q| clamped to 448 (code 0x7E);
+//   FNUZ: 2 min(|q|, 224) + 0 converted as OCP (an FNUZ byte decodes to half
+//         the OCP value; + 0 turns -0 into +0, FNUZ having no -0), and the
+//         low bit set above 232, the midpoint to 240 (0x7F = 0x7E | 1).
+template <bool FNUZ>
+__device__ __forceinline__ bool needs_exact(float q) {
+    constexpr float lo = FNUZ ? 0x1p-7f : 0x1p-6f;              // smallest normal
+    const bool below_normal = __builtin_fabsf(q) < lo && q != 0.0f;
+    const bool not_finite = !(__builtin_fabsf(q) < __builtin_inff());
+    // fraction bits 19..0 within [0x80000 - 3, 0x80000 + 3]: shifted to the
+    // top of the word, the window is one unsigned compare
+    const bool near_mid = (__float_as_uint(q) << 12) - (0x7FFFDu << 12) <= (6u << 12);
+    return below_normal || not_finite || near_mid;
+}
+
+template <bool FNUZ>
+__device__ __forceinline__ uint2 encode8_fast(const float q[8]) {
+    constexpr float top = FNUZ ? 224.0f : 448.0f;
+    uint32_t o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float c4[4];
+        uint32_t hi_bit = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float qc = __builtin_amdgcn_fmed3f(q[4 * h + j], -top, top);
+            c4[j] = FNUZ ? __builtin_fmaf(qc, 2.0f, 0.0f) : qc;
+            if (FNUZ) hi_bit |= (__builtin_fabsf(q[4 * h + j]) > 232.0f ? 1u : 0u) << (8 * j);
+        }
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(c4[0], c4[1], 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(c4[2], c4[3], c, true);
+        o[h] = static_cast<uint32_t>(c) | hi_bit;
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+// All eight codes: the hardware ones, the elements that need it re-encoded
+// from the exact quotient in a branch, taken by a wave when any of its lanes
+// needs it (the flags are combined as wave-wide lane masks).
+template <bool FNUZ>
+__device__ __forceinline__ uint2 encode8_quotient(const float v[8], float sc, float rcp) {
+    float q[8];
+    uint64_t any = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        q[j] = v[j] * rcp;
+        any |= __builtin_amdgcn_ballot_w64(needs_exact<FNUZ>(q[j]));
+    }
+    const uint2 f = encode8_fast<FNUZ>(q);
+    uint32_t o[2] = {f.x, f.y};
+    if (__builtin_expect(any != 0, 0)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // recomputed here: an opaque copy keeps the compiler from carrying
+            // the eight flags across the branch in registers
+            float qj = q[j];
+            asm volatile("" : "+v"(qj));
+            if (needs_exact<FNUZ>(qj)) {
+                const uint32_t code = encode_e4m3<FNUZ>(__fdiv_rn(v[j], sc));
+                o[j >> 2] = (o[j >> 2] & ~(0xFFu << (8 * (j & 3)))) | (code << (8 * (j & 3)));
+            }
+        }
+    }
+    return make_uint2(o[0], o[1]);
+}
+
 // One workgroup per 16-row tile.  Phase 1: row absmax -> scale.  Phase 2:
 // each thread encodes 8-value slots (reads 2 x 16 B, writes 8 B / 16 B).
 template <int WFMT>
@@ -75,15 +150,8 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(const float* __
                 make_uint4(w[0], w[1], w[2], w[3]);
         } else {
             const float sc = s_scale[n1];
-            uint32_t w[2] = {0, 0};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float x = __fdiv_rn(v[i], sc);
-                const uint32_t code = (WFMT == VLA_WFMT_E4M3_FNUZ) ? encode_e4m3<true>(x)
-                                                                    : encode_e4m3<false>(x);
-                w[i >> 2] |= code << (8 * (i & 3));
-            }
-            *reinterpret_cast<uint2*>(static_cast<uint8_t*>(Wq) + off) = make_uint2(w[0], w[1]);
+            *reinterpret_cast<uint2*>(static_cast<uint8_t*>(Wq) + off) =
+                encode8_quotient<WFMT == VLA_WFMT_E4M3_FNUZ>(v, sc, __fdiv_rn(1.0f, sc));
         }
     }
 }
@@ -151,6 +219,107 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quantize_pack_kernel(const flo
             *reinterpret_cast<uint32_t*>(Wq + slot * 4) = w;
         }
         sc_base[(n0 * 16 + n1) * P + k0] = static_cast<uint8_t>(127 + se);
+    }
+}
+
+// Register-resident FP8 quantize + pack of one 16-row tile by NT threads
+// (the tile's 2K slots of 8 values, SPT = 2K / NT per thread): thread t owns
+// slots t + NT i, which all belong to row t % 16 of the tile (slot % 16 is
+// the row), so the weights are read from HBM once: every load is issued up
+// front, the row maxima are reduced over the threads of each row (lanes
+// l ^ 16, l ^ 32 in a wave, then the waves through LDS), and the codes are
+// encoded from registers with the same encoder (encode8_quotient) as
+// quantize_pack_kernel.  NT = 1024 keeps a thread's share at K / 64 values,
+// so two tiles fit on a compute unit at K = 2048 and the grid drains in
+// whole rounds.
+template <int WFMT, int SPT, int NT>
+__global__ __launch_bounds__(NT) void quantize_pack_reg_kernel(const float* __restrict__ W,
+                                                               uint8_t* __restrict__ Wq,
+                                                               float* __restrict__ scales, int64_t K,
+                                                               int layout) {
+    constexpr int NW = NT / kWave;
+    __shared__ float red[NW][16];
+    const int64_t n0 = blockIdx.x;
+    const int t = threadIdx.x, n1 = t & 15, k1 = (t & 63) >> 4;
+    const float* row = W + (n0 * 16 + n1) * K;
+    float4 a[SPT], b[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int64_t k0 = (t >> 6) + NW * i;      // slot t + NT i: k0 = slot / 64
+        const float* src = row + k0 * 32 + k1 * 8;
+        a[i] = *reinterpret_cast<const float4*>(src);
+        b[i] = *reinterpret_cast<const float4*>(src + 4);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i)
+        m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a[i].x), fabsf(a[i].y)), fmaxf(fabsf(a[i].z), fabsf(a[i].w))),
+                           fmaxf(fmaxf(fabsf(b[i].x), fabsf(b[i].y)), fmaxf(fabsf(b[i].z), fabsf(b[i].w)))));
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    if ((t & 63) < 16) red[t >> 6][n1] = m;
+    __syncthreads();
+    float rm = red[0][n1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) rm = fmaxf(rm, red[w][n1]);
+    const float maxv = (WFMT == VLA_WFMT_E4M3_FNUZ) ? 240.0f : 448.0f;
+    const float sc = (rm == 0.0f) ? 1.0f : __fdiv_rn(rm, maxv);
+    if (t < 16) scales[n0 * 16 + t] = sc;
+    const float rcp = __fdiv_rn(1.0f, sc);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const float v[8] = {a[i].x, a[i].y, a[i].z, a[i].w, b[i].x, b[i].y, b[i].z, b[i].w};
+        *reinterpret_cast<uint2*>(Wq + slot_offset(layout, n0, t + NT * i, K)) =
+            encode8_quotient<WFMT == VLA_WFMT_E4M3_FNUZ>(v, sc, rcp);
+    }
+}
+
+// The same for the row-major layout with K a multiple of 512: wave w owns
+// rows RPW w .. RPW w + RPW - 1 of the tile (RPW = 16 / waves), lane l the 8
+// values at k = 512 c + 8 l of each, so every load and store of a wave is
+// one contiguous run of the row (2 KiB of fp32 in, 512 bytes of codes out)
+// and the row maxima are wave reductions.
+template <int WFMT, int SPT, int NT>
+__global__ __launch_bounds__(NT) void quantize_rows_reg_kernel(const float* __restrict__ W,
+                                                               uint8_t* __restrict__ Wq,
+                                                               float* __restrict__ scales, int64_t K) {
+    constexpr int RPW = 16 / (NT / kWave);           // rows per wave
+    constexpr int CPR = SPT / RPW;                   // 512-value chunks per row
+    static_assert(SPT % RPW == 0, "K a multiple of 512");
+    const int64_t n0 = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    float4 a[SPT], b[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int r = wave * RPW + i / CPR, c = i % CPR;
+        const float* src = W + (n0 * 16 + r) * K + c * 512 + lane * 8;
+        a[i] = *reinterpret_cast<const float4*>(src);
+        b[i] = *reinterpret_cast<const float4*>(src + 4);
+    }
+    float sc[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        float m = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPR; ++c) {
+            const int i = q * CPR + c;
+            m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a[i].x), fabsf(a[i].y)), fmaxf(fabsf(a[i].z), fabsf(a[i].w))),
+                               fmaxf(fmaxf(fabsf(b[i].x), fabsf(b[i].y)), fmaxf(fabsf(b[i].z), fabsf(b[i].w)))));
+        }
+        m = wave_max(m);
+        const float maxv = (WFMT == VLA_WFMT_E4M3_FNUZ) ? 240.0f : 448.0f;
+        sc[q] = (m == 0.0f) ? 1.0f : __fdiv_rn(m, maxv);
+        if (lane == 0) scales[n0 * 16 + wave * RPW + q] = sc[q];
+    }
+    float rcp[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) rcp[q] = __fdiv_rn(1.0f, sc[q]);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int r = wave * RPW + i / CPR, c = i % CPR;
+        const float v[8] = {a[i].x, a[i].y, a[i].z, a[i].w, b[i].x, b[i].y, b[i].z, b[i].w};
+        *reinterpret_cast<uint2*>(Wq + (n0 * 16 + r) * K + c * 512 + lane * 8) =
+            encode8_quotient<WFMT == VLA_WFMT_E4M3_FNUZ>(v, sc[i / CPR], rcp[i / CPR]);
     }
 }
 
@@ -223,6 +392,122 @@ __global__ __launch_bounds__(kThreads) void reencode_kernel(const uint8_t* q, co
     if (t < 16) sc2[n0 * 16 + t] = has240[t] ? sc[n0 * 16 + t] : sc[n0 * 16 + t] * 0.5f;
 }
 
+// Register-resident FNUZ -> OCP for K a multiple of 128 up to 2048: the same
+// slot ownership as quantize_pack_reg_kernel, so every byte is read once
+// (all reads precede any write of the tile, so in-place use stays safe) and
+// the per-row "+-240 present" flag is an OR over the row's 16 threads.
+template <int SPT>
+__global__ __launch_bounds__(kThreads) void reencode_reg_kernel(const uint8_t* q, const float* sc, uint8_t* q2,
+                                                                float* sc2, int64_t K, int layout) {
+    __shared__ uint8_t lut[2][256];
+    __shared__ int hitw[kThreads / kWave][16];
+    const int64_t n0 = blockIdx.x;
+    const int t = threadIdx.x, n1 = t & 15;
+    uint2 v[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) v[i] = *reinterpret_cast<const uint2*>(q + slot_offset(layout, n0, t + kThreads * i, K));
+    {
+        // lut[j][b] = encode_ocp(2^j * decode_fnuz(b)); FNUZ NaN -> 0x7F
+        const uint32_t b = static_cast<uint32_t>(t);
+        if (b == 0x80u) {
+            lut[0][b] = 0x7F;
+            lut[1][b] = 0x7F;
+        } else {
+            const float x = decode_e4m3<true>(b);
+            lut[0][b] = encode_e4m3<false>(x);
+            lut[1][b] = encode_e4m3<false>(x * 2.0f);
+        }
+    }
+    int hit = 0;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hit |= ((((e < 4 ? v[i].x : v[i].y) >> (8 * (e & 3))) & 0x7Fu) == 0x7Fu) ? 1 : 0;
+    hit |= __shfl_xor(hit, 16, kWave);
+    hit |= __shfl_xor(hit, 32, kWave);
+    if ((t & 63) < 16) hitw[t >> 6][n1] = hit;
+    __syncthreads();
+    int h = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) h |= hitw[w][n1];
+    const int j = h ? 0 : 1;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t byte = ((e < 4 ? v[i].x : v[i].y) >> (8 * (e & 3))) & 0xFFu;
+            w[e >> 2] |= static_cast<uint32_t>(lut[j][byte]) << (8 * (e & 3));
+        }
+        *reinterpret_cast<uint2*>(q2 + slot_offset(layout, n0, t + kThreads * i, K)) = make_uint2(w[0], w[1]);
+    }
+    if (t < 16) sc2[n0 * 16 + t] = h ? sc[n0 * 16 + t] : sc[n0 * 16 + t] * 0.5f;
+}
+
+// Row-major FNUZ -> OCP with K a multiple of 512: the row mapping of
+// quantize_rows_reg_kernel (contiguous 512-byte runs per wave, the +-240
+// flag of a row is a wave ballot).  All reads precede the writes.
+template <int SPT>
+__global__ __launch_bounds__(kThreads) void reencode_rows_reg_kernel(const uint8_t* q, const float* sc, uint8_t* q2,
+                                                                     float* sc2, int64_t K) {
+    constexpr int RPW = 16 / (kThreads / kWave);
+    constexpr int CPR = SPT / RPW;
+    static_assert(SPT % RPW == 0, "K a multiple of 512");
+    __shared__ uint8_t lut[2][256];
+    const int64_t n0 = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    uint2 v[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int r = wave * RPW + i / CPR, c = i % CPR;
+        v[i] = *reinterpret_cast<const uint2*>(q + (n0 * 16 + r) * K + c * 512 + lane * 8);
+    }
+    // lane q < RPW carries the scale of the wave's row q
+    const float s_my = (lane < RPW) ? sc[n0 * 16 + wave * RPW + lane] : 0.0f;
+    {
+        const uint32_t b = static_cast<uint32_t>(t);
+        if (b == 0x80u) {
+            lut[0][b] = 0x7F;
+            lut[1][b] = 0x7F;
+        } else {
+            const float x = decode_e4m3<true>(b);
+            lut[0][b] = encode_e4m3<false>(x);
+            lut[1][b] = encode_e4m3<false>(x * 2.0f);
+        }
+    }
+    int jr[RPW];
+#pragma unroll
+    for (int qr = 0; qr < RPW; ++qr) {
+        bool hit = false;
+#pragma unroll
+        for (int c = 0; c < CPR; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                hit |= (((e < 4 ? v[qr * CPR + c].x : v[qr * CPR + c].y) >> (8 * (e & 3))) & 0x7Fu) == 0x7Fu;
+        jr[qr] = __ballot(hit) ? 0 : 1;
+    }
+    __syncthreads();   // the byte maps are built
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int r = wave * RPW + i / CPR, c = i % CPR;
+        const int j = jr[i / CPR];
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t byte = ((e < 4 ? v[i].x : v[i].y) >> (8 * (e & 3))) & 0xFFu;
+            w[e >> 2] |= static_cast<uint32_t>(lut[j][byte]) << (8 * (e & 3));
+        }
+        *reinterpret_cast<uint2*>(q2 + (n0 * 16 + r) * K + c * 512 + lane * 8) = make_uint2(w[0], w[1]);
+    }
+    if (lane < RPW) {
+        int jm = jr[0];
+#pragma unroll
+        for (int qr = 1; qr < RPW; ++qr)
+            if (lane == qr) jm = jr[qr];
+        sc2[n0 * 16 + wave * RPW + lane] = jm ? s_my * 0.5f : s_my;
+    }
+}
+
 // Activation quantization, pass 1: per-block absmax of 8-element chunks.
 constexpr int kActBlocks = 512;
 
@@ -263,44 +548,13 @@ __global__ __launch_bounds__(kThreads) void act_absmax_kernel(const uint16_t* __
     }
 }
 
-// OCP E4M3 codes of fp32(x / sc) for the 8 bf16 values of one dword quad,
-// the quotient correctly rounded as IEEE division gives it.  With rcp =
-// RN(1/sc), q = RN(x * rcp) is within 2 fp32 ulps of RN(x / sc), and the
-// code only changes at the midpoints between E4M3 values (fp32 fraction
-// bits 19..0 == 0x80000 in the normal range), so the code of q is the code
-// of the exact quotient unless q lies within 3 ulps of a midpoint, below the
-// smallest normal E4M3 value (2^-6) but not zero, at/above 448, or is not
-// finite.  Such q take the exact division and the bit-level encoder; all
-// other q are zero or normal-range E4M3 values, which the hardware
-// conversion (round to nearest even, gfx950's OCP format, signed zero kept)
-// encodes two per instruction.
+// OCP E4M3 codes of fp32(x / sc) for the 8 bf16 values of one dword quad
+// (encode8_quotient with the bf16 values widened to fp32).
 __device__ __forceinline__ uint2 act_codes8(const uint32_t w[4], float sc, float rcp) {
-    float x[8], q[8];
-    bool slow[8];
+    float x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        x[j] = __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
-        q[j] = x[j] * rcp;
-        const uint32_t a = __float_as_uint(q[j]) & 0x7FFFFFFFu;
-        const bool out_of_range = (a - 0x3C800000u) >= (0x43E00000u - 0x3C800000u);   // not in [2^-6, 448)
-        const bool near_mid = ((a & 0xFFFFFu) - (0x80000u - 3u)) <= 6u;
-        slow[j] = (out_of_range && a != 0u) || near_mid;
-    }
-    uint32_t o[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int v = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * h], q[4 * h + 1], 0, false);
-        v = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * h + 2], q[4 * h + 3], v, true);
-        o[h] = static_cast<uint32_t>(v);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (__builtin_expect(slow[j], 0)) {
-            const uint32_t code = encode_e4m3<false>(__fdiv_rn(x[j], sc));
-            o[j >> 2] = (o[j >> 2] & ~(0xFFu << (8 * (j & 3)))) | (code << (8 * (j & 3)));
-        }
-    }
-    return make_uint2(o[0], o[1]);
+    for (int j = 0; j < 8; ++j) x[j] = __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+    return encode8_quotient<false>(x, sc, rcp);
 }
 
 // Pass 2: every block loads its kActUnroll chunks per thread first, then
@@ -352,9 +606,48 @@ __global__ __launch_bounds__(kThreads) void act_encode_kernel(const uint16_t* __
 
 }  // namespace
 
+// K / 128 slots per thread, 1 .. 16 (K a multiple of 128, at most 2048).
+#define VLA_SPT_CASES(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
+
 hipError_t launch_quantize_pack(const float* W, void* Wq, float* scales, int64_t N, int64_t K,
                                 int wfmt, int layout, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 16));
+    // K a multiple of 512 up to 4096: 1024 threads per tile (one row per
+    // wave in the row-major kernel), K / 512 slots per thread
+    if (wfmt != VLA_WFMT_BF16 && K % 512 == 0 && K <= 4096) {
+        const int spt = static_cast<int>(K / 512);
+        uint8_t* q = static_cast<uint8_t*>(Wq);
+#define VLA_Q1K(SPT_)                                                                                  \
+        if (spt == SPT_) {                                                                             \
+            if (layout == 0 && wfmt == VLA_WFMT_E4M3_OCP)                                              \
+                quantize_rows_reg_kernel<VLA_WFMT_E4M3_OCP, SPT_, 1024><<<grid, 1024, 0, s>>>(W, q, scales, K); \
+            else if (layout == 0)                                                                      \
+                quantize_rows_reg_kernel<VLA_WFMT_E4M3_FNUZ, SPT_, 1024><<<grid, 1024, 0, s>>>(W, q, scales, K); \
+            else if (wfmt == VLA_WFMT_E4M3_OCP)                                                        \
+                quantize_pack_reg_kernel<VLA_WFMT_E4M3_OCP, SPT_, 1024><<<grid, 1024, 0, s>>>(W, q, scales, K, layout); \
+            else                                                                                       \
+                quantize_pack_reg_kernel<VLA_WFMT_E4M3_FNUZ, SPT_, 1024><<<grid, 1024, 0, s>>>(W, q, scales, K, layout); \
+            return hipGetLastError();                                                                  \
+        }
+        VLA_Q1K(1) VLA_Q1K(2) VLA_Q1K(3) VLA_Q1K(4) VLA_Q1K(5) VLA_Q1K(6) VLA_Q1K(7) VLA_Q1K(8)
+#undef VLA_Q1K
+    }
+    // other K, multiples of 128 up to 2048: 256 threads, K / 128 slots each
+    if (wfmt != VLA_WFMT_BF16 && K % 128 == 0 && K <= 2048) {
+        const int spt = static_cast<int>(K / 128);
+        uint8_t* q = static_cast<uint8_t*>(Wq);
+#define VLA_QP(SPT_)                                                                                   \
+        if (spt == SPT_) {                                                                             \
+            if (wfmt == VLA_WFMT_E4M3_OCP)                                                             \
+                quantize_pack_reg_kernel<VLA_WFMT_E4M3_OCP, SPT_, kThreads><<<grid, kThreads, 0, s>>>(W, q, scales, K, layout); \
+            else                                                                                       \
+                quantize_pack_reg_kernel<VLA_WFMT_E4M3_FNUZ, SPT_, kThreads><<<grid, kThreads, 0, s>>>(W, q, scales, K, layout); \
+            return hipGetLastError();                                                                  \
+        }
+        VLA_QP(1) VLA_QP(2) VLA_QP(3) VLA_QP(5) VLA_QP(6) VLA_QP(7) VLA_QP(9) VLA_QP(10) VLA_QP(11) VLA_QP(13)
+        VLA_QP(14) VLA_QP(15)
+#undef VLA_QP
+    }
     switch (wfmt) {
         case VLA_WFMT_BF16:
             quantize_pack_kernel<VLA_WFMT_BF16><<<grid, kThreads, 0, s>>>(W, Wq, scales, K, layout);
@@ -384,6 +677,26 @@ hipError_t launch_pack_fp8(const uint8_t* q, uint8_t* qp, int64_t N, int64_t K, 
 
 hipError_t launch_reencode(const uint8_t* q, const float* sc, uint8_t* q2, float* sc2, int64_t N,
                            int64_t K, int layout, hipStream_t s) {
+    if (layout == 0 && K % 512 == 0 && K <= 2048) {
+        const int spt = static_cast<int>(K / 128);
+#define VLA_RR(SPT_)                                                                                                    \
+        if (spt == SPT_) {                                                                                              \
+            reencode_rows_reg_kernel<SPT_><<<static_cast<unsigned>(N / 16), kThreads, 0, s>>>(q, sc, q2, sc2, K);      \
+            return hipGetLastError();                                                                                   \
+        }
+        VLA_RR(4) VLA_RR(8) VLA_RR(12) VLA_RR(16)
+#undef VLA_RR
+    }
+    if (K % 128 == 0 && K <= 2048) {
+        const int spt = static_cast<int>(K / 128);
+#define VLA_RE(SPT_)                                                                                                  \
+        if (spt == SPT_) {                                                                                            \
+            reencode_reg_kernel<SPT_><<<static_cast<unsigned>(N / 16), kThreads, 0, s>>>(q, sc, q2, sc2, K, layout); \
+            return hipGetLastError();                                                                                 \
+        }
+        VLA_SPT_CASES(VLA_RE)
+#undef VLA_RE
+    }
     reencode_kernel<<<static_cast<unsigned>(N / 16), kThreads, 0, s>>>(q, sc, q2, sc2, K, layout);
     return hipGetLastError();
 }

@@ -32,7 +32,10 @@ def oracle_codes(W, dialect, layout):
     return (oracle.pack(q, 8) if layout == vla.VLA_LAYOUT_MFMA else q.reshape(-1)), s
 
 
-SHAPES = [(64, 128, "tiny.W"), (16, 32, "edge.min"), (48, 96, "edge.ragged"), (1024, 4096, "skinny.down.W")]
+# K a multiple of 512 up to 4096 takes the 1024-thread register-resident kernels, other multiples
+# of 128 up to 2048 the 256-thread one, the others the two-pass kernel
+SHAPES = [(64, 128, "tiny.W"), (16, 32, "edge.min"), (48, 96, "edge.ragged"), (1024, 4096, "skinny.down.W"),
+          (4096, 1024, "skinny.up.W"), (32, 384, "edge.spt3"), (48, 2048, "wide.up.A"), (32, 2560, "edge.k2560")]
 
 
 @pytest.mark.parametrize("dialect", [OCP, FNUZ])
@@ -46,6 +49,53 @@ def test_quantize_pack_bit_exact(dialect, layout, N, K, name):
     q, s = gpu_quantize(W, WFMT[dialect], layout)
     ref_q, ref_s = oracle_codes(W, dialect, layout)
     assert np.array_equal(s.numpy(np.float32), ref_s)
+    got = q.numpy(np.uint8)
+    assert np.array_equal(got, ref_q), f"{(got != ref_q).sum()} bytes differ"
+
+
+def _e4m3_grid(fnuz):
+    """Non-negative finite E4M3 values in increasing order (OCP: max 448; FNUZ:
+    every OCP byte's value halved, 0x7F = 240 included)."""
+    vals = [m / 8 * 2.0 ** -6 for m in range(8)]
+    vals += [2.0 ** (e - 7) * (1 + m / 8) for e in range(1, 16) for m in range(8)]
+    vals = vals[:-1]                                      # OCP 0x7F is NaN
+    return [v / 2 for v in vals] + [240.0] if fnuz else vals
+
+
+@pytest.mark.parametrize("dialect", [OCP, FNUZ])
+@pytest.mark.parametrize("layout", [vla.VLA_LAYOUT_MFMA, vla.VLA_LAYOUT_ROWMAJOR])
+@pytest.mark.parametrize("K", [512, 96])
+def test_quantize_pack_rounding_midpoints(dialect, layout, K):
+    """Quotients placed within a few fp32 ulps of every E4M3 rounding midpoint
+    (and of every grid value, the range top and the subnormal range), where
+    a reciprocal-based encoder must fall back to exact division."""
+    print(f"quantize_pack midpoints dialect={dialect} layout={layout} K={K}", flush=True)
+    grid = _e4m3_grid(dialect == FNUZ)
+    fmax = grid[-1]
+    amax = np.float32(3.7)
+    s = np.float32(np.float64(amax) / fmax)
+    targets = [(a + b) / 2 for a, b in zip(grid[:-1], grid[1:])] + grid[1:] + [grid[1] / 2, grid[1] / 4]
+    cand = []
+    for t in targets:
+        w = np.float32(t * np.float64(s))
+        for k in range(-4, 5):
+            x = w
+            for _ in range(abs(k)):
+                x = np.nextafter(x, np.float32(np.inf if k > 0 else -np.inf))
+            if abs(x) <= amax:
+                cand += [x, -x]
+    per_row = K - 1
+    N = -(-len(cand) // per_row)
+    N = -(-N // 16) * 16
+    rng = np.random.default_rng(77)
+    W = rng.uniform(-3.5, 3.5, size=(N, K)).astype(np.float32)
+    flat = W[:, 1:].reshape(-1)
+    flat[:len(cand)] = np.float32(cand)
+    W[:, 1:] = flat.reshape(N, per_row)
+    W[:, 0] = np.where(np.arange(N) % 2 == 0, amax, -amax)
+    q, sg = gpu_quantize(W, WFMT[dialect], layout)
+    ref_q, ref_s = oracle_codes(W, dialect, layout)
+    assert np.array_equal(sg.numpy(np.float32), ref_s)
     got = q.numpy(np.uint8)
     assert np.array_equal(got, ref_q), f"{(got != ref_q).sum()} bytes differ"
 
@@ -79,11 +129,12 @@ def test_dialect_config_fnuz_reencode_pack():
     assert np.array_equal(qp.numpy(np.uint8), oracle.pack(ref_q2, 8))
 
 
+@pytest.mark.parametrize("K", [256, 160, 2048])
 @pytest.mark.parametrize("layout", [vla.VLA_LAYOUT_MFMA, vla.VLA_LAYOUT_ROWMAJOR])
-def test_reencode_j1_rows_and_in_place(layout):
+def test_reencode_j1_rows_and_in_place(layout, K):
     """Rows without +-240 keep their bytes at half scale; in-place use allowed."""
     g = synthetic.rng(4242)
-    N, K = 64, 256
+    N = 64
     allowed = np.array([b for b in range(256) if b not in (0x7F, 0xFF, 0x80)], np.uint8)
     q = allowed[g.integers(0, len(allowed), (N, K))]
     q[::3, 5] = 0x7F            # every third row holds +240 -> j = 0
