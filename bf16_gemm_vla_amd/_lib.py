@@ -54,7 +54,7 @@ SIGNATURES = {
     "vla_gemm_fp8w": (INT, [P, P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_gemm_bf16": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_gemm_mxfp4w": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
-    "vla_gemm_fp8w_gelu_mul": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
+    "vla_gemm_fp8w_gelu_mul": (INT, [P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_mlp_chain_scratch_bytes": (SZ, [I64, I64, I64]),
     "vla_mlp_chain_enqueue": (INT, [P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P]),
     "vla_mlp_chain_create": (INT, [P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P, P]),
@@ -203,8 +203,8 @@ def vla_gemm_mxfp4w(A, Wq, bias, residual, Y, ws, ws_bytes, M, N, K, stream=None
                                   M, N, K, _stream(stream)), "vla_gemm_mxfp4w")
 
 
-def vla_gemm_fp8w_gelu_mul(A, Wgu, s_gu, act, gu, ws, ws_bytes, M, I, K, stream=None):
-    _check(load().vla_gemm_fp8w_gelu_mul(_ptr(A), _ptr(Wgu), _ptr(s_gu), _ptr(act), _ptr(gu),
+def vla_gemm_fp8w_gelu_mul(A, Wgu, s_gu, bias, act, gu, ws, ws_bytes, M, I, K, stream=None):
+    _check(load().vla_gemm_fp8w_gelu_mul(_ptr(A), _ptr(Wgu), _ptr(s_gu), _ptr(bias), _ptr(act), _ptr(gu),
                                          _ptr(ws), ws_bytes, M, I, K, _stream(stream)),
            "vla_gemm_fp8w_gelu_mul")
 

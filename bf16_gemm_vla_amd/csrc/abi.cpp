@@ -562,7 +562,7 @@ int vla_gemm_mxfp4w(const uint16_t* A, const uint8_t* Wq, const uint16_t* bias, 
     return run_gemm(fn, p, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
-int vla_gemm_fp8w_gelu_mul(const uint16_t* A, const uint8_t* Wgu, const float* s_gu,
+int vla_gemm_fp8w_gelu_mul(const uint16_t* A, const uint8_t* Wgu, const float* s_gu, const uint16_t* bias,
                            uint16_t* act, uint16_t* gu, void* ws, size_t ws_bytes, int64_t M,
                            int64_t I, int64_t K, void* stream) {
     const char* fn = "vla_gemm_fp8w_gelu_mul";
@@ -571,11 +571,12 @@ int vla_gemm_fp8w_gelu_mul(const uint16_t* A, const uint8_t* Wgu, const float* s
     REQUIRE_PTR(A);
     REQUIRE_PTR(Wgu);
     REQUIRE_PTR(s_gu);
+    OPTIONAL_PTR(bias);
     REQUIRE_PTR(act);
     OPTIONAL_PTR(gu);
     REQUIRE_PTR(ws);
     vla::GemmProblem p{};
-    p.A = A; p.W = Wgu; p.s_w = s_gu; p.Y = act; p.gu = gu; p.ws = ws;
+    p.A = A; p.W = Wgu; p.s_w = s_gu; p.bias = bias; p.Y = act; p.gu = gu; p.ws = ws;
     p.M = M; p.N = 2 * I; p.K = K;
     p.atype = vla::AType::BF16;
     p.wtype = vla::WType::FP8;

@@ -43,7 +43,8 @@ struct KArgs {
 struct EpiIn {
     float4 s;       // weight scales (gate scales for the fused gate/up epilogue)
     float4 su;      // up scales (fused gate/up epilogue)
-    uint2 bias;
+    uint2 bias;     // bias (gate bias for the fused gate/up epilogue)
+    uint2 bu;       // up bias (fused gate/up epilogue)
     uint2 resid;
 };
 
@@ -56,10 +57,15 @@ __device__ __forceinline__ EpiIn load_epi(const KArgs& a, int m, int n, bool wit
     e.s = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
     e.su = e.s;
     e.bias = make_uint2(0, 0);
+    e.bu = make_uint2(0, 0);
     e.resid = make_uint2(0, 0);
     if (WT == WType::FP8) e.s = *reinterpret_cast<const float4*>(a.s_w + n);
     if (EPI == Epi::GELU_MUL) {
         e.su = *reinterpret_cast<const float4*>(a.s_w + (a.N >> 1) + n);
+        if (a.bias) {
+            e.bias = *reinterpret_cast<const uint2*>(a.bias + n);
+            e.bu = *reinterpret_cast<const uint2*>(a.bias + (a.N >> 1) + n);
+        }
     } else {
         if (a.bias) e.bias = *reinterpret_cast<const uint2*>(a.bias + n);
         if (a.resid && with_resid) e.resid = *reinterpret_cast<const uint2*>(a.resid + static_cast<int64_t>(m) * a.N + n);
@@ -103,11 +109,24 @@ __device__ __forceinline__ void store_plain(const KArgs& a, int m, int n, f32x4_
     *reinterpret_cast<uint2*>(a.Y + static_cast<int64_t>(m) * a.N + n) = o;
 }
 
-// act = bf16(gelu_tanh(g) * u) with g = bf16(vg * sg), u = bf16(vu * su);
-// four gate columns.  g and u are returned for the optional gate/up output.
-__device__ __forceinline__ uint2 epi_gelu4(f32x4_t vg, f32x4_t vu, const EpiIn& e, uint2& gp, uint2& up) {
-    gp = make_uint2(f32x2_to_bf16x2(vg[0] * e.s.x, vg[1] * e.s.y), f32x2_to_bf16x2(vg[2] * e.s.z, vg[3] * e.s.w));
-    up = make_uint2(f32x2_to_bf16x2(vu[0] * e.su.x, vu[1] * e.su.y), f32x2_to_bf16x2(vu[2] * e.su.z, vu[3] * e.su.w));
+// act = bf16(gelu_tanh(g) * u) with g = bf16(vg * sg (+ bg)), u = bf16(vu * su
+// (+ bu)); four gate columns.  g and u are returned for the optional gate/up
+// output.
+__device__ __forceinline__ uint2 epi_gelu4(f32x4_t vg, f32x4_t vu, const EpiIn& e, bool bias, uint2& gp, uint2& up) {
+    float g[4] = {vg[0] * e.s.x, vg[1] * e.s.y, vg[2] * e.s.z, vg[3] * e.s.w};
+    float u[4] = {vu[0] * e.su.x, vu[1] * e.su.y, vu[2] * e.su.z, vu[3] * e.su.w};
+    if (bias) {
+        g[0] += bf16_to_f32(lo16(e.bias.x));
+        g[1] += bf16_to_f32(hi16(e.bias.x));
+        g[2] += bf16_to_f32(lo16(e.bias.y));
+        g[3] += bf16_to_f32(hi16(e.bias.y));
+        u[0] += bf16_to_f32(lo16(e.bu.x));
+        u[1] += bf16_to_f32(hi16(e.bu.x));
+        u[2] += bf16_to_f32(lo16(e.bu.y));
+        u[3] += bf16_to_f32(hi16(e.bu.y));
+    }
+    gp = make_uint2(f32x2_to_bf16x2(g[0], g[1]), f32x2_to_bf16x2(g[2], g[3]));
+    up = make_uint2(f32x2_to_bf16x2(u[0], u[1]), f32x2_to_bf16x2(u[2], u[3]));
     const float a0 = gelu_tanh(bf16_to_f32(lo16(gp.x))) * bf16_to_f32(lo16(up.x));
     const float a1 = gelu_tanh(bf16_to_f32(hi16(gp.x))) * bf16_to_f32(hi16(up.x));
     const float a2 = gelu_tanh(bf16_to_f32(lo16(gp.y))) * bf16_to_f32(lo16(up.y));
@@ -119,7 +138,7 @@ __device__ __forceinline__ uint2 epi_gelu4(f32x4_t vg, f32x4_t vu, const EpiIn& 
 __device__ __forceinline__ void store_gelu(const KArgs& a, int m, int n, f32x4_t vg, f32x4_t vu, const EpiIn& e) {
     const int I = a.N >> 1;
     uint2 g, u;
-    const uint2 o = epi_gelu4(vg, vu, e, g, u);
+    const uint2 o = epi_gelu4(vg, vu, e, a.bias != nullptr, g, u);
     *reinterpret_cast<uint2*>(a.Y + static_cast<int64_t>(m) * I + n) = o;
     if (a.gu) {
         *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + n) = g;

@@ -563,7 +563,7 @@ void wide_gemm_kernel(KArgs a) {
                     *reinterpret_cast<uint2*>(orow + nl * 2) =
                         epi_gelu4(f32x4_t{vg[4 * rq], vg[4 * rq + 1], vg[4 * rq + 2], vg[4 * rq + 3]},
                                   f32x4_t{vu[4 * rq], vu[4 * rq + 1], vu[4 * rq + 2], vu[4 * rq + 3]},
-                                  ein[ns][rq], gq, uq);
+                                  ein[ns][rq], a.bias != nullptr, gq, uq);
                     if (a.gu && m < a.M) {
                         *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + n) = gq;
                         *reinterpret_cast<uint2*>(a.gu + static_cast<int64_t>(m) * a.N + outN + n) = uq;

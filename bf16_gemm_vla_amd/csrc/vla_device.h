@@ -143,9 +143,16 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// GELU, tanh form: 0.5 g (1 + tanh(z)), z = sqrt(2/pi) (g + 0.044715 g^3),
+// evaluated as g / (1 + exp(-2z)) (the same function: 1 + tanh(z) =
+// 2 / (1 + exp(-2z))), which keeps its relative accuracy for negative g,
+// where 1 + tanh(z) cancels to a few ulps or to zero in fp32.  The IEEE
+// division keeps tiny results (down to the subnormals); for very negative g,
+// exp overflows to inf and the result is -0.
 __device__ __forceinline__ float gelu_tanh(float g) {
     const float c = 0.7978845608028654f;  // sqrt(2/pi)
-    return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+    const float z = c * (g + 0.044715f * g * g * g);
+    return g / (1.0f + expf(-2.0f * z));
 }
 
 }  // namespace vla

@@ -235,13 +235,19 @@ int vla_gemm_bf16(const uint16_t *A, const uint16_t *Wq, const uint16_t *bias,
  * "Real-time VLA inference on AMD hardware", section "Merging gate and up":
  * the gate and up weights are concatenated, W = [W_gate; W_up] (2I x K,
  * rows 0..I-1 gate, I..2I-1 up), and one GEMM computes both.
- *   g = bf16(s[n] * A @ W_gate^T), u = bf16(s[I+n] * A @ W_up^T),
+ *   g = bf16(s[n] * A @ W_gate^T + b[n]), u = bf16(s[I+n] * A @ W_up^T + b[I+n]),
  *   act = bf16( 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) * u ).
+ * The bias is added in the same epilogue, as that section describes.
  *   A     device bf16 M x K.
  *   Wgu   OCP E4M3 2I x K in VLA_LAYOUT_MFMA, s_gu its fp32[2I] scales.
+ *   bias  device bf16[2I] = [b_gate, b_up], or NULL for none.
  *   act   device bf16 M x I output.
  *   gu    device bf16 M x 2I output of [g, u], or NULL.
  * I must be a multiple of 16.  Workspace: vla_gemm_workspace_bytes(M, 2I, K, OCP). */
+int vla_gemm_fp8w_gelu_mul(const uint16_t *A, const uint8_t *Wgu, const float *s_gu, const uint16_t *bias,
+                           uint16_t *act, uint16_t *gu, void *ws, size_t ws_bytes, int64_t M,
+                           int64_t I, int64_t K, void *stream);
+
 /* As vla_gemm_fp8w with MXFP4 weights (bf16 activations, no per-channel
  * scale: each 32-value block of a weight row carries its E8M0 scale):
  *   Y = bf16(A @ (dec(q) * 2^(e - 127))^T + bias) (+ residual, as above)
@@ -253,10 +259,6 @@ int vla_gemm_bf16(const uint16_t *A, const uint16_t *Wq, const uint16_t *bias,
  * workspace vla_gemm_workspace_bytes(M, N, K, VLA_WFMT_MXFP4). */
 int vla_gemm_mxfp4w(const uint16_t *A, const uint8_t *Wq, const uint16_t *bias, const uint16_t *residual,
                     uint16_t *Y, void *ws, size_t ws_bytes, int64_t M, int64_t N, int64_t K, void *stream);
-
-int vla_gemm_fp8w_gelu_mul(const uint16_t *A, const uint8_t *Wgu, const float *s_gu,
-                           uint16_t *act, uint16_t *gu, void *ws, size_t ws_bytes, int64_t M,
-                           int64_t I, int64_t K, void *stream);
 
 /* ------------------------------------------------------- gated-MLP chain */
 

@@ -92,7 +92,9 @@ def test_gemm_workspace_too_small(lib):
 
 def test_gelu_mul_shape_errors(lib):
     # I = 24 is not a multiple of 16
-    assert rc_of("vla_gemm_fp8w_gelu_mul", A16, A16, A16, A16, None, A16, 1 << 20, 50, 24, 128, None) == vla.VLA_ESHAPE
+    assert rc_of("vla_gemm_fp8w_gelu_mul", A16, A16, A16, None, A16, None, A16, 1 << 20, 50, 24, 128, None) == vla.VLA_ESHAPE
+    # a misaligned bias is rejected before any launch
+    assert rc_of("vla_gemm_fp8w_gelu_mul", A16, A16, A16, A16 + 2, A16, None, A16, 1 << 20, 50, 32, 128, None) == vla.VLA_EALIGN
 
 
 def test_codec_errors(lib):

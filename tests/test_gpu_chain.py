@@ -47,7 +47,7 @@ def test_gelu_mul_stage(M, I, K):
     A = synthetic.activations(M, K, 7000 + M)
     act, gu = Guarded(M * I * 2), Guarded(M * 2 * I * 2)
     ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, 2 * I, K, 1))
-    vla.vla_gemm_fp8w_gelu_mul(dev(A), cw.wgu[0], cw.sgu[0], act.t, gu.t, ws, ws.numel(), M, I, K)
+    vla.vla_gemm_fp8w_gelu_mul(dev(A), cw.wgu[0], cw.sgu[0], None, act.t, gu.t, ws, ws.numel(), M, I, K)
     act.check(); gu.check()
     gu_bits = gu.numpy(np.uint16).reshape(M, 2 * I)
     # stage 1: the merged GEMM against the oracle GEMM
@@ -61,8 +61,32 @@ def test_gelu_mul_stage(M, I, K):
     assert np.all((diff <= 1) & same_sign | (got == want))
     # without the debug output the activation is identical
     act2 = torch.empty(M * I, dtype=torch.int16, device="cuda")
-    vla.vla_gemm_fp8w_gelu_mul(dev(A), cw.wgu[0], cw.sgu[0], act2, None, ws, ws.numel(), M, I, K)
+    vla.vla_gemm_fp8w_gelu_mul(dev(A), cw.wgu[0], cw.sgu[0], None, act2, None, ws, ws.numel(), M, I, K)
     assert np.array_equal(host(act2).view(np.uint16).reshape(M, I), got)
+
+
+@pytest.mark.parametrize("M,I,K", [(50, 4096, 1024), (17, 48, 96), (300, 256, 512)])
+def test_gelu_mul_stage_bias(M, I, K):
+    """The merged gate/up GEMM adds [b_gate, b_up] in its epilogue: g and u
+    against the oracle GEMM with the bias, act from the GPU's own g and u."""
+    print(f"gelu_mul bias M={M} I={I} K={K}", flush=True)
+    cw = ChainWeights(1, K, I, seed=M + 1, with_down=False)
+    A = synthetic.activations(M, K, 7100 + M)
+    b_bits = synthetic.activations(1, 2 * I, 7200 + M)[0]
+    act, gu = Guarded(M * I * 2), Guarded(M * 2 * I * 2)
+    ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, 2 * I, K, 1))
+    vla.vla_gemm_fp8w_gelu_mul(dev(A), cw.wgu[0], cw.sgu[0], dev(b_bits), act.t, gu.t, ws, ws.numel(), M, I, K)
+    act.check(); gu.check()
+    gu_bits = gu.numpy(np.uint16).reshape(M, 2 * I)
+    ref, yabs = oracle.gemm(bf16_f64(A), oracle.dequant_rows(cw.o_gu[0], cw.o_sgu[0]), bf16_f64(b_bits))
+    assert_gemm_close(gu_bits, ref, yabs)
+    want = oracle.gelu_mul(gu_bits[:, :I], gu_bits[:, I:])
+    got = act.numpy(np.uint16).reshape(M, I)
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    same_sign = (got >> 15) == (want >> 15)
+    assert np.all((diff <= 1) & same_sign | (got == want))
+    # every split-K counter is back at zero after the call
+    assert int(host(ws[:61440]).view(np.uint32).sum()) == 0
 
 
 def make_chain(L, M, H, I, seed=0):

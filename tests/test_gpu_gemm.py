@@ -310,7 +310,7 @@ def test_graph_replays_equal_eager():
     wg = Weights(synthetic.weights(2 * I, K, 9971), vla.VLA_WFMT_E4M3_OCP)
     wsg = zeros_ws(vla.vla_gemm_workspace_bytes(M, 2 * I, K, 1))
     act = torch.empty(M * I, dtype=torch.int16, device="cuda")
-    calls.append(lambda: vla.vla_gemm_fp8w_gelu_mul(Ag, wg.q, wg.s, act, None, wsg, wsg.numel(), M, I, K))
+    calls.append(lambda: vla.vla_gemm_fp8w_gelu_mul(Ag, wg.q, wg.s, None, act, None, wsg, wsg.numel(), M, I, K))
     calls[-1].Y = act
 
     for c in calls:
