@@ -322,7 +322,8 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
     for Mw, prefix in ((768, "wide"), (571, "wide_m571")):
         for name, (n, k) in ((prefix + "_up", (16384, 2048)), (prefix + "_down", (2048, 16384))):
             A = up_bits(synthetic.activations(Mw, k, 910 + n))
-            q, s = quantize(synthetic.weights(n, k, 911 + n))
+            Wf = synthetic.weights(n, k, 911 + n)
+            q, s = quantize(Wf)
             Y = torch.empty(Mw * n, dtype=torch.int16, device=dev)
             wsb = vla.vla_gemm_workspace_bytes(Mw, n, k, 1)
             ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
@@ -357,6 +358,23 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
                 vla.vla_quantize_act_static(A, sa, qa, Mw, k)
             ms = time_graph(actq_static, 20)
             out[f"{name}_act_quant_static_us"] = round(ms * 1000.0 / 20, 2)
+
+            if Mw == 768:   # MXFP4 weights, bf16 activations (converted to bf16 in registers, bf16 MFMA)
+                qm = torch.empty(vla.vla_packed_bytes(n, k, vla.VLA_WFMT_MXFP4), dtype=torch.uint8, device=dev)
+                vla.vla_quantize_pack(up_bits(Wf), qm, None, n, k, vla.VLA_WFMT_MXFP4, vla.VLA_LAYOUT_MFMA)
+                wsmb = vla.vla_gemm_workspace_bytes(Mw, n, k, vla.VLA_WFMT_MXFP4)
+                wsm_w = torch.zeros(wsmb, dtype=torch.uint8, device=dev)
+
+                def w4a16(i):
+                    vla.vla_gemm_mxfp4w(A, qm, None, None, Y, wsm_w, wsmb, Mw, n, k)
+                ms = time_graph(w4a16, 20)
+                us = ms * 1000.0 / 20
+                tf = flops / (us * 1e-6) / 1e12
+                out[f"{name}_mxfp4_us"] = round(us, 2)
+                out[f"{name}_mxfp4_TFLOPs"] = round(tf, 1)
+                out[f"{name}_mxfp4_frac"] = round(tf / BF16_PEAK_TFLOPS, 4)
+                del qm, wsm_w
+            del Wf
 
     log("secondary: fused decoder boundary")
     bx, by, bg, bs = (up_bits(t) for t in synthetic.boundary_inputs(M, H, M))

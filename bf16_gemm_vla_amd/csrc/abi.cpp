@@ -490,7 +490,6 @@ int vla_gemm_supported(int64_t M, int64_t N, int64_t K, int wfmt, int fp8_act, i
                           : (wfmt == VLA_WFMT_MXFP4 ? vla::WType::FP4 : vla::WType::FP8);
     const vla::Epi epi = gelu_mul ? vla::Epi::GELU_MUL : vla::Epi::PLAIN;
     if ((gelu_mul || fp8_act) && wt != vla::WType::FP8) return fail(VLA_EINVAL, fn, "fp8_act and gelu_mul need FP8 weights");
-    if (wt == vla::WType::FP4 && M > 64) return fail(VLA_ESHAPE, fn, "MXFP4 weights: M <= 64 only");
     if (gelu_mul && fp8_act) return fail(VLA_EINVAL, fn, "gelu_mul takes bf16 activations");
     if (gelu_mul && (N % 32) != 0) return fail(VLA_ESHAPE, fn, "gelu_mul needs N = 2I with I a multiple of 16");
     const vla::GemmPlan p = vla::plan_gemm(M, N, K, at, wt, epi);
@@ -546,7 +545,6 @@ int vla_gemm_mxfp4w(const uint16_t* A, const uint8_t* Wq, const uint16_t* bias, 
                     uint16_t* Y, void* ws, size_t ws_bytes, int64_t M, int64_t N, int64_t K, void* stream) {
     const char* fn = "vla_gemm_mxfp4w";
     if (int rc = check_mnk(fn, M, N, K)) return rc;
-    if (M > 64) return fail(VLA_ESHAPE, fn, "M=%lld: MXFP4 weights run in the skinny kernel only (M <= 64)", (long long)M);
     REQUIRE_PTR(A);
     REQUIRE_PTR(Wq);
     OPTIONAL_PTR(bias);

@@ -353,7 +353,7 @@ hipError_t launch_skinny(const KArgs& ka, const GemmPlan& p, hipStream_t s) {
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_typed(const KArgs& ka, const GemmPlan& p, hipStream_t s) {
     if (p.kernel == 0) return launch_skinny<AT, WT, EPI>(ka, p, s);
-    if constexpr (WT == WType::FP4) return hipErrorInvalidValue;   // no wide MXFP4 kernel
+    if constexpr (WT == WType::FP4 && (AT != AType::BF16 || EPI != Epi::PLAIN)) return hipErrorInvalidValue;
     else return launch_wide<AT, WT, EPI>(ka, p, s);
 }
 
@@ -430,21 +430,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
             return skinny_plan(M, N, K, epi, 2 * nt, steps, waves, 2, at == AType::BF16);
         return skinny_plan(M, N, K, epi, nt, steps, waves, 4, at == AType::BF16);
     }
-    if (wt == WType::FP4) {   // MXFP4 weights: the skinny kernel only
-        GemmPlan p{};
-        p.kernel = 1;
-        p.ok = false;
-        return p;
-    }
     // Wide kernel: 192-row blocks; 256-column tiles when they give enough
     // workgroups, else 128-column tiles and K split until ~256 workgroups
     // (each split keeps at least 8 pipeline stages).  Wave layout: 8 waves
     // of 96 x BN/4; 64 K per stage, 128 for FP8 x FP8 on 128-column tiles
     // (FP8 x FP8 on 256-column tiles: 2048 -> 16384 at M = 768, 35.0 ->
-    // 29.7 us against 4 waves of 96 x 128).  BF16 weights
-    // always take 128-column tiles (a 256-column stage would not fit the
-    // four-stage LDS ring).  The buffer resources address A and W with
-    // 32-bit offsets.
+    // 29.7 us against 4 waves of 96 x 128).  MXFP4 weights follow FP8's
+    // choice (bf16 activations, codes converted with their block scales).
+    // BF16 weights always take 128-column tiles (a 256-column stage would
+    // not fit the four-stage LDS ring).  The buffer resources address A and
+    // W with 32-bit offsets.
     GemmPlan p{};
     p.kernel = 1;
     p.mblocks = static_cast<int>((M + 191) / 192);
@@ -453,7 +448,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
         p.groups = static_cast<int>(std::max<int64_t>(1, (tiles / 2 + 7) / 8));
     } else {
         const int64_t g256 = (tiles + 15) / 16;
-        if (wt == WType::FP8 && g256 * p.mblocks >= 192) {
+        if (wt != WType::BF16 && g256 * p.mblocks >= 192) {
             p.nt = 256;
             p.groups = static_cast<int>(g256);
         } else {
@@ -474,7 +469,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
     while (base * (ks + 1) <= 256 && kt_total / (ks + 1) >= 8) ++ks;
     p.ksplit = ks;
     const int64_t a_bytes = M * K * (at == AType::FP8 ? 1 : 2);
-    const int64_t w_bytes = N * K * (wt == WType::FP8 ? 1 : 2);
+    const int64_t w_bytes = (wt == WType::FP4) ? N * K / 2 + N * (((K >> 5) + 7) & ~int64_t(7))
+                                               : N * K * (wt == WType::FP8 ? 1 : 2);
     // split-K counters: kWideCounters per output tile
     p.ok = base * kWideCounters <= kMaxCounters && a_bytes < (int64_t(1) << 31) && w_bytes < (int64_t(1) << 31);
     return p;

@@ -3,8 +3,9 @@
 // Output tile 192 (rows of A) x BN (weight rows, 256 or 128) per workgroup
 // of 8 waves, two per SIMD, arranged 2 (rows) x 4 (columns); each wave
 // owns a 96 x BN/4 tile (3 x BN/128 accumulators of 32 x 32).  MFMA shapes
-// with the full gfx950 rate: v_mfma_f32_32x32x16_bf16 for bf16 activations (FP8 weights
-// are converted to bf16 exactly in registers) and the scaled
+// with the full gfx950 rate: v_mfma_f32_32x32x16_bf16 for bf16 activations (FP8
+// weights, and MXFP4 weights with their E8M0 block scales, are converted to
+// bf16 exactly in registers) and the scaled
 // v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit E8M0 scales) for
 // FP8 x FP8.  The packed weight tile is the MFMA "A" operand (32 output
 // channels), the activation tile the "B" operand (32 rows), so a lane's
@@ -16,10 +17,14 @@
 //  * activations row-major, 128 bytes of K per row (64 for FP8 on
 //    256-column tiles), the 16-byte chunks of each row XOR-swizzled so the
 //    32-row operand reads hit distinct banks;
-//  * weights in their packed fragment order, one 1 KiB (FP8) or 2 KiB
-//    (bf16) block per 16-row tile; FP8 blocks of odd tiles have their
-//    128-byte halves swapped, so the two 16-row halves of a 32-row operand
-//    read fall in different banks.
+//  * weights in their packed fragment order, one 1 KiB (FP8), 512-byte
+//    (MXFP4) or 2 KiB (bf16) block per 16-row tile; FP8 blocks of odd tiles
+//    have their 128-byte halves swapped (MXFP4: 64-byte halves), so the two
+//    16-row halves of a 32-row operand read fall in different banks;
+//  * MXFP4 block scales: per stage and weight sub-tile, each lane's 4-byte
+//    word of E8M0 bytes holding the stage's two blocks of its weight row,
+//    loaded into LDS with the stage's other operands (256 bytes per wave
+//    and sub-tile).
 // Out-of-range rows, tiles and the ragged K tail fall outside the buffer
 // resource and load zeros, so every wave issues the same number of loads
 // per stage.  Each stage has one barrier, placed before the stage's last
@@ -49,7 +54,7 @@ struct WideCfg {
     static constexpr int WAVES = 2 * WNW;                       // 2 along M x WNW along N
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int AB = (AT == AType::FP8) ? 1 : 2;       // activation bytes / element
-    static constexpr int WLB = (WT == WType::FP8) ? 8 : 16;     // weight bytes per lane slot
+    static constexpr int WLB = (WT == WType::FP8) ? 8 : (WT == WType::FP4 ? 4 : 16);   // weight bytes per lane slot
     static constexpr int KMF = (AT == AType::FP8) ? 64 : 16;    // K of one MFMA
     static constexpr int NKS = BK / KMF;                        // MFMA steps per stage
     static constexpr int ARB = BK * AB;                         // A bytes per row per stage
@@ -64,16 +69,23 @@ struct WideCfg {
     // a pad of the stage buffer, so every wave still issues the same loads
     static constexpr int A_SLOTS = (A_LOADS + WAVES - 1) / WAVES * WAVES;
     static constexpr int A_REGION = A_SLOTS * 1024;
-    static constexpr int STAGE = A_REGION + W_BYTES;
     static constexpr int W_LOADS = W_BYTES / 1024;
+    // weight load slots, rounded up to a multiple of the wave count the same
+    // way (MXFP4 on 128-column tiles: 4 KiB of codes, half a load per wave)
+    static constexpr int W_SLOTS = (W_LOADS + WAVES - 1) / WAVES * WAVES;
+    static constexpr int W_REGION = W_SLOTS * 1024;
+    static constexpr int S_REGION = (WT == WType::FP4) ? WAVES * (BN / WNW / 32) * 256 : 0;   // MXFP4 scales
+    static constexpr int STAGE = A_REGION + W_REGION + S_REGION;
     static constexpr int LA = A_SLOTS / WAVES;                  // activation slots per wave per stage
-    static constexpr int L = LA + W_LOADS / WAVES;              // loads per wave per stage
+    static constexpr int L = LA + W_SLOTS / WAVES;              // loads per wave per stage
     static constexpr int MSUB = 3;                              // 96-row wave tile
     static constexpr int WN = BN / WNW;                         // wave tile width
     static constexpr int NSUB = WN / 32;
-    static_assert(A_BYTES % 1024 == 0 && W_LOADS % WAVES == 0, "loads split evenly over the waves");
+    static constexpr int LV = L + (WT == WType::FP4 ? NSUB : 0);  // vector-memory ops per wave per stage
+    static_assert(A_BYTES % 1024 == 0 && W_BYTES % 1024 == 0, "whole 1 KiB loads");
     static_assert(kWideStages * STAGE <= 160 * 1024, "the stage ring fits the LDS");
-    static_assert(L <= 15, "the partial vmcnt wait fits its field");
+    static_assert(L <= 15 && 2 * LV <= 63, "the partial vmcnt waits fit their field");
+    static_assert(WT != WType::FP4 || (AT == AType::BF16 && BK == 64), "MXFP4 weights: bf16 activations, 64 K per stage");
 };
 
 // s_waitcnt immediate that waits until at most n vector-memory operations
@@ -115,7 +127,9 @@ struct Frags;
 template <WType WT, int MSUB, int NSUB>
 struct Frags<AType::BF16, WT, MSUB, NSUB> {
     u32x4_t a[MSUB];
-    typename std::conditional<WT == WType::FP8, u32x2_t, u32x4_t>::type w[NSUB];   // as read from LDS
+    typename std::conditional<WT == WType::FP8, u32x2_t,
+                              typename std::conditional<WT == WType::FP4, uint32_t, u32x4_t>::type>::type
+        w[NSUB];                                                                   // as read from LDS
     bf16x8_t wb[NSUB];                                                             // MFMA operands
 };
 template <WType WT, int MSUB, int NSUB>
@@ -182,20 +196,47 @@ void wide_gemm_kernel(KArgs a) {
             in_tail = c * (16 / C::AB) < krem;
         } else {
             const int j = q - C::A_SLOTS;
-            constexpr int PER_TILE = C::WTB / 1024;
-            const int tt = j / PER_TILE, h = j % PER_TILE;
-            const int gt = wide_wtile<EPI, BN, C::WN>(g, tt, a.N);
-            const int chunk = (WT == WType::FP8) ? (lane ^ (8 * (tt & 1))) : lane;
-            const int sb = h * 1024 + chunk * 16;               // byte within the tile's stage block
+            int tt, sb;                                         // tile slot, byte within its stage block
+            if constexpr (WT == WType::FP4) {
+                // two 512-byte tile blocks per load, odd tiles' 64-byte halves swapped
+                tt = 2 * j + (lane >> 5);
+                sb = ((lane & 31) ^ (4 * (tt & 1))) * 16;
+            } else {
+                constexpr int PER_TILE = C::WTB / 1024;
+                tt = j / PER_TILE;
+                const int chunk = (WT == WType::FP8) ? (lane ^ (8 * (tt & 1))) : lane;
+                sb = (j % PER_TILE) * 1024 + chunk * 16;
+            }
+            const int gt = (j < C::W_LOADS) ? wide_wtile<EPI, BN, C::WN>(g, tt, a.N) : -1;   // pad slots: none
             voff[t] = gt >= 0 ? static_cast<uint32_t>(gt * ksteps * 64 * C::WLB + sb) : kOOB;
             in_tail = (sb / (64 * C::WLB)) * 32 < krem;         // packed fragment within the tile
         }
         voffT[t] = in_tail ? voff[t] : kOOB;
     }
+    // MXFP4 block scales: E8M0 bytes after the codes, one row of P = K/32
+    // (rounded up to 8) bytes per weight row.  The lane's weight row of
+    // sub-tile ns is (tile slot of its 32-row operand half) * 16 + l32 % 16;
+    // stage kt's blocks 2kt, 2kt + 1 lie in the aligned word at byte
+    // 2kt & ~3 of the row, at byte 2 (kt & 1) of it.
+    const int sP = ((a.K >> 5) + 7) & ~7;
+    const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(a.W)) + static_cast<int64_t>(a.N >> 4) * ksteps * 64 * C::WLB,
+        0, a.N * sP, kRsrcWord3);
+    uint32_t svoff[C::NSUB];
+    if constexpr (WT == WType::FP4) {
+#pragma unroll
+        for (int ns = 0; ns < C::NSUB; ++ns) {
+            const int gt = wide_wtile<EPI, BN, C::WN>(g, ((wn * C::WN + ns * 32) >> 4) + ((l32 >> 4) & 1), a.N);
+            svoff[ns] = gt >= 0 ? static_cast<uint32_t>((gt * 16 + (l32 & 15)) * sP) : kOOB;
+        }
+    }
     // Loads of a stage past the range (real == false) are pushed outside the
     // resources through the scalar offset: they only write zeros into a free
     // buffer, which keeps every stage's load count and wait identical.
-    auto issue = [&](int kt, uint8_t* buf, bool real) __attribute__((always_inline)) {
+    // Stage buffer (and scale ring slot) RC.
+    auto issue = [&](auto RC, int kt, bool real) __attribute__((always_inline)) {
+        constexpr int r = decltype(RC)::value;
+        uint8_t* const buf = bufs[r];
         const bool ktail = kt == kt_total - 1;                  // uniform
         const int sA = real ? kt * C::ARB : static_cast<int>(kOOB);
         const int sW = real ? kt * C::WTB : static_cast<int>(kOOB);
@@ -203,6 +244,14 @@ void wide_gemm_kernel(KArgs a) {
         for (int t = 0; t < C::L; ++t) {
             buffer_load_lds16(t < C::LA ? rA : rW, buf + (wave + C::WAVES * t) * 1024, ktail ? voffT[t] : voff[t],
                               t < C::LA ? sA : sW);
+        }
+        if constexpr (WT == WType::FP4) {
+            const int sS = real ? ((2 * kt) & ~3) : static_cast<int>(kOOB);
+#pragma unroll
+            for (int ns = 0; ns < C::NSUB; ++ns)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rS, (__attribute__((address_space(3))) void*)(buf + C::A_REGION + C::W_REGION + (wave * C::NSUB + ns) * 256),
+                    4, svoff[ns], sS, 0, 0);
         }
     };
 
@@ -217,6 +266,8 @@ void wide_gemm_kernel(KArgs a) {
     int woff;
     if constexpr (WT == WType::BF16)
         woff = C::A_REGION + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 16 + g2 * 256;
+    else if constexpr (WT == WType::FP4)
+        woff = C::A_REGION + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 4 + (g2 ^ oddW) * 64;
     else if constexpr (AT == AType::BF16)
         woff = C::A_REGION + ((wn * C::WN) >> 4) * C::WTB + oddW * C::WTB + (l32 & 15) * 8 + (g2 ^ oddW) * 128;
     else
@@ -234,6 +285,8 @@ void wide_gemm_kernel(KArgs a) {
                 // packed fragment ks/2, K group 2(ks&1) + g2 (FP8 tiles of odd slots: 128-byte halves swapped)
                 if constexpr (WT == WType::FP8)
                     f.w[ns] = *reinterpret_cast<const u32x2_t*>(buf + woff + ns * 2 * C::WTB + ks * 256);
+                else if constexpr (WT == WType::FP4)
+                    f.w[ns] = *reinterpret_cast<const uint32_t*>(buf + woff + ns * 2 * C::WTB + ks * 128);
                 else
                     f.w[ns] = *reinterpret_cast<const u32x4_t*>(buf + woff + ns * 2 * C::WTB + ks * 512);
             }
@@ -262,13 +315,30 @@ void wide_gemm_kernel(KArgs a) {
 #pragma unroll
         for (int j = 0; j < C::MSUB; ++j) acc[i][j] = Acc{};
 
-    // weight operands as bf16 (an exact conversion for FP8 weights)
-    auto convert = [&](F& f) __attribute__((always_inline)) {
+    // weight operands as bf16 (an exact conversion for FP8 and MXFP4
+    // weights); f holds step ks of K tile kt, staged in buffer RC.  MXFP4:
+    // step ks uses block ks / 2 of the tile's two; their scales are read
+    // from the buffer's scale area with step 0 (every step of a tile is
+    // converted after its step 0 and before the next tile's)
+    float sf[C::NSUB][2];
+    auto convert = [&](F& f, auto RC, int kt, int ks) __attribute__((always_inline)) {
         if constexpr (AT == AType::BF16) {
 #pragma unroll
             for (int ns = 0; ns < C::NSUB; ++ns) {
-                if constexpr (WT == WType::FP8) f.wb[ns] = ocp8_to_bf16x8(f.w[ns]);
-                else f.wb[ns] = as_bf16x8(f.w[ns]);
+                if constexpr (WT == WType::FP8) {
+                    f.wb[ns] = ocp8_to_bf16x8(f.w[ns]);
+                } else if constexpr (WT == WType::FP4) {
+                    if (ks == 0) {
+                        const uint32_t sw = *reinterpret_cast<const uint32_t*>(
+                            bufs[decltype(RC)::value] + C::A_REGION + C::W_REGION + (wave * C::NSUB + ns) * 256 + lane * 4);
+                        const uint32_t pair = sw >> (16 * (kt & 1));
+                        sf[ns][0] = e8m0_to_f32(pair & 0xFFu);
+                        sf[ns][1] = e8m0_to_f32((pair >> 8) & 0xFFu);
+                    }
+                    f.wb[ns] = fp4_to_bf16x8(f.w[ns], sf[ns][ks >> 1]);
+                } else {
+                    f.wb[ns] = as_bf16x8(f.w[ns]);
+                }
             }
         }
     };
@@ -327,7 +397,7 @@ void wide_gemm_kernel(KArgs a) {
                 __builtin_amdgcn_s_setprio(1);
                 mfmas(cf, 0, NM);
                 __builtin_amdgcn_s_setprio(0);
-                convert(of);
+                convert(of, UC, kt_begin + i, ks + 1);
 #pragma unroll
                 for (int j = 0; j < HALF; ++j) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
@@ -345,16 +415,16 @@ void wide_gemm_kernel(KArgs a) {
                 mfmas(cf, 0, HALF);
                 __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * C::L));
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * C::LV));
                 __builtin_amdgcn_s_barrier();
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 __builtin_amdgcn_sched_barrier(0);
                 read_step(bufs[(u + 1) % S], 0, of);
-                issue(kt_begin + i + S - 1, bufs[(u + S - 1) % S], i + S - 1 < nkt);
+                issue(std::integral_constant<int, (u + S - 1) % S>{}, kt_begin + i + S - 1, i + S - 1 < nkt);
                 __builtin_amdgcn_s_setprio(1);
                 mfmas(cf, HALF, NM);
                 __builtin_amdgcn_s_setprio(0);
-                convert(of);
+                convert(of, std::integral_constant<int, (u + 1) % S>{}, kt_begin + i + 1, 0);
 #pragma unroll
                 for (int j = HALF; j < NM; ++j) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads
@@ -367,13 +437,14 @@ void wide_gemm_kernel(KArgs a) {
         }
     };
     if (nkt > 0) {
-#pragma unroll
-        for (int j = 0; j < S - 1; ++j) issue(kt_begin + j, bufs[j], j < nkt);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * C::L));
+        issue(std::integral_constant<int, 0>{}, kt_begin, 0 < nkt);
+        issue(std::integral_constant<int, 1>{}, kt_begin + 1, 1 < nkt);
+        issue(std::integral_constant<int, 2>{}, kt_begin + 2, 2 < nkt);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * C::LV));
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         read_step(lds0, 0, f0);
-        convert(f0);
+        convert(f0, std::integral_constant<int, 0>{}, kt_begin, 0);
         const int full = nkt & ~(S - 1);
         for (int i0 = 0; i0 < full; i0 += S) {
             stage(std::integral_constant<int, 0>{}, i0);
@@ -617,6 +688,7 @@ size_t wide_part_bytes(const GemmPlan& p) {
 #define VLA_WIDE_BF16W(X) X(128, 4, 64)
 #define VLA_WIDE_FP8A(X) X(256, 4, 64) X(128, 4, 128)
 #define VLA_WIDE_BF16A(X) X(256, 4, 64) X(128, 4, 64)
+#define VLA_WIDE_FP4W(X) X(256, 4, 64) X(128, 4, 64)
 
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStream_t s) {
@@ -630,6 +702,8 @@ hipError_t launch_wide(const gemm_detail::KArgs& ka, const GemmPlan& p, hipStrea
         VLA_WIDE_GELU(VLA_WIDE)
     } else if constexpr (WT == WType::BF16) {
         VLA_WIDE_BF16W(VLA_WIDE)
+    } else if constexpr (WT == WType::FP4) {
+        VLA_WIDE_FP4W(VLA_WIDE)
     } else if constexpr (AT == AType::FP8) {
         VLA_WIDE_FP8A(VLA_WIDE)
     } else {
@@ -648,6 +722,9 @@ bool wide_dispatchable(const GemmPlan& p, AType at, WType wt, Epi epi) {
     } else if (wt == WType::BF16) {
         if (at != AType::BF16) return false;
         VLA_WIDE_BF16W(VLA_WIDE)
+    } else if (wt == WType::FP4) {
+        if (at != AType::BF16) return false;
+        VLA_WIDE_FP4W(VLA_WIDE)
     } else if (at == AType::FP8) {
         VLA_WIDE_FP8A(VLA_WIDE)
     } else {
@@ -661,5 +738,6 @@ template hipError_t launch_wide<AType::BF16, WType::FP8, Epi::PLAIN>(const gemm_
 template hipError_t launch_wide<AType::BF16, WType::FP8, Epi::GELU_MUL>(const gemm_detail::KArgs&, const GemmPlan&, hipStream_t);
 template hipError_t launch_wide<AType::BF16, WType::BF16, Epi::PLAIN>(const gemm_detail::KArgs&, const GemmPlan&, hipStream_t);
 template hipError_t launch_wide<AType::FP8, WType::FP8, Epi::PLAIN>(const gemm_detail::KArgs&, const GemmPlan&, hipStream_t);
+template hipError_t launch_wide<AType::BF16, WType::FP4, Epi::PLAIN>(const gemm_detail::KArgs&, const GemmPlan&, hipStream_t);
 
 }  // namespace vla

@@ -254,9 +254,11 @@ int vla_gemm_fp8w_gelu_mul(const uint16_t *A, const uint8_t *Wgu, const float *s
  * 4-bit weights ("FlashRT: an inference engine for real-time robot
  * control", section 7.2) in the OCP MX form; the kernel converts each code
  * to bf16 with its block scale in one gfx950 instruction per pair, exactly,
- * and streams half the bytes of FP8.  The skinny kernel only: M <= 64, else
- * VLA_ESHAPE.  Wq from vla_quantize_pack(..., VLA_WFMT_MXFP4, VLA_LAYOUT_MFMA);
- * workspace vla_gemm_workspace_bytes(M, N, K, VLA_WFMT_MXFP4). */
+ * and streams half the bytes of FP8.  Any M: M <= 64 runs the skinny kernel,
+ * larger M the wide one (the section's 4-bit encoder FFN shapes), which
+ * stages each K tile's E8M0 bytes beside its codes.  Wq from
+ * vla_quantize_pack(..., VLA_WFMT_MXFP4, VLA_LAYOUT_MFMA); workspace
+ * vla_gemm_workspace_bytes(M, N, K, VLA_WFMT_MXFP4). */
 int vla_gemm_mxfp4w(const uint16_t *A, const uint8_t *Wq, const uint16_t *bias, const uint16_t *residual,
                     uint16_t *Y, void *ws, size_t ws_bytes, int64_t M, int64_t N, int64_t K, void *stream);
 

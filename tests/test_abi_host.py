@@ -122,10 +122,13 @@ def test_mxfp4_errors(lib):
     assert vla.vla_packed_bytes(64, 1024, vla.VLA_WFMT_MXFP4) == 64 * 1024 // 2 + 64 * 32
     assert rc_of("vla_quantize_pack", A16, A16, A16, 64, 128, vla.VLA_WFMT_MXFP4, 1, None) == vla.VLA_EINVAL   # scales given
     assert rc_of("vla_quantize_pack", A16, A16, None, 64, 128, vla.VLA_WFMT_MXFP4, 0, None) == vla.VLA_EINVAL  # row-major
-    assert rc_of("vla_gemm_mxfp4w", A16, A16, None, None, A16, A16, 1 << 20, 65, 1024, 1024, None) == vla.VLA_ESHAPE
+    assert rc_of("vla_gemm_mxfp4w", A16, A16, None, None, A16, A16, 1 << 20, 65, 1024, 1000, None) == vla.VLA_ESHAPE
     assert rc_of("vla_gemm_mxfp4w", A16, A16, None, None, A16, A16, 0, 50, 1024, 1024, None) == vla.VLA_EWORKSPACE
     assert vla.vla_gemm_supported(50, 4096, 1024, vla.VLA_WFMT_MXFP4) == 0
-    assert vla.vla_gemm_supported(100, 4096, 1024, vla.VLA_WFMT_MXFP4) == vla.VLA_ESHAPE
+    # M > 64 runs the wide kernel
+    assert vla.vla_gemm_supported(100, 4096, 1024, vla.VLA_WFMT_MXFP4) == 0
+    assert vla.vla_gemm_supported(768, 2048, 16384, vla.VLA_WFMT_MXFP4) == 0
+    assert vla.vla_gemm_supported(768, 16384, 2048, vla.VLA_WFMT_MXFP4) == 0
     assert vla.vla_gemm_supported(50, 4096, 1024, vla.VLA_WFMT_MXFP4, gelu_mul=True) == vla.VLA_EINVAL
     assert vla.vla_gemm_workspace_bytes(10, 1024, 4096, vla.VLA_WFMT_MXFP4) >= 65536
 

@@ -1,8 +1,8 @@
 """GPU parity of the MXFP4 weight path: quantize + pack (codes and E8M0 block
-scales) byte for byte against the oracle, and the skinny GEMM on MXFP4
-weights against the oracle's fp64 GEMM on the dequantized weights
-(|y - y_ref| <= 4e-3 * sum |a w|), with a one-hot lane-map probe that must
-reproduce A's columns bit for bit."""
+scales) byte for byte against the oracle, and the skinny (M <= 64) and wide
+GEMMs on MXFP4 weights against the oracle's fp64 GEMM on the dequantized
+weights (|y - y_ref| <= 4e-3 * sum |a w|), with one-hot lane-map probes that
+must reproduce A's columns bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -114,3 +114,56 @@ def test_mxfp4_lane_map_one_hot():
     A = synthetic.activations(M, K, 9801)
     y = run(A, Mx(W), M)
     assert np.array_equal(y, A[:, perm])
+
+
+# ------------------------------------------------------------- wide kernel
+
+@pytest.mark.parametrize("M", [65, 200, 571])
+@pytest.mark.parametrize("N,K", [(272, 1056), (512, 2048), (4096, 1024)])
+def test_mxfp4_wide_gemm_matches_oracle(M, N, K):
+    """M > 64 runs the wide kernel: 256-column tiles, E8M0 scales staged per
+    K tile; ragged N (272) and a K tile holding one real block (1056 = 16.5
+    tiles of 64) included."""
+    print(f"mxfp4 wide gemm M={M} N={N} K={K}", flush=True)
+    A = synthetic.activations(M, K, 9900 + M)
+    mx = Mx(special_weights(N, K, 9910 + N))
+    y = run(A, mx, M)
+    ref, yabs = oracle.gemm(bf16_f64(A), mx.w)
+    assert_gemm_close(y, ref, yabs)
+
+
+def test_mxfp4_wide_lane_map_one_hot():
+    M, N, K = 300, 512, 1024
+    perm = synthetic.rng(9920).permutation(K)[:N]
+    W = np.zeros((N, K), np.float32)
+    W[np.arange(N), perm] = 1.0
+    A = synthetic.activations(M, K, 9921)
+    y = run(A, Mx(W), M)
+    assert np.array_equal(y, A[:, perm])
+
+
+def test_mxfp4_wide_bias_and_residual():
+    M, N, K = 300, 768, 2048
+    A = synthetic.activations(M, K, 9930)
+    mx = Mx(synthetic.weights(N, K, 9931))
+    b = synthetic.activations(1, N, 9932)[0]
+    r = synthetic.activations(M, N, 9933)
+    y = run(A, mx, M, bias=dev(b), resid=dev(r))
+    ref, yabs = oracle.gemm(bf16_f64(A), mx.w, bf16_f64(b))
+    yv, rv = bf16_f64(y), bf16_f64(r)
+    assert np.all(np.abs(yv - (rv + ref)) <= 4e-3 * (yabs + np.abs(rv)) + 2.0 ** -8 * np.abs(rv + ref) + 1e-30)
+
+
+@pytest.mark.parametrize("N,K", [(16384, 2048), (2048, 16384)])
+def test_mxfp4_wide_full_size_sampled(N, K):
+    """The encoder shapes at M = 768 in the launch configuration the bench
+    times (the 16384-deep one splits K across workgroups); sampled rows
+    against the oracle."""
+    M = 768
+    print(f"mxfp4 wide full M={M} N={N} K={K}", flush=True)
+    A = synthetic.activations(M, K, 9940)
+    mx = Mx(synthetic.weights(N, K, 9941))
+    y = run(A, mx, M)
+    rows = np.array([0, 1, 191, 192, 383, 500, 766, 767])
+    ref, yabs = oracle.gemm(bf16_f64(A[rows]), mx.w)
+    assert_gemm_close(y[rows], ref, yabs)
