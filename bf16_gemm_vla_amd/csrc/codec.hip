@@ -332,7 +332,39 @@ __global__ __launch_bounds__(NT) void quantize_rows_reg_kernel(const float* __re
     }
 }
 
-// Row-major FP8 -> MFMA layout: one thread per 8-byte slot.
+// Row-major FP8 -> MFMA layout through LDS, one workgroup per 16-row tile
+// (K <= 8192: the tile's 16 K bytes fit in LDS): 16-byte chunks are read
+// with the row fastest across lanes (a wave covers 64 bytes of each of the
+// 16 rows), each chunk's two 8-byte slots are written to their place in the
+// tile's packed order in LDS (the 16 rows' slots of one K group are 128
+// contiguous bytes, so these writes do not collide in banks), and the tile
+// then leaves as one contiguous block.
+// The tile occupies the same bytes in both layouts and every byte of it is
+// read before any is written.
+constexpr int kPackMaxK = 8192;
+
+__global__ __launch_bounds__(kThreads) void pack_fp8_tile_kernel(const uint8_t* __restrict__ q,
+                                                                 uint8_t* __restrict__ qp, int64_t K) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t tile[];   // 16 K bytes
+    const int64_t n0 = blockIdx.x;
+    const uint8_t* src = q + n0 * 16 * K;
+    const int cpr = static_cast<int>(K >> 4);        // 16-byte chunks per row
+    const int chunks = 16 * cpr;
+    for (int c = threadIdx.x; c < chunks; c += kThreads) {
+        const int n1 = c & 15, j = c >> 4;          // row, chunk along the row (k = 16 j ..)
+        const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(n1) * K + j * 16);
+        const int k0 = j >> 1, k1 = (j & 1) * 2;    // slots (k0, k1, n1) and (k0, k1 + 1, n1)
+        const int o = ((k0 * 64 + 16 * k1 + n1) * 8);
+        *reinterpret_cast<uint2*>(tile + o) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2*>(tile + o + 128) = make_uint2(v.z, v.w);
+    }
+    __syncthreads();
+    uint8_t* dst = qp + n0 * 16 * K;
+    for (int c = threadIdx.x; c < chunks; c += kThreads)
+        *reinterpret_cast<uint4*>(dst + c * 16) = *reinterpret_cast<const uint4*>(tile + c * 16);
+}
+
+// Row-major FP8 -> MFMA layout: one thread per 8-byte slot (K > 8192).
 __global__ __launch_bounds__(kThreads) void pack_fp8_kernel(const uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ qp, int64_t N,
                                                             int64_t K) {
@@ -715,6 +747,10 @@ hipError_t launch_mxfp4_quantize_pack(const float* W, uint8_t* Wq, int64_t N, in
 }
 
 hipError_t launch_pack_fp8(const uint8_t* q, uint8_t* qp, int64_t N, int64_t K, hipStream_t s) {
+    if (K <= kPackMaxK) {
+        pack_fp8_tile_kernel<<<static_cast<unsigned>(N / 16), kThreads, static_cast<size_t>(16 * K), s>>>(q, qp, K);
+        return hipGetLastError();
+    }
     const int64_t total = N * K / 8;
     const int64_t blocks = (total + kThreads - 1) / kThreads;
     const unsigned grid = static_cast<unsigned>(blocks < 65536 ? blocks : 65536);

@@ -149,9 +149,10 @@ def test_reencode_j1_rows_and_in_place(layout, K):
     assert np.array_equal(host(ds), ref_s)
 
 
-def test_pack_fp8_matches_oracle():
-    g = synthetic.rng(4243)
-    N, K = 80, 160
+@pytest.mark.parametrize("N,K", [(80, 160), (32, 8192), (16, 8224), (48, 32)])
+def test_pack_fp8_matches_oracle(N, K):
+    """K up to 8192 packs a tile through LDS, longer rows slot by slot."""
+    g = synthetic.rng(4243 + K)
     q = g.integers(0, 256, (N, K)).astype(np.uint8)
     out = Guarded(N * K)
     vla.vla_pack_fp8(dev(q), out.t, N, K)
