@@ -110,28 +110,33 @@ __device__ __forceinline__ uint2 encode8_quotient(const float v[8], float sc, fl
     return make_uint2(o[0], o[1]);
 }
 
-// One workgroup per 16-row tile.  Phase 1: row absmax -> scale.  Phase 2:
-// each thread encodes 8-value slots (reads 2 x 16 B, writes 8 B / 16 B).
-template <int WFMT>
-__global__ __launch_bounds__(kThreads) void quantize_pack_kernel(const float* __restrict__ W,
-                                                                 void* __restrict__ Wq,
-                                                                 float* __restrict__ scales,
-                                                                 int64_t K, int layout) {
+// One workgroup of NT threads per 16-row tile (any K; the second read of
+// the tile mostly hits L2).  Phase 1: row absmax -> scale.  Phase 2: each
+// thread encodes 8-value slots (reads 2 x 16 B, writes 8 B / 16 B).  NT =
+// 1024 keeps 16 waves' loads in flight per tile: a 2048 x 16384 matrix has
+// only 128 tiles.
+template <int WFMT, int NT>
+__global__ __launch_bounds__(NT) void quantize_pack_kernel(const float* __restrict__ W,
+                                                           void* __restrict__ Wq,
+                                                           float* __restrict__ scales,
+                                                           int64_t K, int layout) {
+    constexpr int TPR = NT / 16;                 // threads per row in phase 1
     __shared__ float s_scale[16];
     const int64_t n0 = blockIdx.x;
     const int t = threadIdx.x;
     const float* tile = W + n0 * 16 * K;
 
     if (WFMT != VLA_WFMT_BF16) {
-        // 16 threads per row, float4 loads strided by 64 floats
-        const int r = t >> 4, c = t & 15;
+        // TPR threads per row, float4 loads strided by 4 TPR floats
+        const int r = t / TPR, c = t % TPR;
         const float* row = tile + static_cast<int64_t>(r) * K;
         float m = 0.0f;
-        for (int64_t k = 4 * c; k < K; k += 64) {
+#pragma unroll 4
+        for (int64_t k = 4 * c; k < K; k += 4 * TPR) {
             float4 v = *reinterpret_cast<const float4*>(row + k);
             m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
         }
-        m = group_max<16>(m);
+        m = group_max<TPR>(m);
         if (c == 0) {
             const float maxv = (WFMT == VLA_WFMT_E4M3_FNUZ) ? 240.0f : 448.0f;
             const float sc = (m == 0.0f) ? 1.0f : __fdiv_rn(m, maxv);
@@ -142,7 +147,10 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(const float* __
     }
 
     const int64_t nslots = (K >> 5) * 64;
-    for (int64_t slot = t; slot < nslots; slot += kThreads) {
+    // slot % 64 = t % 64: the thread's row n1 and its scale stay fixed
+    const float sc = (WFMT == VLA_WFMT_BF16) ? 1.0f : s_scale[t & 15];
+    const float rcp = __fdiv_rn(1.0f, sc);
+    for (int64_t slot = t; slot < nslots; slot += NT) {
         const int64_t k0 = slot >> 6;
         const int lane = static_cast<int>(slot & 63), k1 = lane >> 4, n1 = lane & 15;
         const float* src = tile + static_cast<int64_t>(n1) * K + k0 * 32 + k1 * 8;
@@ -158,9 +166,8 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(const float* __
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Wq) + off) =
                 make_uint4(w[0], w[1], w[2], w[3]);
         } else {
-            const float sc = s_scale[n1];
             *reinterpret_cast<uint2*>(static_cast<uint8_t*>(Wq) + off) =
-                encode8_quotient<WFMT == VLA_WFMT_E4M3_FNUZ>(v, sc, __fdiv_rn(1.0f, sc));
+                encode8_quotient<WFMT == VLA_WFMT_E4M3_FNUZ>(v, sc, rcp);
         }
     }
 }
@@ -190,7 +197,8 @@ __device__ __forceinline__ uint32_t encode_e2m1(float v) {
 // the low nibble) in the FP8 fragment order; the E8M0 scale bytes follow all
 // codes, row-major with rows padded to P = K/32 rounded up to 8 bytes (pad
 // bytes 127): byte N*K/2 + n * P + k0, so a wave's consecutive K steps of one
-// row are one aligned load.
+// row are one aligned load.  Blocks are independent, so a tile's blocks are
+// shared among gridDim.y workgroups (enough workgroups for few, long rows).
 __global__ __launch_bounds__(kThreads) void mxfp4_quantize_pack_kernel(const float* __restrict__ W,
                                                                        uint8_t* __restrict__ Wq, int64_t N,
                                                                        int64_t K) {
@@ -198,7 +206,8 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quantize_pack_kernel(const flo
     const int64_t ksteps = K >> 5;
     const int64_t P = mxfp4_scale_row_bytes(K);
     uint8_t* const sc_base = Wq + N * K / 2;
-    for (int64_t b = threadIdx.x; b < P * 16; b += kThreads) {
+    for (int64_t b = blockIdx.y * static_cast<int64_t>(kThreads) + threadIdx.x; b < P * 16;
+         b += static_cast<int64_t>(gridDim.y) * kThreads) {
         const int64_t k0 = b >> 4;
         const int n1 = static_cast<int>(b & 15);
         if (k0 >= ksteps) {   // row padding
@@ -729,20 +738,25 @@ hipError_t launch_quantize_pack(const float* W, void* Wq, float* scales, int64_t
     }
     switch (wfmt) {
         case VLA_WFMT_BF16:
-            quantize_pack_kernel<VLA_WFMT_BF16><<<grid, kThreads, 0, s>>>(W, Wq, scales, K, layout);
+            quantize_pack_kernel<VLA_WFMT_BF16, 1024><<<grid, 1024, 0, s>>>(W, Wq, scales, K, layout);
             break;
         case VLA_WFMT_E4M3_OCP:
-            quantize_pack_kernel<VLA_WFMT_E4M3_OCP><<<grid, kThreads, 0, s>>>(W, Wq, scales, K, layout);
+            quantize_pack_kernel<VLA_WFMT_E4M3_OCP, 1024><<<grid, 1024, 0, s>>>(W, Wq, scales, K, layout);
             break;
         default:
-            quantize_pack_kernel<VLA_WFMT_E4M3_FNUZ><<<grid, kThreads, 0, s>>>(W, Wq, scales, K, layout);
+            quantize_pack_kernel<VLA_WFMT_E4M3_FNUZ, 1024><<<grid, 1024, 0, s>>>(W, Wq, scales, K, layout);
             break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_mxfp4_quantize_pack(const float* W, uint8_t* Wq, int64_t N, int64_t K, hipStream_t s) {
-    mxfp4_quantize_pack_kernel<<<static_cast<unsigned>(N / 16), kThreads, 0, s>>>(W, Wq, N, K);
+    // split each tile's 16 P blocks over enough workgroups for ~1024 in all
+    const int64_t tiles = N / 16;
+    const int64_t per_tile = (mxfp4_scale_row_bytes(K) * 16 + kThreads - 1) / kThreads;
+    const int64_t ys = std::max<int64_t>(1, std::min<int64_t>(per_tile, (1024 + tiles - 1) / tiles));
+    mxfp4_quantize_pack_kernel<<<dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(ys)), kThreads, 0, s>>>(
+        W, Wq, N, K);
     return hipGetLastError();
 }
 
