@@ -423,10 +423,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
             waves = 8;
             steps = chunk <= 16 ? 2 : 4;
         }
-        // FP8 weights, plain epilogue, more than 32 rows: two 16-column tiles
-        // x two row halves per workgroup read 36% fewer bytes per CU than one
-        // tile x all rows (the 1024 -> 4096 up-projection: 5.4 -> 5.1 us)
-        if (wt != WType::BF16 && epi == Epi::PLAIN && mt_total > 2 && steps == 4)
+        // FP8 weights, more than 32 rows: two 16-column tiles (two gate/up
+        // pairs for the fused epilogue) x two row halves per workgroup read
+        // 36% fewer bytes per CU than one tile (pair) x all rows (the
+        // 1024 -> 4096 up-projection: 5.4 -> 5.1 us)
+        if (wt != WType::BF16 && mt_total > 2 && steps == 4)
             return skinny_plan(M, N, K, epi, 2 * nt, steps, waves, 2, at == AType::BF16);
         return skinny_plan(M, N, K, epi, nt, steps, waves, 4, at == AType::BF16);
     }
