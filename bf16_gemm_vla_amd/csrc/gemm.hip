@@ -328,7 +328,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
     X(4, 1, 8, 4) X(4, 2, 8, 4) X(4, 2, 4, 4) X(4, 4, 4, 4)                                              \
     X(1, 2, 8, 1) X(1, 4, 8, 1) X(1, 4, 16, 1) X(1, 8, 16, 1)                                            \
     X(2, 2, 8, 1) X(2, 4, 8, 1) X(2, 4, 16, 1) X(2, 8, 16, 1)                                            \
-    X(2, 4, 8, 2) X(4, 4, 8, 2) X(4, 4, 8, 1) X(8, 4, 8, 1)
+    X(2, 4, 8, 2) X(4, 4, 8, 2) X(4, 4, 8, 1) X(8, 4, 8, 1) X(2, 2, 16, 2)
 
 template <AType AT, WType WT, Epi EPI>
 hipError_t launch_skinny(const KArgs& ka, const GemmPlan& p, hipStream_t s) {
@@ -426,8 +426,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
         // FP8 weights, more than 32 rows: two 16-column tiles (two gate/up
         // pairs for the fused epilogue) x two row halves per workgroup read
         // 36% fewer bytes per CU than one tile (pair) x all rows (the
-        // 1024 -> 4096 up-projection: 5.4 -> 5.1 us)
-        if (wt != WType::BF16 && mt_total > 2 && steps == 4)
+        // 1024 -> 4096 up-projection: 5.4 -> 5.1 us); BF16 weights the same
+        // with their 16 waves x 2 steps.  The fused epilogue needs an even
+        // number of gate tiles (a group never straddles the gate/up halves).
+        if (mt_total > 2 && ((wt != WType::BF16 && steps == 4) || (wt == WType::BF16 && steps == 2)) &&
+            (epi == Epi::PLAIN || (tiles / 2) % 2 == 0))
             return skinny_plan(M, N, K, epi, 2 * nt, steps, waves, 2, at == AType::BF16);
         return skinny_plan(M, N, K, epi, nt, steps, waves, 4, at == AType::BF16);
     }

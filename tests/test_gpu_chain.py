@@ -40,7 +40,8 @@ class ChainWeights:
             self.o_d.append(c); self.o_sd.append(d)
 
 
-@pytest.mark.parametrize("M,I,K", [(50, 4096, 1024), (4, 64, 128), (17, 48, 96), (300, 256, 512)])
+@pytest.mark.parametrize("M,I,K", [(50, 4096, 1024), (4, 64, 128), (17, 48, 96), (300, 256, 512),
+                                   (33, 4112, 1024), (40, 4128, 1024)])
 def test_gelu_mul_stage(M, I, K):
     print(f"gelu_mul M={M} I={I} K={K}", flush=True)
     cw = ChainWeights(1, K, I, seed=M, with_down=False)

@@ -140,6 +140,14 @@ def test_skinny_configs(wfmt, N, K):
     check(50, N, K, wfmt, synthetic.IDS["skinny.up.A"] if N == 4096 else synthetic.IDS["skinny.down.A"])
 
 
+@pytest.mark.parametrize("wfmt", [vla.VLA_WFMT_E4M3_OCP, vla.VLA_WFMT_BF16])
+@pytest.mark.parametrize("M,N", [(33, 4112), (64, 4096), (40, 8224)])
+def test_two_tiles_row_halves(wfmt, M, N):
+    """More than 32 rows and >= 256 column tiles: workgroups of two column
+    tiles x half the rows, with a ragged last group and a one-row half."""
+    check(M, N, 1024, wfmt, 6400 + M + N)
+
+
 @pytest.mark.parametrize("M", [1, 10, 16, 17, 33, 64, 65, 100, 129, 571])
 def test_ragged_rows(M):
     check(M, 96, 160, vla.VLA_WFMT_E4M3_OCP, 6000 + M)
