@@ -341,6 +341,56 @@ __global__ __launch_bounds__(NT) void quantize_rows_reg_kernel(const float* __re
     }
 }
 
+// The row mapping of quantize_rows_reg_kernel (one row per wave, 1024
+// threads, K a multiple of 512 up to 4096) for the MFMA layout: each lane's
+// 8 codes (row r, k = 512 c + 8 l) are one slot (k0 = k / 32, k1 = l % 4,
+// n1 = r), placed in LDS in the tile's packed order with the row index
+// XOR-ed by k0 % 16 (without it the 16 k0 slots a wave writes fall in two
+// banks), and the tile then leaves as one contiguous block, each lane
+// reading a 16-byte slot pair (n1 even, odd) and swapping its halves when
+// the XOR reversed them.  Reads of the weights are contiguous runs of a row
+// instead of 16 rows x 32 bytes per wave.
+template <int WFMT, int SPT>
+__global__ __launch_bounds__(1024) void quantize_rows_packed_kernel(const float* __restrict__ W,
+                                                                    uint8_t* __restrict__ Wq,
+                                                                    float* __restrict__ scales, int64_t K) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t ptile[];   // 16 K bytes
+    const int64_t n0 = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, r = t >> 6;
+    const float* row = W + (n0 * 16 + r) * K;
+    float4 a[SPT], b[SPT];
+#pragma unroll
+    for (int c = 0; c < SPT; ++c) {
+        a[c] = *reinterpret_cast<const float4*>(row + c * 512 + lane * 8);
+        b[c] = *reinterpret_cast<const float4*>(row + c * 512 + lane * 8 + 4);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < SPT; ++c)
+        m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a[c].x), fabsf(a[c].y)), fmaxf(fabsf(a[c].z), fabsf(a[c].w))),
+                           fmaxf(fmaxf(fabsf(b[c].x), fabsf(b[c].y)), fmaxf(fabsf(b[c].z), fabsf(b[c].w)))));
+    m = wave_max(m);
+    const float maxv = (WFMT == VLA_WFMT_E4M3_FNUZ) ? 240.0f : 448.0f;
+    const float sc = (m == 0.0f) ? 1.0f : __fdiv_rn(m, maxv);
+    if (lane == 0) scales[n0 * 16 + r] = sc;
+    const float rcp = __fdiv_rn(1.0f, sc);
+#pragma unroll
+    for (int c = 0; c < SPT; ++c) {
+        const float v[8] = {a[c].x, a[c].y, a[c].z, a[c].w, b[c].x, b[c].y, b[c].z, b[c].w};
+        const int k0 = 16 * c + (lane >> 2), k1 = lane & 3;
+        *reinterpret_cast<uint2*>(ptile + (k0 * 64 + 16 * k1 + (r ^ (k0 & 15))) * 8) =
+            encode8_quotient<WFMT == VLA_WFMT_E4M3_FNUZ>(v, sc, rcp);
+    }
+    __syncthreads();
+    uint8_t* dst = Wq + n0 * 16 * K;
+    for (int x = t; x < K; x += 1024) {            // 16-byte output chunk x = slots 2x, 2x + 1
+        const int slot = 2 * x, k0 = slot >> 6, k1 = (slot >> 4) & 3, n1 = slot & 15, sw = k0 & 15;
+        uint4 v = *reinterpret_cast<const uint4*>(ptile + (k0 * 64 + 16 * k1 + ((n1 ^ sw) & ~1)) * 8);
+        if (sw & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+        *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(x) * 16) = v;
+    }
+}
+
 // Row-major FP8 -> MFMA layout through LDS, one workgroup per 16-row tile
 // (K <= 8192: the tile's 16 K bytes fit in LDS): 16-byte chunks are read
 // with the row fastest across lanes (a wave covers 64 bytes of each of the
@@ -700,8 +750,8 @@ __global__ __launch_bounds__(kThreads) void act_encode_kernel(const uint16_t* __
 hipError_t launch_quantize_pack(const float* W, void* Wq, float* scales, int64_t N, int64_t K,
                                 int wfmt, int layout, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(N / 16));
-    // K a multiple of 512 up to 4096: 1024 threads per tile (one row per
-    // wave in the row-major kernel), K / 512 slots per thread
+    // K a multiple of 512 up to 4096: 1024 threads per tile, one row per
+    // wave, K / 512 slots per thread (the MFMA layout through LDS)
     if (wfmt != VLA_WFMT_BF16 && K % 512 == 0 && K <= 4096) {
         const int spt = static_cast<int>(K / 512);
         uint8_t* q = static_cast<uint8_t*>(Wq);
@@ -712,9 +762,9 @@ hipError_t launch_quantize_pack(const float* W, void* Wq, float* scales, int64_t
             else if (layout == 0)                                                                      \
                 quantize_rows_reg_kernel<VLA_WFMT_E4M3_FNUZ, SPT_, 1024><<<grid, 1024, 0, s>>>(W, q, scales, K); \
             else if (wfmt == VLA_WFMT_E4M3_OCP)                                                        \
-                quantize_pack_reg_kernel<VLA_WFMT_E4M3_OCP, SPT_, 1024><<<grid, 1024, 0, s>>>(W, q, scales, K, layout); \
+                quantize_rows_packed_kernel<VLA_WFMT_E4M3_OCP, SPT_><<<grid, 1024, 16 * K, s>>>(W, q, scales, K); \
             else                                                                                       \
-                quantize_pack_reg_kernel<VLA_WFMT_E4M3_FNUZ, SPT_, 1024><<<grid, 1024, 0, s>>>(W, q, scales, K, layout); \
+                quantize_rows_packed_kernel<VLA_WFMT_E4M3_FNUZ, SPT_><<<grid, 1024, 16 * K, s>>>(W, q, scales, K); \
             return hipGetLastError();                                                                  \
         }
         VLA_Q1K(1) VLA_Q1K(2) VLA_Q1K(3) VLA_Q1K(4) VLA_Q1K(5) VLA_Q1K(6) VLA_Q1K(7) VLA_Q1K(8)
