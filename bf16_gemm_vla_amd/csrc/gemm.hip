@@ -92,10 +92,13 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
 
     using L = SkinnyLds<WAVES, S, MT>;
     constexpr int RED_BYTES = WAVES * NT * MT * 64 * 16;
-    constexpr int LDS_BYTES = (ALDS && L::BYTES > RED_BYTES) ? L::BYTES : RED_BYTES;
-    static_assert(LDS_BYTES <= 160 * 1024, "the workgroup's LDS fits");
+    // the reduction area follows the activation chunk when both fit, so the
+    // partial sums need not wait for every wave to finish its LDS reads
+    constexpr bool SEPARATE = ALDS && (L::BYTES + RED_BYTES <= 160 * 1024);
+    constexpr int LDS_BYTES = SEPARATE ? L::BYTES + RED_BYTES : ((ALDS && L::BYTES > RED_BYTES) ? L::BYTES : RED_BYTES);
+    static_assert(LDS_BYTES <= 160 * 1024 && L::BYTES % 16 == 0, "the workgroup's LDS fits");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-    auto red = reinterpret_cast<f32x4_t(*)[NT][MT][64]>(lds);
+    auto red = reinterpret_cast<f32x4_t(*)[NT][MT][64]>(lds + (SEPARATE ? L::BYTES : 0));
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = blockIdx.x, split = blockIdx.y, mh = blockIdx.z;
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm_kernel(KArgs a) {
                     acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w_operand<WT>(wf[s][j]), bop, acc[j][mt], 0, 0, 0);
         }
     }
-    if constexpr (ALDS) __syncthreads();   // activation reads done before LDS is reused
+    if constexpr (ALDS && !SEPARATE) __syncthreads();   // activation reads done before LDS is reused
     // 5. cross-wave reduction through LDS with one barrier: every wave
     //    publishes its K slice, then wave w sums fragments w, w+WAVES, ...
     //    over all waves in wave order (bitwise repeatable)
