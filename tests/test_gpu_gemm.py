@@ -301,9 +301,10 @@ def test_concurrent_streams_with_separate_workspaces():
 
 
 def test_graph_replays_equal_eager():
-    """Split-K skinny and wide GEMMs (and the fused gate/up GEMM) captured in
-    one HIP graph: every replay, with other eager work and synchronizations
-    between replays, equals the eager results bit for bit."""
+    """Split-K skinny and wide GEMMs (FP8 and MXFP4 weights), the fused gate/up
+    GEMM with a bias and both activation quantizers captured in one HIP
+    graph: every replay, with other eager work and synchronizations between
+    replays, equals the eager results bit for bit."""
     calls = []
     for i, (M, N, K) in enumerate([(10, 1024, 4096), (50, 1024, 4096), (768, 2048, 16384), (300, 256, 4096)]):
         A = dev(synthetic.activations(M, K, 9950 + i))
@@ -318,8 +319,29 @@ def test_graph_replays_equal_eager():
     wg = Weights(synthetic.weights(2 * I, K, 9971), vla.VLA_WFMT_E4M3_OCP)
     wsg = zeros_ws(vla.vla_gemm_workspace_bytes(M, 2 * I, K, 1))
     act = torch.empty(M * I, dtype=torch.int16, device="cuda")
-    calls.append(lambda: vla.vla_gemm_fp8w_gelu_mul(Ag, wg.q, wg.s, None, act, None, wsg, wsg.numel(), M, I, K))
+    bg = dev(synthetic.activations(1, 2 * I, 9972)[0])
+    calls.append(lambda: vla.vla_gemm_fp8w_gelu_mul(Ag, wg.q, wg.s, bg, act, None, wsg, wsg.numel(), M, I, K))
     calls[-1].Y = act
+    # wide MXFP4 (128-column tiles, K split over workgroups)
+    M4, N4, K4 = 768, 2048, 16384
+    A4 = dev(synthetic.activations(M4, K4, 9973))
+    q4 = torch.empty(vla.vla_packed_bytes(N4, K4, vla.VLA_WFMT_MXFP4), dtype=torch.uint8, device="cuda")
+    vla.vla_quantize_pack(dev(synthetic.weights(N4, K4, 9974)), q4, None, N4, K4, vla.VLA_WFMT_MXFP4, vla.VLA_LAYOUT_MFMA)
+    ws4 = zeros_ws(vla.vla_gemm_workspace_bytes(M4, N4, K4, vla.VLA_WFMT_MXFP4))
+    Y4 = torch.empty(M4 * N4, dtype=torch.int16, device="cuda")
+    calls.append(lambda: vla.vla_gemm_mxfp4w(A4, q4, None, None, Y4, ws4, ws4.numel(), M4, N4, K4))
+    calls[-1].Y = Y4
+    # activation quantization, dynamic (two kernels through the workspace) and frozen scale
+    Mq, Kq = 768, 2048
+    Aq = dev(synthetic.activations(Mq, Kq, 9975))
+    qa, sa = torch.empty(Mq * Kq, dtype=torch.uint8, device="cuda"), torch.empty(1, dtype=torch.float32, device="cuda")
+    wsq = zeros_ws(vla.vla_quantize_act_workspace_bytes(Mq, Kq))
+    calls.append(lambda: vla.vla_quantize_act(Aq, qa, sa, wsq, wsq.numel(), Mq, Kq))
+    calls[-1].Y = qa
+    sfix = dev(np.float32([0.0125]))
+    qs = torch.empty(Mq * Kq, dtype=torch.uint8, device="cuda")
+    calls.append(lambda: vla.vla_quantize_act_static(Aq, sfix, qs, Mq, Kq))
+    calls[-1].Y = qs
 
     for c in calls:
         c()
