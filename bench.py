@@ -241,6 +241,25 @@ def main():
             extra[f"mxfp4_{name}_us"] = round(us, 3)
             extra[f"mxfp4_{name}_GBps"] = round(mx_bytes / (us * 1e-6) / 1e9, 1)
 
+        # the fused gate/up GEMM of the gated MLP (merged 2I x H weights,
+        # GELU-tanh(gate) * up epilogue), same activations, cold rotation
+        W_gu = np.concatenate([W_up, synthetic.weights(I, H, synthetic.IDS["skinny.up.W"] + 1000)])
+        q_gu, s_gu = quantize(W_gu)
+        gcopies = max(1, (1 << 30) // q_gu.numel()) if args.cache == "cold" else 1
+        qs_gu = [q_gu] + [q_gu.clone() for _ in range(gcopies - 1)]
+        act_gu = torch.empty(M * I, dtype=torch.int16, device=dev)
+        wsg_bytes = vla.vla_gemm_workspace_bytes(M, 2 * I, H, 1)
+        wsg = torch.zeros(wsg_bytes, dtype=torch.uint8, device=dev)
+
+        def gateup(i):
+            vla.vla_gemm_fp8w_gelu_mul(A_up, qs_gu[i % gcopies], s_gu, None, act_gu, None, wsg, wsg_bytes, M, I, H)
+        ms = time_graph(gateup, args.steps)
+        us = ms * 1000.0 / args.steps
+        gu_bytes = 2 * I * H + 4 * 2 * I + 2 * M * H + 2 * M * I
+        extra["gateup_us"] = round(us, 3)
+        extra["gateup_GBps"] = round(gu_bytes / (us * 1e-6) / 1e9, 1)
+        del qs_gu
+
         # the pages' own decoder row count (10 rows), same weights and rotation
         A10_up = up_bits(synthetic.activations(10, H, synthetic.IDS["skinny.up.A"]))
         A10_dn = up_bits(synthetic.activations(10, I, synthetic.IDS["skinny.down.A"]))
