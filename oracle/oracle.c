@@ -323,11 +323,18 @@ void orc_gemm(const double *a, const double *w, const double *bias, int64_t M, i
 
 /* ------------------------------------------------------ gated-MLP chain */
 
-/* GELU, tanh form: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))). */
+/* GELU, tanh form (Hendrycks & Gimpel): 0.5 g (1 + tanh(z)) with
+ * z = sqrt(2/pi) (g + 0.044715 g^3).  Evaluated through the identity
+ * 1 + tanh(z) = 2 / (1 + exp(-2z)), i.e. g / (1 + exp(-2z)): the literal
+ * 1 + tanh(z) cancels in fp64 once it falls below the spacing of doubles
+ * near 1 (z < -19, g below about -7.5), where the true value is tiny but not
+ * zero; for z < -354 exp overflows and the result is the true value's
+ * underflow, a zero with g's sign. */
 double orc_gelu_tanh(double g)
 {
     const double c = sqrt(2.0 / M_PI);
-    return 0.5 * g * (1.0 + tanh(c * (g + 0.044715 * g * g * g)));
+    const double z = c * (g + 0.044715 * g * g * g);
+    return g / (1.0 + exp(-2.0 * z));
 }
 
 /* act = bf16(gelu_tanh(g) * u) for bf16 inputs g, u. */

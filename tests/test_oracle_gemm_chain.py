@@ -79,6 +79,55 @@ def test_gelu_tanh_matches_torch():
     assert oracle.gelu_tanh(0.0) == 0.0 and oracle.gelu_tanh(30.0) == 30.0 and oracle.gelu_tanh(-30.0) == 0.0
 
 
+def _gelu_definition(g, digits=120):
+    """The GELU tanh form evaluated literally, 0.5 g (1 + tanh z) with
+    tanh z = (e^{2z} - 1) / (e^{2z} + 1), in decimal arithmetic with 120
+    significant digits: the cancellation in 1 + tanh z costs at most ~90 of
+    them for |z| <= 100, leaving far more than fp64 needs."""
+    import decimal
+
+    with decimal.localcontext() as ctx:
+        ctx.prec = digits
+        G = decimal.Decimal(float(g))
+        c = (decimal.Decimal(2) / decimal.Decimal(ctx.create_decimal("3.14159265358979323846264338327950288419716939937510582097494459230781640628620899862803482534211706798214808651328230664709384460955058223172535940812848111745028410270193852110555964462294895493038196"))).sqrt()
+        z = c * (G + decimal.Decimal("0.044715") * G * G * G)
+        e = (2 * z).exp()
+        return 0.5 * g if z == 0 else float(decimal.Decimal("0.5") * G * (1 + (e - 1) / (e + 1)))
+
+
+def test_gelu_tanh_matches_high_precision_definition():
+    """Including the negative tail where the true value is tiny but not zero
+    (g = -8: about -1e-21; g = -10: about -1e-38), which a literal fp64
+    evaluation of 1 + tanh z turns into 0."""
+    gs = np.concatenate([np.linspace(-14, 6, 401), [-7.5, -8.0, -9.0, -10.0, -10.25, -11.0, -12.0, 1e-6, -1e-6]])
+    for g in gs:
+        want = _gelu_definition(g)
+        got = oracle.gelu_tanh(float(g))
+        c = np.sqrt(2 / np.pi)
+        z = abs(c * (g + 0.044715 * g ** 3))
+        assert abs(got - want) <= 4e-16 * (4 + 2 * z) * abs(want) + 1e-300, (g, got, want)
+    assert oracle.gelu_tanh(-8.0) < -1e-22 and oracle.gelu_tanh(-10.0) < -1e-40
+
+
+def test_gelu_mul_tail_large_up():
+    """act = bf16(gelu(g) u) where gelu(g) is tiny and u large (the values
+    deep in a chain whose residual stream grows): within half a bf16 ulp of
+    the high-precision definition times u."""
+    gs = np.array([-8.0, -9.0, -9.5, -10.0, -10.125, -10.25, -10.5], np.float32)
+    us = np.array([1.0, 1e3, 1e20, -3e30, 2.5e38], np.float32)
+    g_bits = synthetic.fp32_to_bf16_bits(np.repeat(gs, us.size))
+    u_bits = synthetic.fp32_to_bf16_bits(np.tile(us, gs.size))
+    got = bf16_bits_to_f64(oracle.gelu_mul(g_bits, u_bits))
+    for gb, ub, v in zip(bf16_bits_to_f64(g_bits), bf16_bits_to_f64(u_bits), got):
+        exact = _gelu_definition(gb) * ub
+        if abs(exact) < 2.0 ** -133:                          # below half the smallest bf16 subnormal
+            assert v == 0.0
+            continue
+        e = np.floor(np.log2(abs(exact)))
+        ulp = 2.0 ** (max(e, -126) - 7)
+        assert abs(v - exact) <= 0.5 * ulp * (1 + 1e-12), (gb, ub, v, exact)
+
+
 def test_gelu_mul_matches_torch():
     g = synthetic.activations(16, 512, 807)
     u = synthetic.activations(16, 512, 808)
