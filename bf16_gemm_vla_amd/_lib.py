@@ -40,6 +40,10 @@ SZ = ctypes.c_size_t
 SIGNATURES = {
     "vla_status_string": (ctypes.c_char_p, [INT]),
     "vla_last_error": (ctypes.c_char_p, []),
+    "vla_set_wait_limit": (None, [ctypes.c_uint32]),
+    "vla_workspace_status": (INT, [P, P]),
+    "vla_gemm_plan": (INT, [I64, I64, I64, INT, INT, INT, P, INT]),
+    "vla_mlp_chain_enqueue_staged": (INT, [P, P, P, P, P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P]),
     "vla_packed_bytes": (SZ, [I64, I64, INT]),
     "vla_quantize_pack": (INT, [P, P, P, I64, I64, INT, INT, P]),
     "vla_pack_fp8": (INT, [P, P, I64, I64, P]),
@@ -140,6 +144,22 @@ def vla_gemm_supported(M: int, N: int, K: int, wfmt: int, fp8_act: bool = False,
     return load().vla_gemm_supported(M, N, K, wfmt, int(bool(fp8_act)), int(bool(gelu_mul)))
 
 
+def vla_gemm_plan(M: int, N: int, K: int, wfmt: int, fp8_act: bool = False, gelu_mul: bool = False):
+    """(status, info) with info the 10 plan values of include/vla.h; host only."""
+    info = (ctypes.c_int64 * 10)()
+    rc = load().vla_gemm_plan(M, N, K, wfmt, int(bool(fp8_act)), int(bool(gelu_mul)), info, 10)
+    return rc, list(info)
+
+
+def vla_set_wait_limit(polls: int) -> None:
+    load().vla_set_wait_limit(polls)
+
+
+def vla_workspace_status(ws, stream=None) -> None:
+    """Raise RuntimeError if an in-kernel wait of a call that used ws gave up (clears the word)."""
+    _check(load().vla_workspace_status(_ptr(ws), _stream(stream)), "vla_workspace_status")
+
+
 def vla_mlp_chain_scratch_bytes(M: int, H: int, I: int) -> int:
     return load().vla_mlp_chain_scratch_bytes(M, H, I)
 
@@ -222,6 +242,14 @@ def vla_mlp_chain_enqueue(wgu, sgu, wd, sd, x_in, x_out, scratch, scratch_bytes,
                                         _ptr_array(sd), _ptr(x_in), _ptr(x_out), _ptr(scratch),
                                         scratch_bytes, L, M, H, I, _stream(stream)),
            "vla_mlp_chain_enqueue")
+
+
+def vla_mlp_chain_enqueue_staged(wgu, sgu, wd, sd, x_in, x_out, gu_out, act_out, down_out, x_layers, scratch,
+                                 scratch_bytes, L, M, H, I, stream=None):
+    _check(load().vla_mlp_chain_enqueue_staged(_ptr_array(wgu), _ptr_array(sgu), _ptr_array(wd), _ptr_array(sd),
+                                               _ptr(x_in), _ptr(x_out), _ptr(gu_out), _ptr(act_out), _ptr(down_out),
+                                               _ptr(x_layers), _ptr(scratch), scratch_bytes, L, M, H, I,
+                                               _stream(stream)), "vla_mlp_chain_enqueue_staged")
 
 
 def vla_mlp_chain_create(wgu, sgu, wd, sd, x_in, x_out, scratch, scratch_bytes, L, M, H, I,

@@ -3,6 +3,7 @@
 // codec.hip and gemm.hip; nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -17,6 +18,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+std::atomic<uint32_t> g_wait_polls{vla::kDefaultWaitPolls};
 
 int fail(int code, const char* fn, const char* fmt, ...) {
     char msg[384];
@@ -76,6 +78,8 @@ int run_gemm(const char* fn, const vla::GemmProblem& pr, size_t ws_bytes, hipStr
 
 }  // namespace
 
+uint32_t vla::wait_polls() { return g_wait_polls.load(std::memory_order_relaxed); }
+
 struct vla_mlp_chain {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
@@ -86,21 +90,28 @@ namespace {
 std::mutex g_chain_mu;
 std::unordered_set<const vla_mlp_chain*> g_chains;
 
+// Chain scratch: GEMM workspace (first, so its status word sits at the
+// same offset as in a plain GEMM workspace) | x | act.
 struct ChainLayout {
-    size_t x_off, act_off, ws_off, total, ws_bytes;
+    size_t ws_off, x_off, act_off, total, ws_bytes;
 };
 
-ChainLayout chain_layout(int64_t M, int64_t H, int64_t I) {
-    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    ChainLayout c{};
-    c.x_off = 0;
-    c.act_off = up(static_cast<size_t>(M) * H * 2);
-    c.ws_off = c.act_off + up(static_cast<size_t>(M) * I * 2);
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+size_t chain_ws_bytes(int64_t M, int64_t H, int64_t I) {
     const auto pg = vla::plan_gemm(M, 2 * I, H, vla::AType::BF16, vla::WType::FP8, vla::Epi::GELU_MUL);
     const auto pd = vla::plan_gemm(M, H, I, vla::AType::BF16, vla::WType::FP8, vla::Epi::PLAIN);
     const size_t a = vla::gemm_ws_bytes(pg, M, 2 * I), b = vla::gemm_ws_bytes(pd, M, H);
-    c.ws_bytes = up(a > b ? a : b);
-    c.total = c.ws_off + c.ws_bytes;
+    return round256(a > b ? a : b);
+}
+
+ChainLayout chain_layout(int64_t M, int64_t H, int64_t I) {
+    ChainLayout c{};
+    c.ws_off = 0;
+    c.ws_bytes = chain_ws_bytes(M, H, I);
+    c.x_off = c.ws_bytes;
+    c.act_off = c.x_off + round256(static_cast<size_t>(M) * H * 2);
+    c.total = c.act_off + round256(static_cast<size_t>(M) * I * 2);
     return c;
 }
 
@@ -134,53 +145,73 @@ int check_chain(const char* fn, const uint8_t* const* wgu, const float* const* s
     return VLA_OK;
 }
 
+// Per-layer stage outputs of the gated-MLP chain (each nullable): the merged
+// gate/up GEMM result [g | u] (L x M x 2I), the activation (L x M x I), the
+// down GEMM result before the residual add (L x M x H) and x after each
+// layer (L x M x H).
+struct ChainStages {
+    uint16_t* gu = nullptr;
+    uint16_t* act = nullptr;
+    uint16_t* down = nullptr;
+    uint16_t* x = nullptr;
+};
+
 int enqueue_chain(const char* fn, const uint8_t* const* wgu, const float* const* sgu,
                   const uint8_t* const* wd, const float* const* sd, const uint16_t* x_in,
                   uint16_t* x_out, void* scratch, int L, int64_t M, int64_t H, int64_t I,
-                  hipStream_t s) {
+                  const ChainStages& st, hipStream_t s) {
     const ChainLayout c = chain_layout(M, H, I);
     uint8_t* base = static_cast<uint8_t*>(scratch);
     uint16_t* xbuf = reinterpret_cast<uint16_t*>(base + c.x_off);
-    uint16_t* act = reinterpret_cast<uint16_t*>(base + c.act_off);
+    uint16_t* act_buf = reinterpret_cast<uint16_t*>(base + c.act_off);
     void* ws = base + c.ws_off;
+    const size_t mh = static_cast<size_t>(M) * H, mi = static_cast<size_t>(M) * I;
     const uint16_t* x = x_in;
     for (int l = 0; l < L; ++l) {
+        uint16_t* act = st.act ? st.act + l * mi : act_buf;
         vla::GemmProblem g{};
         g.A = x; g.W = wgu[l]; g.s_w = sgu[l]; g.Y = act; g.ws = ws;
+        g.gu = st.gu ? st.gu + l * 2 * mi : nullptr;
         g.M = M; g.N = 2 * I; g.K = H;
         g.atype = vla::AType::BF16; g.wtype = vla::WType::FP8; g.epi = vla::Epi::GELU_MUL;
         if (int rc = run_gemm(fn, g, c.ws_bytes, s)) return rc;
-        uint16_t* y = (l == L - 1) ? x_out : xbuf;
+        // with per-layer x outputs every layer writes its own slot (the
+        // last one is then copied to x_out); else x alternates between
+        // scratch and x_out
+        uint16_t* y = st.x ? st.x + l * mh : ((l == L - 1) ? x_out : xbuf);
         vla::GemmProblem d{};
         d.A = act; d.W = wd[l]; d.s_w = sd[l]; d.resid = x; d.Y = y; d.ws = ws;
+        d.ypre = st.down ? st.down + l * mh : nullptr;
         d.M = M; d.N = H; d.K = I;
         d.atype = vla::AType::BF16; d.wtype = vla::WType::FP8; d.epi = vla::Epi::PLAIN;
         if (int rc = run_gemm(fn, d, c.ws_bytes, s)) return rc;
         x = y;
     }
+    if (st.x) {
+        hipError_t e = hipMemcpyAsync(x_out, x, mh * 2, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(fn, "hipMemcpyAsync", e);
+    }
     return VLA_OK;
 }
 
-// Decoder-block chain scratch: x | h | gate (two, alternating) | down output |
-// act | GEMM workspace.
+// Decoder-block chain scratch: GEMM workspace | x | h | gate (two,
+// alternating) | down output | act.
 struct DecoderLayout {
-    size_t x_off, h_off, g_off[2], d_off, act_off, ws_off, total, ws_bytes;
+    size_t ws_off, x_off, h_off, g_off[2], d_off, act_off, total, ws_bytes;
 };
 
 DecoderLayout decoder_layout(int64_t M, int64_t H, int64_t I) {
-    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    const size_t mh = up(static_cast<size_t>(M) * H * 2);
+    const size_t mh = round256(static_cast<size_t>(M) * H * 2);
     DecoderLayout c{};
-    c.x_off = 0;
-    c.h_off = mh;
-    c.g_off[0] = 2 * mh;
-    c.g_off[1] = 3 * mh;
-    c.d_off = 4 * mh;
-    c.act_off = 5 * mh;
-    c.ws_off = c.act_off + up(static_cast<size_t>(M) * I * 2);
-    const ChainLayout cl = chain_layout(M, H, I);
-    c.ws_bytes = cl.ws_bytes;
-    c.total = c.ws_off + c.ws_bytes;
+    c.ws_off = 0;
+    c.ws_bytes = chain_ws_bytes(M, H, I);
+    c.x_off = c.ws_bytes;
+    c.h_off = c.x_off + mh;
+    c.g_off[0] = c.x_off + 2 * mh;
+    c.g_off[1] = c.x_off + 3 * mh;
+    c.d_off = c.x_off + 4 * mh;
+    c.act_off = c.x_off + 5 * mh;
+    c.total = c.act_off + round256(static_cast<size_t>(M) * I * 2);
     return c;
 }
 
@@ -325,6 +356,28 @@ const char* vla_status_string(int status) {
 }
 
 const char* vla_last_error(void) { return g_err; }
+
+void vla_set_wait_limit(uint32_t polls) {
+    g_wait_polls.store(polls == 0 ? vla::kDefaultWaitPolls : polls, std::memory_order_relaxed);
+}
+
+int vla_workspace_status(void* ws, void* stream) {
+    const char* fn = "vla_workspace_status";
+    REQUIRE_PTR(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t* word = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + vla::kStatusOffset);
+    uint32_t v = 0;
+    static const uint32_t zero = 0;
+    hipError_t e = hipMemcpyAsync(&v, word, 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess && v != 0) e = hipMemcpyAsync(word, &zero, 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(fn, "status word copy", e);
+    if (v == 0) return VLA_OK;
+    return fail(VLA_EHIP, fn, "an in-kernel wait gave up and left output unwritten (status 0x%x:%s%s)", v,
+                (v & vla::kStatusWideSplitK) ? " wide split-K partials" : "",
+                (v & vla::kStatusChainBarrier) ? " fused chain phase barrier" : "");
+}
 
 size_t vla_packed_bytes(int64_t N, int64_t K, int wfmt) {
     if (N <= 0 || K <= 0) return 0;
@@ -481,7 +534,13 @@ size_t vla_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int wfmt) {
 }
 
 int vla_gemm_supported(int64_t M, int64_t N, int64_t K, int wfmt, int fp8_act, int gelu_mul) {
-    const char* fn = "vla_gemm_supported";
+    return vla_gemm_plan(M, N, K, wfmt, fp8_act, gelu_mul, nullptr, 0);
+}
+
+int vla_gemm_plan(int64_t M, int64_t N, int64_t K, int wfmt, int fp8_act, int gelu_mul, int64_t* info,
+                  int n_info) {
+    const char* fn = "vla_gemm_plan";
+    if (n_info < 0 || (n_info > 0 && !info)) return fail(VLA_EINVAL, fn, "info is NULL or n_info < 0");
     if (int rc = check_mnk(fn, M, N, K)) return rc;
     if (wfmt != VLA_WFMT_BF16 && wfmt != VLA_WFMT_E4M3_OCP && wfmt != VLA_WFMT_MXFP4)
         return fail(VLA_EINVAL, fn, "wfmt=%d", wfmt);
@@ -493,6 +552,19 @@ int vla_gemm_supported(int64_t M, int64_t N, int64_t K, int wfmt, int fp8_act, i
     if (gelu_mul && fp8_act) return fail(VLA_EINVAL, fn, "gelu_mul takes bf16 activations");
     if (gelu_mul && (N % 32) != 0) return fail(VLA_ESHAPE, fn, "gelu_mul needs N = 2I with I a multiple of 16");
     const vla::GemmPlan p = vla::plan_gemm(M, N, K, at, wt, epi);
+    const size_t ws = vla::gemm_ws_bytes(p, M, N);
+    const int64_t v[10] = {p.kernel,
+                           p.nt,
+                           p.groups,
+                           p.kernel == 0 ? p.ksplit : p.mblocks,
+                           p.kernel == 0 ? p.mblocks : p.ksplit,
+                           p.ksplit,
+                           static_cast<int64_t>(ws),
+                           static_cast<int64_t>(ws - vla::kCounterBytes),
+                           static_cast<int64_t>(p.waves) * 64,
+                           p.kernel == 0 ? static_cast<int64_t>(p.groups) * p.mblocks
+                                         : static_cast<int64_t>(p.groups) * p.mblocks * vla::kWideCounters};
+    for (int i = 0; i < n_info && i < 10; ++i) info[i] = v[i];
     if (!vla::plan_dispatchable(p, at, wt, epi))
         return fail(VLA_ESHAPE, fn, "M=%lld N=%lld K=%lld exceeds the kernels' limits", (long long)M, (long long)N,
                     (long long)K);
@@ -593,8 +665,39 @@ int vla_mlp_chain_enqueue(const uint8_t* const* wgu, const float* const* sgu,
                           int64_t H, int64_t I, void* stream) {
     const char* fn = "vla_mlp_chain_enqueue";
     if (int rc = check_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, scratch_bytes, L, M, H, I)) return rc;
-    return enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I,
+    return enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I, ChainStages{},
                          static_cast<hipStream_t>(stream));
+}
+
+int vla_mlp_chain_enqueue_staged(const uint8_t* const* wgu, const float* const* sgu,
+                                 const uint8_t* const* wd, const float* const* sd, const uint16_t* x_in,
+                                 uint16_t* x_out, uint16_t* gu_out, uint16_t* act_out, uint16_t* down_out,
+                                 uint16_t* x_layers, void* scratch, size_t scratch_bytes, int L, int64_t M,
+                                 int64_t H, int64_t I, void* stream) {
+    const char* fn = "vla_mlp_chain_enqueue_staged";
+    if (int rc = check_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, scratch_bytes, L, M, H, I)) return rc;
+    OPTIONAL_PTR(gu_out);
+    OPTIONAL_PTR(act_out);
+    OPTIONAL_PTR(down_out);
+    OPTIONAL_PTR(x_layers);
+    const size_t mh = static_cast<size_t>(M) * H * 2 * L, mi = static_cast<size_t>(M) * I * 2 * L;
+    struct Range { const void* p; size_t n; };
+    const Range outs[4] = {{gu_out, 2 * mi}, {act_out, mi}, {down_out, mh}, {x_layers, mh}};
+    const Range others[3] = {{x_in, static_cast<size_t>(M) * H * 2}, {x_out, static_cast<size_t>(M) * H * 2},
+                             {scratch, chain_layout(M, H, I).total}};
+    auto overlap = [](const Range& x, const Range& y) {
+        const uint8_t *a = static_cast<const uint8_t*>(x.p), *b = static_cast<const uint8_t*>(y.p);
+        return a && b && a < b + y.n && b < a + x.n;
+    };
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return fail(VLA_EINVAL, fn, "stage outputs %d and %d overlap", i, j);
+        for (int j = 0; j < 3; ++j)
+            if (overlap(outs[i], others[j])) return fail(VLA_EINVAL, fn, "stage output %d overlaps x_in, x_out or scratch", i);
+    }
+    ChainStages st;
+    st.gu = gu_out; st.act = act_out; st.down = down_out; st.x = x_layers;
+    return enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I, st, static_cast<hipStream_t>(stream));
 }
 
 int vla_mlp_chain_create(const uint8_t* const* wgu, const float* const* sgu,
@@ -607,7 +710,7 @@ int vla_mlp_chain_create(const uint8_t* const* wgu, const float* const* sgu,
     if (!capture_stream) return fail(VLA_EINVAL, fn, "capture_stream must not be the null stream");
     if (int rc = check_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, scratch_bytes, L, M, H, I)) return rc;
     return capture_chain(fn, capture_stream, L, out, [&](hipStream_t s) {
-        return enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I, s);
+        return enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I, ChainStages{}, s);
     });
 }
 

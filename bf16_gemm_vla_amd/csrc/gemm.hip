@@ -375,7 +375,10 @@ GemmPlan skinny_plan(int64_t M, int64_t N, int64_t K, Epi epi, int nt, int steps
     p.groups = static_cast<int>(std::max<int64_t>(1, epi == Epi::GELU_MUL ? (tiles / 2) / (nt / 2) : (tiles + nt - 1) / nt));
     p.ksplit = static_cast<int>((ksteps + static_cast<int64_t>(waves) * steps - 1) / (static_cast<int64_t>(waves) * steps));
     p.mblocks = static_cast<int>((M + 16 * mt - 1) / (16 * mt));
-    p.ok = p.ksplit == 1 || static_cast<int64_t>(p.groups) * p.mblocks <= kMaxCounters;
+    // split-K: one counter per output group, and partials the kernel
+    // addresses with 32-bit byte offsets
+    const uint64_t part = static_cast<uint64_t>(p.ksplit) * p.mblocks * p.groups * nt * mt * 64 * 16;
+    p.ok = p.ksplit == 1 || (static_cast<int64_t>(p.groups) * p.mblocks <= kMaxCounters && part < kMaxPartBytes);
     return p;
 }
 
@@ -478,8 +481,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi)
     const int64_t a_bytes = M * K * (at == AType::FP8 ? 1 : 2);
     const int64_t w_bytes = (wt == WType::FP4) ? N * K / 2 + N * (((K >> 5) + 7) & ~int64_t(7))
                                                : N * K * (wt == WType::FP8 ? 1 : 2);
-    // split-K counters: kWideCounters per output tile
-    p.ok = base * kWideCounters <= kMaxCounters && a_bytes < (int64_t(1) << 31) && w_bytes < (int64_t(1) << 31);
+    // split-K counters: kWideCounters per output tile; partials addressed
+    // with 32-bit byte offsets
+    p.ok = base * kWideCounters <= kMaxCounters && a_bytes < (int64_t(1) << 31) && w_bytes < (int64_t(1) << 31) &&
+           (p.ksplit == 1 || wide_part_bytes(p) < kMaxPartBytes);
     return p;
 }
 
@@ -498,13 +503,16 @@ size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
 hipError_t launch_gemm_plan(const GemmProblem& pr, const GemmPlan& p, hipStream_t s) {
     KArgs ka{};
     ka.A = pr.A; ka.s_a = pr.s_a; ka.W = pr.W; ka.s_w = pr.s_w;
-    ka.bias = pr.bias; ka.resid = pr.resid; ka.Y = pr.Y; ka.gu = pr.gu;
+    ka.bias = pr.bias; ka.resid = pr.resid; ka.Y = pr.Y; ka.gu = pr.gu; ka.ypre = pr.ypre;
     ka.M = static_cast<int>(pr.M); ka.N = static_cast<int>(pr.N); ka.K = static_cast<int>(pr.K);
     ka.ksplit = p.ksplit;
     ka.groups = p.groups;
     ka.msplit = p.mblocks;
     ka.tickets = static_cast<uint32_t*>(pr.ws);
+    ka.err = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(pr.ws) + kStatusOffset);
+    ka.wait_polls = wait_polls();
     ka.part = reinterpret_cast<float*>(static_cast<uint8_t*>(pr.ws) + kCounterBytes);
+    // below 2^32 for every plan marked ok (plan_gemm checks it)
     ka.part_bytes = static_cast<uint32_t>(gemm_ws_bytes(p, pr.M, pr.N) - kCounterBytes);
 
     if (pr.epi == Epi::GELU_MUL) return launch_typed<AType::BF16, WType::FP8, Epi::GELU_MUL>(ka, p, s);

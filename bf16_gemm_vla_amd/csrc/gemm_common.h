@@ -27,9 +27,12 @@ struct KArgs {
     const uint16_t* resid;
     uint16_t* Y;
     uint16_t* gu;
+    uint16_t* ypre;     // nullable: bf16(acc * scale + bias) before the residual add
     uint32_t* tickets;
+    uint32_t* err;      // the workspace's status word (a bounded wait gave up)
     float* part;
     uint32_t part_bytes;
+    uint32_t wait_polls;   // bound of every in-kernel wait, in polls
     int M, N, K;
     int ksplit;
     int groups;
@@ -103,6 +106,7 @@ template <AType AT, WType WT>
 __device__ __forceinline__ void store_plain(const KArgs& a, int m, int n, f32x4_t v, const EpiIn& e, float sa) {
     uint2 o = epi_plain4<AT, WT>(a, v, e, sa);
     if (a.resid) {
+        if (a.ypre) *reinterpret_cast<uint2*>(a.ypre + static_cast<int64_t>(m) * a.N + n) = o;
         o.x = add_resid2(o.x, e.resid.x);
         o.y = add_resid2(o.y, e.resid.y);
     }
@@ -127,10 +131,10 @@ __device__ __forceinline__ uint2 epi_gelu4(f32x4_t vg, f32x4_t vu, const EpiIn& 
     }
     gp = make_uint2(f32x2_to_bf16x2(g[0], g[1]), f32x2_to_bf16x2(g[2], g[3]));
     up = make_uint2(f32x2_to_bf16x2(u[0], u[1]), f32x2_to_bf16x2(u[2], u[3]));
-    const float a0 = gelu_tanh(bf16_to_f32(lo16(gp.x))) * bf16_to_f32(lo16(up.x));
-    const float a1 = gelu_tanh(bf16_to_f32(hi16(gp.x))) * bf16_to_f32(hi16(up.x));
-    const float a2 = gelu_tanh(bf16_to_f32(lo16(gp.y))) * bf16_to_f32(lo16(up.y));
-    const float a3 = gelu_tanh(bf16_to_f32(hi16(gp.y))) * bf16_to_f32(hi16(up.y));
+    const float a0 = gelu_mul(bf16_to_f32(lo16(gp.x)), bf16_to_f32(lo16(up.x)));
+    const float a1 = gelu_mul(bf16_to_f32(hi16(gp.x)), bf16_to_f32(hi16(up.x)));
+    const float a2 = gelu_mul(bf16_to_f32(lo16(gp.y)), bf16_to_f32(lo16(up.y)));
+    const float a3 = gelu_mul(bf16_to_f32(hi16(gp.y)), bf16_to_f32(hi16(up.y)));
     return make_uint2(f32x2_to_bf16x2(a0, a1), f32x2_to_bf16x2(a2, a3));
 }
 
@@ -185,6 +189,13 @@ __device__ __forceinline__ bool splitk_arrive_last(uint32_t* tickets, int slot, 
 
 __device__ __forceinline__ void splitk_reset(uint32_t* tickets, int slot) {
     if (threadIdx.x == 0) __hip_atomic_store(tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Record that a bounded wait gave up (its output was not written): OR the
+// cause bit into the workspace's status word, read back on the host by
+// vla_workspace_status.
+__device__ __forceinline__ void report_wait_timeout(uint32_t* err, uint32_t cause) {
+    __hip_atomic_fetch_or(err, cause, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace gemm_detail

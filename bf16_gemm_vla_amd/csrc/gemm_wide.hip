@@ -46,7 +46,6 @@ using namespace gemm_detail;
 constexpr int kWideBM = 192;
 constexpr int kWideStages = 4;
 constexpr uint32_t kOOB = 0x80000000u;   // voffset beyond every resource's range
-constexpr int kWideSpinMax = 1 << 20;     // polls before an owner gives up waiting (never reached)
 
 template <AType AT, WType WT, int BN, int WNW, int BK_>
 struct WideCfg {
@@ -533,13 +532,18 @@ void wide_gemm_kernel(KArgs a) {
                     if (((handed >> ms) & 1u) || ms >= a.ksplit) mine |= 1u << ms;
             }
             if (wait_own) {
-                for (int it = 0; it < kWideSpinMax; ++it) {
+                // bounded: an owner that gives up leaves its slice unwritten
+                // and records that in the workspace's status word
+                bool arrived = false;
+                for (uint32_t it = 0; it < a.wait_polls; ++it) {
                     if ((__hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFFFFu) == ks) {
-                        mine |= 1u << own;
+                        arrived = true;
                         break;
                     }
                     __builtin_amdgcn_s_sleep(2);
                 }
+                if (arrived) mine |= 1u << own;
+                else report_wait_timeout(a.err, kStatusWideSplitK);
             }
             // no counter of the tile is read after this point; the last
             // workgroup past it clears them for the next call
@@ -660,6 +664,8 @@ void wide_gemm_kernel(KArgs a) {
                 const uint8_t* src = ((row >> 5) ? pair1 : pair0) + (row & 31) * OSTRIDE + ch * 16;
                 uint4 v = *reinterpret_cast<const uint4*>(src);
                 if constexpr (decltype(WITH_RESID)::value) {
+                    if (a.ypre)
+                        *reinterpret_cast<uint4*>(a.ypre + static_cast<int64_t>(gm) * a.N + n) = v;
                     const uint4 r = *reinterpret_cast<const uint4*>(a.resid + static_cast<int64_t>(gm) * a.N + n);
                     v.x = add_resid2(v.x, r.x);
                     v.y = add_resid2(v.y, r.y);

@@ -143,16 +143,22 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
-// GELU, tanh form: 0.5 g (1 + tanh(z)), z = sqrt(2/pi) (g + 0.044715 g^3),
-// evaluated as g / (1 + exp(-2z)) (the same function: 1 + tanh(z) =
-// 2 / (1 + exp(-2z))), which keeps its relative accuracy for negative g,
-// where 1 + tanh(z) cancels to a few ulps or to zero in fp32.  The IEEE
-// division keeps tiny results (down to the subnormals); for very negative g,
-// exp overflows to inf and the result is -0.
-__device__ __forceinline__ float gelu_tanh(float g) {
+// GELU, tanh form, times u: 0.5 g (1 + tanh(z)) u, z = sqrt(2/pi) (g +
+// 0.044715 g^3), evaluated as g / (1 + exp(-2z)) * u (the same function:
+// 1 + tanh(z) = 2 / (1 + exp(-2z))), which keeps its relative accuracy for
+// negative g, where 1 + tanh(z) cancels to a few ulps or to zero in fp32;
+// the IEEE division keeps tiny results.  For z < -40 (g below about -9.2)
+// gelu(g) is below ~1e-34: in fp32 it reaches the subnormals (and exp(-2z)
+// overflows near g = -10.1) while gelu(g) * u can still be a normal number
+// when |u| is large, so that tail is evaluated in fp64, as
+// g e^{2z} / (1 + e^{2z}) * u.  Rare in practice (a wave takes the branch
+// only if one of its lanes needs it).
+__device__ __forceinline__ float gelu_mul(float g, float u) {
     const float c = 0.7978845608028654f;  // sqrt(2/pi)
     const float z = c * (g + 0.044715f * g * g * g);
-    return g / (1.0f + expf(-2.0f * z));
+    if (z > -40.0f) return g / (1.0f + expf(-2.0f * z)) * u;
+    const double e = exp(2.0 * static_cast<double>(z));
+    return static_cast<float>(static_cast<double>(g) * e / (1.0 + e) * static_cast<double>(u));
 }
 
 }  // namespace vla

@@ -45,6 +45,7 @@ struct GemmProblem {
     const uint16_t* resid;  // nullable
     uint16_t* Y;            // PLAIN: M x N; GELU_MUL: M x N/2
     uint16_t* gu;           // GELU_MUL debug output M x N, nullable
+    uint16_t* ypre;         // PLAIN: output before the residual add, M x N, nullable
     void* ws;
     int64_t M, N, K;        // N = weight rows
     AType atype;
@@ -64,7 +65,7 @@ struct GemmPlan {
     int mblocks;    // M blocks (wide: grid y of 192 rows; skinny: grid z of mt 16-row tiles)
     int mt;         // skinny: 16-row activation tiles per workgroup
     bool alds;      // skinny: stage activations through LDS
-    bool ok;        // false when the shape exceeds the split-K counter space
+    bool ok;        // false when the shape exceeds the split-K counter or partial space
 };
 
 // The first kCounterBytes of every GEMM workspace hold the split-K arrival
@@ -76,6 +77,17 @@ constexpr size_t kCounterBytes = 65536;
 constexpr size_t kZeroPageOffset = kCounterBytes - 4096;
 constexpr int kMaxCounters = static_cast<int>(kZeroPageOffset / 4);
 constexpr int kWideCounters = 4;   // three used, one pad
+// The status word: the first 4 bytes of the page after the counters.  Zero
+// until a bounded in-kernel wait gives up; each cause sets one bit.
+constexpr size_t kStatusOffset = kZeroPageOffset;
+constexpr uint32_t kStatusWideSplitK = 1u;   // wide split-K owner gave up waiting for partials
+constexpr uint32_t kStatusChainBarrier = 2u;   // fused chain: a phase barrier gave up
+// Split-K partial regions are addressed with 32-bit offsets.
+constexpr uint64_t kMaxPartBytes = uint64_t(1) << 32;
+// Default bound of every in-kernel wait, in polls (about 2 s of polling on
+// MI355X; never reached by a grid that is resident).
+constexpr uint32_t kDefaultWaitPolls = 1u << 22;
+uint32_t wait_polls();                  // current bound (vla_set_wait_limit)
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi);
 size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N);

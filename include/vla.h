@@ -69,6 +69,23 @@ const char *vla_status_string(int status);
 /* Message of the calling thread's last failed call ("" if none). */
 const char *vla_last_error(void);
 
+/* Bounded in-kernel waits.  Kernels that wait for other workgroups (the wide
+ * GEMM's split-K hand-over, the fused chain's phase barriers) poll at most
+ * `polls` times (about 0.5 us per poll), then give up, leave the output they
+ * were waiting to produce unwritten, record the cause in the workspace's
+ * status word and exit normally, so no wait can hang the device.  0 restores
+ * the default (2^22 polls, never reached by a grid that is resident).  The
+ * bound is read when a call is enqueued (or captured).  Process-wide. */
+void vla_set_wait_limit(uint32_t polls);
+
+/* Read and clear the status word of a GEMM workspace or chain scratch
+ * buffer (byte 61440 of it): VLA_OK when no in-kernel wait of a call that
+ * used `ws` has given up since the last query, else VLA_EHIP naming the
+ * cause (its output is incomplete).  Copies 4 bytes to the host and
+ * synchronises `stream` (which must have run those calls): not for use under
+ * stream capture.  Errors: EINVAL/EALIGN for ws, EHIP if a copy fails. */
+int vla_workspace_status(void *ws, void *stream);
+
 /* --------------------------------------------------------- weight codecs */
 
 /* Bytes of an N x K weight in format `wfmt` (either layout; MXFP4: codes
@@ -187,8 +204,9 @@ int vla_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blo
 /* ------------------------------------------------------------------ GEMM */
 
 /* Workspace for vla_gemm_fp8w / vla_gemm_bf16 / vla_gemm_fp8w_gelu_mul at
- * this shape (N = weight rows; for gelu_mul N = 2 I).  Its first 64 KiB
- * hold the split-K arrival counters (the same place for every shape); the
+ * this shape (N = weight rows; for gelu_mul N = 2 I).  Its first 60 KiB
+ * hold the split-K arrival counters (the same place for every shape), the
+ * next 4 KiB the status word (vla_workspace_status) and unused bytes; the
  * rest holds split-K partial sums.  The workspace must be
  * ZERO-FILLED before its first use; every completed call leaves the
  * counters at zero again, so one zeroed buffer (sized for the largest
@@ -203,6 +221,22 @@ size_t vla_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int wfmt);
  * GEMM with N = 2I), else the status the GEMM call itself would return
  * (EINVAL, ESHAPE). */
 int vla_gemm_supported(int64_t M, int64_t N, int64_t K, int wfmt, int fp8_act, int gelu_mul);
+
+/* Host-only query, no device work: the launch plan a GEMM of this shape
+ * takes (arguments as vla_gemm_supported).  Writes min(n_info, 10) values:
+ *   [0] kernel (0 = skinny, M <= 64; 1 = wide)
+ *   [1] skinny: 16-column weight tiles per workgroup; wide: tile width
+ *   [2] [3] [4] grid x, y, z (skinny: column groups, K splits, row blocks;
+ *               wide: column groups, 192-row blocks, K splits)
+ *   [5] K splits across workgroups
+ *   [6] workspace bytes (vla_gemm_workspace_bytes for this operand class)
+ *   [7] split-K partial bytes (addressed with 32-bit offsets: < 2^32)
+ *   [8] threads per workgroup
+ *   [9] split-K counters used (at most 15360)
+ * Returns what vla_gemm_supported returns; the values are written in
+ * either case when the shape passes the argument checks. */
+int vla_gemm_plan(int64_t M, int64_t N, int64_t K, int wfmt, int fp8_act, int gelu_mul, int64_t *info,
+                  int n_info);
 
 /* Y = bf16( s[n] * sum_k A[m,k] * dec(Wq[n,k]) + bias[n] ), optionally
  * followed by Y = bf16(residual + Y).
@@ -288,6 +322,25 @@ int vla_mlp_chain_enqueue(const uint8_t *const *wgu, const float *const *sgu,
                           const uint16_t *x_in, uint16_t *x_out, void *scratch,
                           size_t scratch_bytes, int L, int64_t M, int64_t H, int64_t I,
                           void *stream);
+
+/* vla_mlp_chain_enqueue that also writes every layer's intermediate
+ * results, so each rounding point of the chain ("Real-time VLA inference
+ * on AMD hardware", "Merging gate and up" and "Fusing the BF16 decoder
+ * boundary") can be checked on its own inputs.  Each output is nullable:
+ *   gu_out    device bf16 L x M x 2I: [g | u] of layer l (before GELU * mul)
+ *   act_out   device bf16 L x M x I:  act of layer l
+ *   down_out  device bf16 L x M x H:  bf16(act @ Wdown_l^T), before the
+ *             residual add (x_l+1 = bf16(x_l + down_l))
+ *   x_layers  device bf16 L x M x H:  x after layer l (x_layers[L-1] equals
+ *             x_out)
+ * Outputs must not overlap each other, x_in, x_out or scratch (EINVAL).
+ * x_out equals vla_mlp_chain_enqueue's result bit for bit. */
+int vla_mlp_chain_enqueue_staged(const uint8_t *const *wgu, const float *const *sgu,
+                                 const uint8_t *const *wd, const float *const *sd,
+                                 const uint16_t *x_in, uint16_t *x_out, uint16_t *gu_out,
+                                 uint16_t *act_out, uint16_t *down_out, uint16_t *x_layers,
+                                 void *scratch, size_t scratch_bytes, int L, int64_t M, int64_t H,
+                                 int64_t I, void *stream);
 
 typedef struct vla_mlp_chain vla_mlp_chain;
 

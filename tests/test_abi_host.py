@@ -245,3 +245,82 @@ def test_gemm_supported_rejects_bad_arguments(lib):
     assert vla.vla_gemm_supported(4, 48, 64, 1, gelu_mul=True) == vla.VLA_ESHAPE
     # the wide kernel addresses operands with 32-bit offsets
     assert vla.vla_gemm_supported(768, 1 << 20, 4096, 1) == vla.VLA_ESHAPE
+
+
+def test_plan_sweep_limits(lib):
+    """Every plan the library accepts keeps its split-K partials below 2^32
+    bytes (the kernels address them with 32-bit buffer offsets) and its
+    counters within the 15360 counter slots, sizes its workspace as counters
+    plus partials, and covers the output with its grid; shapes past those
+    limits are refused (ESHAPE) instead of planned."""
+    Ms = (1, 10, 16, 17, 50, 64, 65, 192, 571, 768, 4096, 1 << 16, 1 << 20)
+    Ns = (16, 1024, 4096, 16384, 65536, 1 << 20)
+    Ks = (32, 1024, 4096, 16384, 262144, 1 << 20)
+    classes = [(vla.VLA_WFMT_E4M3_OCP, False, False), (vla.VLA_WFMT_BF16, False, False),
+               (vla.VLA_WFMT_E4M3_OCP, True, False), (vla.VLA_WFMT_E4M3_OCP, False, True),
+               (vla.VLA_WFMT_MXFP4, False, False)]
+    accepted = refused = 0
+    for M in Ms:
+        for N in Ns:
+            for K in Ks:
+                if N * K > (1 << 40):
+                    continue
+                for wfmt, fp8, gelu in classes:
+                    rc, info = vla.vla_gemm_plan(M, N, K, wfmt, fp8, gelu)
+                    kernel, tile, gx, gy, gz, ksplit, ws, part, threads, counters = info
+                    if rc != 0:
+                        assert rc == vla.VLA_ESHAPE, (M, N, K, wfmt, fp8, gelu, rc)
+                        refused += 1
+                        continue
+                    accepted += 1
+                    key = (M, N, K, wfmt, fp8, gelu, info)
+                    assert kernel == (0 if M <= 64 else 1), key
+                    assert 0 <= part < (1 << 32), key
+                    assert ws == 65536 + (part if ksplit > 1 else 0), key
+                    assert ws <= vla.vla_gemm_workspace_bytes(M, N, K, wfmt), key
+                    assert ksplit == 1 or counters <= 15360, key
+                    assert threads in (256, 512, 1024), key
+                    cols = N // 2 if gelu else N
+                    if kernel == 0:
+                        per_group = tile * 16 // (2 if gelu else 1)
+                        assert gx * per_group >= cols and gy == ksplit, key
+                    else:
+                        per_group = tile // (2 if gelu else 1)
+                        assert gx * per_group >= cols and gy * 192 >= M and gz == ksplit, key
+    assert accepted > 1000 and refused > 0
+
+
+def test_partial_offsets_fit_32_bits(lib):
+    """A skinny split-K shape whose partials would span exactly 2^32 bytes
+    (M=50, N=65536, K=262144, FP8 weights: 256 splits x 2 row blocks x 2048
+    groups of 2 x 2 fragments) is refused rather than run with offsets that
+    wrap around."""
+    rc, info = vla.vla_gemm_plan(50, 65536, 262144, vla.VLA_WFMT_E4M3_OCP)
+    assert rc == vla.VLA_ESHAPE and info[7] >= (1 << 32)
+    assert rc_of("vla_gemm_fp8w", A16, None, A16, A16, None, None, A16, A16, 1 << 40, 50, 65536, 262144,
+                 None) == vla.VLA_ESHAPE
+
+
+def test_wait_limit_and_status_arguments(lib):
+    """The status query validates its pointer before any device access; the
+    wait bound is a plain setter (0 restores the default)."""
+    assert rc_of("vla_workspace_status", None, None) == vla.VLA_EINVAL
+    assert rc_of("vla_workspace_status", A16 + 4, None) == vla.VLA_EALIGN
+    vla.vla_set_wait_limit(5)
+    vla.vla_set_wait_limit(0)
+
+
+def test_staged_chain_errors(lib):
+    arr = (ctypes.c_void_p * 2)(A16, A16)
+    M, H, I, L = 50, 1024, 4096, 2
+    need = vla.vla_mlp_chain_scratch_bytes(M, H, I)
+    XI, XO, SC = 1 << 33, 1 << 34, 1 << 35
+    GU, ACT, DN, XL = 1 << 36, 1 << 37, 1 << 38, 1 << 39
+
+    def rc(gu=GU, act=ACT, dn=DN, xl=XL):
+        return rc_of("vla_mlp_chain_enqueue_staged", arr, arr, arr, arr, XI, XO, gu, act, dn, xl, SC, need, L, M,
+                     H, I, None)
+    assert rc(act=GU + 16) == vla.VLA_EINVAL                          # act over gu
+    assert rc(xl=SC + 256) == vla.VLA_EINVAL                          # per-layer x in scratch
+    assert rc(dn=XO) == vla.VLA_EINVAL                                # over x_out
+    assert rc(gu=GU + 8) == vla.VLA_EALIGN

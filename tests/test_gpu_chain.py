@@ -1,8 +1,9 @@
-"""GPU parity of the gated-MLP chain: the fused gate/up GELU*mul GEMM stage
-against the oracle fed the GPU's own inputs, the residual stage, eager vs
-graph replay (bitwise), graph purity under input mutation, and the 18-layer
-chain against the oracle's fp64 chain (per-stage bounds; end-to-end error
-and cosine reported)."""
+"""GPU parity of the gated-MLP chain, stage by stage on the GPU's own
+inputs: every layer's merged gate/up GEMM and down GEMM against the oracle
+GEMM (|y - y_ref| <= 4e-3 * sum |a w|), GELU*mul within one bf16 ulp of the
+oracle, and the residual add bit for bit; eager vs graph replay (bitwise)
+and graph purity under input mutation.  The end-to-end cosine against the
+oracle's fp64 chain is reported, not asserted."""
 import numpy as np
 import pytest
 import torch
@@ -90,6 +91,39 @@ def test_gelu_mul_stage_bias(M, I, K):
     assert int(host(ws[:61440]).view(np.uint32).sum()) == 0
 
 
+@pytest.mark.parametrize("M", [50, 200])
+def test_gelu_mul_tail_values(M):
+    """One-hot gate/up weights (scale 1) pass activation columns through as g
+    and u exactly, so GELU*mul sees constructed values: g across the negative
+    tail where gelu(g) is tiny (down to where it underflows) and across the
+    ordinary range, u from 1e-3 to 1e37 of both signs.  Every act within one
+    bf16 ulp of the oracle, for the skinny (M <= 64) and the wide epilogue."""
+    I, K = 64, 128
+    g_vals = np.concatenate([np.linspace(-12.5, -7.0, 45), np.linspace(-6.0, 6.0, 19)]).astype(np.float32)
+    rng = synthetic.rng(7300 + M)
+    u_mag = (10.0 ** rng.uniform(-3, 37, (M, I))).astype(np.float32) * rng.choice([-1.0, 1.0], (M, I)).astype(np.float32)
+    A = np.zeros((M, K), np.float32)
+    A[:, :I] = rng.permuted(np.tile(g_vals, (M, 1)), axis=1)
+    A[:, I:] = u_mag
+    A_bits = synthetic.fp32_to_bf16_bits(A)
+    q = np.zeros((2 * I, K), np.uint8)
+    q[np.arange(2 * I), np.arange(2 * I)] = 0x38                  # gate row j <- column j, up row j <- column I + j
+    ws = zeros_ws(vla.vla_gemm_workspace_bytes(M, 2 * I, K, 1))
+    act, gu = Guarded(M * I * 2), Guarded(M * 2 * I * 2)
+    vla.vla_gemm_fp8w_gelu_mul(dev(A_bits), dev(oracle.pack(q, 8)), dev(np.ones(2 * I, np.float32)), None,
+                               act.t, gu.t, ws, ws.numel(), M, I, K)
+    act.check(); gu.check()
+    gu_bits = gu.numpy(np.uint16).reshape(M, 2 * I)
+    assert np.array_equal(gu_bits, A_bits)                          # g and u are the columns, exactly
+    want = oracle.gelu_mul(A_bits[:, :I], A_bits[:, I:])
+    got = act.numpy(np.uint16).reshape(M, I)
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    ok = ((diff <= 1) & ((got >> 15) == (want >> 15))) | (got == want)
+    assert ok.all(), f"{(~ok).sum()} differ; g={bf16_f64(A_bits[:, :I][~ok])[:4]} u={bf16_f64(A_bits[:, I:][~ok])[:4]}"
+    wv = bf16_f64(want)
+    assert (wv != 0).mean() > 0.8 and ((wv != 0) & (np.abs(wv) < 1e-30)).mean() > 0.05   # tiny, not underflow
+
+
 def make_chain(L, M, H, I, seed=0):
     cw = ChainWeights(L, H, I, seed)
     x = synthetic.activations(M, H, synthetic.IDS["chain.x"] + seed)
@@ -106,41 +140,70 @@ def eager(cw, xin, xout, scratch, M):
     return host(xout).view(np.uint16).reshape(M, cw.H).copy()
 
 
-def test_chain_small_matches_oracle_stagewise():
+def stage_outputs(cw, xin, M, scratch):
+    """Run the staged chain; returns x_out and the per-layer stage arrays."""
+    L, H, I = cw.L, cw.H, cw.I
+    xout = torch.empty(M * H, dtype=torch.int16, device="cuda")
+    bufs = {k: Guarded(L * M * n * 2) for k, n in (("gu", 2 * I), ("act", I), ("down", H), ("x", H))}
+    vla.vla_mlp_chain_enqueue_staged(cw.wgu, cw.sgu, cw.wd, cw.sd, xin, xout, bufs["gu"].t, bufs["act"].t,
+                                     bufs["down"].t, bufs["x"].t, scratch, scratch.numel(), L, M, H, I)
+    for b in bufs.values():
+        b.check()
+    out = {k: b.numpy(np.uint16).reshape(L, M, -1) for k, b in bufs.items()}
+    return host(xout).view(np.uint16).reshape(M, H).copy(), out
+
+
+def check_stages(cw, x_in, st, M, tag):
+    """Every stage of every layer whose inputs and outputs are finite, each on
+    the GPU's own stage inputs.  Returns the number of layers checked."""
+    L, H, I = cw.L, cw.H, cw.I
+    finite = lambda b: bool(np.isfinite(bf16_f64(b)).all())
+    x = x_in
+    for l in range(L):
+        gu, act, down, xn = st["gu"][l], st["act"][l], st["down"][l], st["x"][l]
+        if not all(finite(b) for b in (x, gu, act, down, xn)):
+            print(f"{tag}: layer {l} holds non-finite values (bf16 overflow); stop", flush=True)
+            return l
+        # 1. merged gate/up GEMM
+        ref, yabs = oracle.gemm(bf16_f64(x), oracle.dequant_rows(cw.o_gu[l], cw.o_sgu[l]))
+        assert_gemm_close(gu, ref, yabs)
+        # 2. GELU-tanh(g) * u within one bf16 ulp (same sign)
+        want = oracle.gelu_mul(gu[:, :I], gu[:, I:])
+        diff = np.abs(act.astype(np.int32) - want.astype(np.int32))
+        assert np.all(((diff <= 1) & ((act >> 15) == (want >> 15))) | (act == want)), f"{tag} layer {l} gelu_mul"
+        # 3. down GEMM before the residual
+        ref, yabs = oracle.gemm(bf16_f64(act), oracle.dequant_rows(cw.o_d[l], cw.o_sd[l]))
+        assert_gemm_close(down, ref, yabs)
+        # 4. residual add, bit for bit
+        assert np.array_equal(xn, oracle.bf16_round(bf16_f64(x) + bf16_f64(down))), f"{tag} layer {l} residual"
+        x = xn
+    return L
+
+
+def test_chain_small_stagewise():
     L, M, H, I = 3, 50, 256, 512
     cw, x, xin, xout, scratch = make_chain(L, M, H, I, seed=1)
     got = eager(cw, xin, xout, scratch, M)
-    # replay the oracle one layer at a time on the GPU's own layer input
-    # (run the GPU chain with 1..L layers to get its intermediate x)
-    xs = [x]
-    for l in range(1, L + 1):
-        sub = ChainSub(cw, l)
-        xs.append(eager(sub, xin, xout, scratch, M))
-    assert np.array_equal(xs[-1], got)
-    for l in range(L):
-        ref = oracle.mlp_chain(xs[l], [cw.o_gu[l]], [cw.o_sgu[l]], [cw.o_d[l]], [cw.o_sd[l]])
-        a, b = bf16_f64(xs[l + 1]), bf16_f64(ref)
-        rel = np.abs(a - b) / np.maximum(np.abs(b), 1e-3)
-        assert np.percentile(rel, 99) < 2e-2 and np.max(np.abs(a - b)) < 0.05 * np.max(np.abs(b))
+    staged_out, st = stage_outputs(cw, xin, M, scratch)
+    assert np.array_equal(staged_out, got) and np.array_equal(st["x"][-1], got)
+    assert check_stages(cw, x, st, M, "small") == L
 
 
-class ChainSub:
-    """The first l layers of a ChainWeights (same device tensors)."""
-
-    def __init__(self, cw, l):
-        self.L, self.H, self.I = l, cw.H, cw.I
-        self.wgu, self.sgu, self.wd, self.sd = cw.wgu[:l], cw.sgu[:l], cw.wd[:l], cw.sd[:l]
+@pytest.mark.parametrize("M,H,I", [(17, 96, 160), (130, 256, 512)])
+def test_chain_ragged_and_wide_stagewise(M, H, I):
+    """Ragged rows and tiles, and M > 64 (the wide kernel's fused epilogues)."""
+    L = 2
+    cw, x, xin, xout, scratch = make_chain(L, M, H, I, seed=3)
+    got = eager(cw, xin, xout, scratch, M)
+    staged_out, st = stage_outputs(cw, xin, M, scratch)
+    assert np.array_equal(staged_out, got)
+    assert check_stages(cw, x, st, M, f"M={M}") == L
 
 
 def test_chain_config_replay_eager_purity():
     """18 layers, M=50, H=1024, I=4096: graph replay == eager bitwise; replay
-    after mutating x_in equals a fresh eager run; every layer close to the
-    oracle's layer applied to the GPU's own layer input.
-
-    With the configured N(0, 0.02) weights and no normalisation between
-    layers, the residual stream grows quadratically and overflows bf16 near
-    layer 16 on both sides; the per-layer comparison covers the layers whose
-    input is still finite and below 1e4 in magnitude."""
+    after mutating x_in equals a fresh eager run (the recorded region is a
+    pure function of its device inputs); replay after destroy raises."""
     L, M, H, I = 18, 50, 1024, 4096
     print("chain config: building weights", flush=True)
     cw, x, xin, xout, scratch = make_chain(L, M, H, I)
@@ -172,22 +235,28 @@ def test_chain_config_replay_eager_purity():
         vla.vla_mlp_chain_destroy(h)
     with pytest.raises(RuntimeError, match="vla_mlp_chain_replay"):
         vla.vla_mlp_chain_replay(h, stream)
-    # per layer: the GPU's x_l (chain truncated to l layers) through one oracle layer
-    print("chain config: per-layer oracle", flush=True)
-    prev = x
-    checked = 0
-    for l in range(L):
-        cur = eager(ChainSub(cw, l + 1), xin, xout, scratch, M)
-        pv = bf16_f64(prev)
-        if not np.isfinite(pv).all() or np.abs(pv).max() > 1e4:
-            break
-        ref = oracle.mlp_chain(prev, [cw.o_gu[l]], [cw.o_sgu[l]], [cw.o_d[l]], [cw.o_sd[l]])
-        a, b = bf16_f64(cur).ravel(), bf16_f64(ref).ravel()
-        cos = float(a @ b / np.linalg.norm(a) / np.linalg.norm(b))
-        rel = np.abs(a - b) / np.maximum(np.abs(b), 1e-3)
-        print(f"layer {l}: max|x|={np.abs(b).max():.4g} cosine={cos:.7f} p99 rel={np.percentile(rel, 99):.3g}", flush=True)
-        assert cos > 0.9999 and np.percentile(rel, 99) < 2e-2
-        prev = cur
-        checked += 1
-    assert np.array_equal(prev, ref_eager) or checked >= 10
-    assert checked >= 10
+    vla.vla_workspace_status(scratch)
+
+
+def test_chain_config_stagewise():
+    """18 layers, M=50, H=1024, I=4096, every stage of every layer on the
+    GPU's own stage inputs.  With the configured N(0, 0.02) weights and no
+    normalisation between layers the residual stream grows quadratically
+    and overflows bf16 in the last layers (the oracle's fp64 chain does the
+    same); every layer before the first non-finite value is checked.  The
+    staged run's output equals the plain chain's bit for bit."""
+    L, M, H, I = 18, 50, 1024, 4096
+    print("chain stages: building weights", flush=True)
+    cw, x, xin, xout, scratch = make_chain(L, M, H, I)
+    ref_eager = eager(cw, xin, xout, scratch, M)
+    staged_out, st = stage_outputs(cw, xin, M, scratch)
+    assert np.array_equal(staged_out, ref_eager)
+    checked = check_stages(cw, x, st, M, "config")
+    print(f"chain stages: {checked} of {L} layers checked stage by stage", flush=True)
+    assert checked >= 12
+    # reported only: end-to-end agreement with the oracle's fp64 chain over the checked layers
+    o_x = oracle.mlp_chain(x, cw.o_gu[:checked], cw.o_sgu[:checked], cw.o_d[:checked], cw.o_sd[:checked])
+    a, b = bf16_f64(st["x"][checked - 1]).ravel(), bf16_f64(o_x).ravel()
+    print(f"chain end to end after {checked} layers: cosine {float(a @ b / np.linalg.norm(a) / np.linalg.norm(b)):.7f}",
+          flush=True)
+    vla.vla_workspace_status(scratch)
