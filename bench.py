@@ -10,12 +10,22 @@ resident in HBM before timing starts.
 
 Cache regime: "cold" (default) rotates every step through distinct copies of
 the packed weights totalling >= 1 GiB, so weights stream from HBM rather than
-the 256 MB Infinity Cache; "warm" reuses one copy.
+the 256 MB Infinity Cache, and writes a 1 GiB buffer right before every timed
+replay, so no copy the replay reads is cache-resident at any step count;
+"warm" reuses one copy and skips the flush.
 
 Timing: W untimed warmup steps, then K steps recorded once into a HIP graph
-(the way the pages run inference) and replayed between HIP events on the
-launch stream, with torch.cuda.synchronize() on both sides.  value = mean
-microseconds per GEMM call (lower is better).
+(the way the pages run inference), one untimed replay, the cache flush, and
+one replay timed between HIP events on the launch stream, with
+torch.cuda.synchronize() on both sides.  value = mean microseconds per GEMM
+call of that replay (lower is better); six more flushed replays give the
+p10/p50/p90 spread.  A one-workgroup marker kernel runs right before and
+right after the timed replay (outside the events), so a kernel trace of this
+command can pick out exactly the timed dispatches:
+
+    rocprofv3 --kernel-trace --stats -d DIR -o run --output-format csv -- \
+        python3 bench.py --gpus 1 --steps 20 --warmup 5
+    python3 bench.py --trace-summary DIR --bench-json <the JSON line's file>
 
 Prints one JSON line.  --gpus above 1 exits: this path runs on one GPU.
 """
@@ -66,7 +76,14 @@ def main():
     ap.add_argument("--wide-only", action="store_true",
                     help="only run the M = 768 encoder GEMMs (W8A16 and FP8 x FP8, both shapes, 8 calls "
                          "each; the workload of the wide-kernel counter runs) and exit")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="summarize a rocprofv3 kernel trace of this script (no GPU work): the dispatches "
+                         "between the two marker kernels, i.e. the headline's timed replay, and exit")
+    ap.add_argument("--bench-json", metavar="FILE", help="with --trace-summary: the bench's output, to compare")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.bench_json)
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(the GEMMs shard by output columns with no exchange; see the design notes)",
@@ -145,8 +162,27 @@ def main():
         vla.vla_gemm_fp8w(A_up, None, qs_up[c], s_up, None, None, Y_up, ws, ws_bytes, *UP)
         vla.vla_gemm_fp8w(A_dn, None, qs_dn[c], s_dn, None, None, Y_dn, ws, ws_bytes, *DOWN)
 
-    def time_graph(fn, n, reps=1):
-        """Record fn(0..n-1) into one graph; replay `reps` times; ms per replay."""
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cache == "cold" else None
+    flush_val = [0]
+    marker_sink = torch.zeros(64, dtype=torch.int32, device=dev)
+
+    def flush():
+        """Write 1 GiB (4x the Infinity Cache) so nothing read next is cache-resident."""
+        if flush_buf is not None:
+            flush_val[0] = (flush_val[0] + 1) & 0xFF
+            flush_buf.fill_(flush_val[0])
+
+    def marker():
+        # one workgroup of the streaming-read probe over 16 bytes: the only
+        # one-workgroup dispatch this script makes, so a kernel trace can
+        # find the timed replay between two of them
+        vla.vla_probe_stream_read(marker_sink, 16, marker_sink[16:], 1)
+
+    def time_graph_all(fn, n, reps=1, cold=None, mark=False):
+        """Record fn(0..n-1) into one graph, replay once untimed, then `reps`
+        times, each after the cache flush (cold regime) and between HIP
+        events; returns the ms of each timed replay."""
+        cold = (args.cache == "cold") if cold is None else cold
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -156,13 +192,26 @@ def main():
                 fn(i)
         g.replay()                      # one untimed replay
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+        out = []
+        for r in range(reps):
+            if cold:
+                flush()
+            if mark and r == 0:
+                marker()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+            e1.record()
+            if mark and r == 0:
+                marker()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        del g
+        return out
+
+    def time_graph(fn, n, cold=None):
+        return time_graph_all(fn, n, 1, cold)[0]
 
     def time_eager(fn, n):
         torch.cuda.synchronize()
@@ -179,13 +228,15 @@ def main():
         step(i)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    ms_graph = time_graph(step, args.steps)
+    reps = time_graph_all(step, args.steps, reps=7, mark=True)
+    ms_graph = reps[0]                  # the headline: exactly K steps, one replay
+    us_reps = np.array(reps) * 1000.0 / (2 * args.steps)
     ms_eager = time_eager(step, args.steps)
     us_call = ms_graph * 1000.0 / (2 * args.steps)
     bytes_step = alg_bytes_fp8w(*UP) + alg_bytes_fp8w(*DOWN)
     achieved = bytes_step / (ms_graph * 1e-3 / args.steps) / 1e9
     floor_buf = torch.zeros(1, device=dev)
-    floor_us = time_graph(lambda i: floor_buf.fill_(1.0), args.steps) * 1000.0 / args.steps
+    floor_us = time_graph(lambda i: floor_buf.fill_(1.0), args.steps, cold=False) * 1000.0 / args.steps
     # streaming-read floor: one launch that only reads one call's 4 MiB of
     # packed weights (same cold rotation as the GEMM pair), best launch size
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -197,6 +248,8 @@ def main():
         read_us[blocks] = time_graph(rd, 2 * args.steps) * 1000.0 / (2 * args.steps)
     best_blocks = min(read_us, key=read_us.get)
     extra = {
+        "us_per_call_p10_p50_p90": [round(float(np.percentile(us_reps, q)), 3) for q in (10, 50, 90)],
+        "timed_replays_for_spread": len(reps),
         "us_per_call_eager": round(ms_eager * 1000.0 / (2 * args.steps), 3),
         "graph_launch_floor_us": round(floor_us, 3),
         "stream_read_4MiB_us": round(read_us[best_blocks], 3),
@@ -298,10 +351,14 @@ def main():
         "config": {
             "workload": "action-decoder skinny FP8-weight GEMM pair, M=50: up 1024->4096 + down 4096->1024",
             "M": M, "hidden": H, "intermediate": I, "weights": "OCP E4M3, per-output-channel fp32 scale",
-            "cache": args.cache, "timing": "HIP graph of K steps replayed between HIP events",
+            "cache": args.cache + (" (1 GiB weight rotation + 1 GiB flush before the timed replay)"
+                                   if args.cache == "cold" else ""),
+            "timing": "HIP graph of K steps replayed once between HIP events",
         },
         "roofline": {
             "bound": "hbm",
+            "kernel": "skinny_gemm_kernel (FP8 weights, bf16 activations), up and down launches",
+            "bytes_per_launch": bytes_step // 2,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -517,27 +574,159 @@ def measured_traffic():
         return None
 
 
+def host_facts():
+    """CPU model, the NUMA node of the GPU (from its PCI device) and of this
+    process's CPUs, as far as the host exposes them."""
+    facts = {"cpu_model": None, "nproc": os.cpu_count(), "gpu_numa_node": None, "process_numa_nodes": None}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                facts["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        import torch
+
+        p = torch.cuda.get_device_properties(0)
+        bus = "%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0), p.pci_bus_id, p.pci_device_id)
+        facts["gpu_pci"] = bus
+        facts["gpu_numa_node"] = int(open(f"/sys/bus/pci/devices/{bus}/numa_node").read())
+    except Exception:       # properties or sysfs not available: leave it unknown
+        pass
+    try:
+        cpus = os.sched_getaffinity(0)
+        facts["process_cpus"] = len(cpus)
+        nodes = set()
+        base = "/sys/devices/system/node"
+        for d in os.listdir(base):
+            if d.startswith("node"):
+                lst = open(os.path.join(base, d, "cpulist")).read().strip()
+                ids = set()
+                for part in lst.split(","):
+                    if "-" in part:
+                        a, b = part.split("-")
+                        ids.update(range(int(a), int(b) + 1))
+                    elif part:
+                        ids.add(int(part))
+                if ids & cpus:
+                    nodes.add(int(d[4:]))
+        facts["process_numa_nodes"] = sorted(nodes)
+    except (OSError, ValueError):
+        pass
+    return facts
+
+
 def cpu_baseline(np, synthetic, W_up, W_dn):
     """The oracle (unchanged) on the same workload: dequantize + fp64 GEMM per
-    call, alternating up and down, for about 10 s of host time."""
+    call, alternating up and down.  Three timed runs of about 4 s on all the
+    threads OpenMP uses (median reported), then one pair of calls on a single
+    thread."""
+    import ctypes
+
     import oracle
 
     A_up = oracle.bf16_value(synthetic.activations(M, H, synthetic.IDS["skinny.up.A"]))
     A_dn = oracle.bf16_value(synthetic.activations(M, I, synthetic.IDS["skinny.down.A"]))
     q_up, s_up = oracle.quantize_rows(W_up, oracle.OCP)
     q_dn, s_dn = oracle.quantize_rows(W_dn, oracle.OCP)
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        for A, q, s in ((A_up, q_up, s_up), (A_dn, q_dn, s_dn)):
-            oracle.gemm(A, oracle.dequant_rows(q, s))
-            calls += 1
-        el = time.perf_counter() - t0
-        if el >= 10.0 or calls >= 2000:
-            break
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(el * 1e6 / calls, 1), "unit": "µs/call", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} calls (alternating up/down, M=50) of dequantize + fp64 GEMM, {el:.1f} s"}
+    work = ((A_up, q_up, s_up), (A_dn, q_dn, s_dn))
+
+    def run(seconds, max_pairs):
+        calls = 0
+        t0 = time.perf_counter()
+        while True:
+            for A, q, s in work:
+                oracle.gemm(A, oracle.dequant_rows(q, s))
+                calls += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or calls >= 2 * max_pairs:
+                return el * 1e6 / calls, calls, el
+
+    gomp = None
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        threads = int(gomp.omp_get_max_threads())
+    except OSError:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    runs = [run(4.0, 1000) for _ in range(3)]
+    us = sorted(r[0] for r in runs)
+    one = None
+    if gomp is not None:
+        gomp.omp_set_num_threads(1)
+        one = run(0.0, 1)[0]               # one up + one down call
+        gomp.omp_set_num_threads(threads)
+    facts = host_facts()
+    total_s = sum(r[2] for r in runs)
+    return {"value": round(us[1], 1), "unit": "µs/call", "cores": threads, "kind": "oracle",
+            "sample": (f"3 runs of {runs[0][1]}-{runs[-1][1]} calls (alternating up/down, M=50) of dequantize + "
+                       f"fp64 GEMM, {total_s:.1f} s; value = median run, {threads} OpenMP threads"),
+            "runs_us": [round(v, 1) for v in us],
+            "one_thread_us": None if one is None else round(one, 1),
+            "cpu_model": facts["cpu_model"], "nproc": facts["nproc"],
+            "gpu_numa_node": facts["gpu_numa_node"], "process_numa_nodes": facts["process_numa_nodes"]}
+
+
+def trace_summary(trace_dir, bench_json=None):
+    """Summarize a rocprofv3 kernel trace of this script: the dispatches
+    between the first two one-workgroup marker kernels (the headline's timed
+    replay), per kernel name, against the bench's HIP-event figure."""
+    import csv
+    import glob
+    import statistics
+
+    files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        sys.exit(f"no *kernel_trace.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+
+    def col(row, *names):
+        for n in names:
+            if n in row:
+                return row[n]
+        raise KeyError(names)
+    recs = []
+    for r in rows:
+        grid = int(col(r, "Grid_Size_X", "Grid_Size")) * int(r.get("Grid_Size_Y", 1)) * int(r.get("Grid_Size_Z", 1))
+        wg = int(col(r, "Workgroup_Size_X", "Workgroup_Size")) * int(r.get("Workgroup_Size_Y", 1)) * \
+            int(r.get("Workgroup_Size_Z", 1))
+        recs.append((int(col(r, "Start_Timestamp")), int(col(r, "End_Timestamp")), col(r, "Kernel_Name"), grid, wg))
+    recs.sort()
+    marks = [i for i, r in enumerate(recs) if "stream_read" in r[2] and r[3] == r[4]]
+    if len(marks) < 2:
+        sys.exit("marker dispatches not found")
+    timed = recs[marks[0] + 1:marks[1]]
+    by = {}
+    for st, en, name, grid, wg in timed:
+        by.setdefault((name, grid // wg, wg), []).append(en - st)
+    span_ns = timed[-1][1] - timed[0][0]
+    gaps = [timed[i + 1][0] - timed[i][1] for i in range(len(timed) - 1)]
+    print(f"# rocprofv3 kernel trace: {os.path.relpath(files[0], trace_dir)}")
+    print(f"dispatches in the timed replay: {len(timed)}")
+    total = 0.0
+    for (name, groups, wg), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        short = name.split("(")[0][:160]
+        total += sum(d)
+        print(f"kernel: {short}")
+        print(f"  workgroups {groups} x {wg} threads; dispatches {len(d)}; mean {statistics.mean(d) / 1e3:.3f} us; "
+              f"median {statistics.median(d) / 1e3:.3f} us; min {min(d) / 1e3:.3f} us; max {max(d) / 1e3:.3f} us")
+    print(f"mean kernel duration over all timed dispatches: {total / len(timed) / 1e3:.3f} us")
+    print(f"first start to last end: {span_ns / 1e3:.3f} us = {span_ns / 1e3 / len(timed):.3f} us per dispatch")
+    print(f"gap between consecutive dispatches: mean {statistics.mean(gaps) / 1e3:.3f} us, "
+          f"median {statistics.median(gaps) / 1e3:.3f} us")
+    if bench_json:
+        line = [l for l in open(bench_json) if l.startswith("{")][-1]
+        b = json.loads(line)
+        ev_us = b["ms_per_step"] * 1000.0 / 2
+        print(f"bench (same run, HIP events around the same replay): {b['ms_per_step'] * 1000:.3f} us per step "
+              f"= {ev_us:.3f} us per call")
+        print(f"mean kernel duration x 2 = {2 * total / len(timed) / 1e3:.3f} us <= ms_per_step "
+              f"{b['ms_per_step'] * 1000:.3f} us: {2 * total / len(timed) / 1e3 <= b['ms_per_step'] * 1000}")
+        nbytes = b["roofline"].get("bytes_per_launch", (alg_bytes_fp8w(*UP) + alg_bytes_fp8w(*DOWN)) // 2)
+        print(f"algorithmic bytes per launch {nbytes}: over the kernel's own duration "
+              f"{nbytes / (total / len(timed)):.1f} GB/s ({nbytes / (total / len(timed)) / HBM_PEAK_GBS:.4f} of "
+              f"8 TB/s); over the event time per call {nbytes / (ev_us * 1e3):.1f} GB/s "
+              f"({nbytes / (ev_us * 1e3) / HBM_PEAK_GBS:.4f}, the bench's roofline.frac {b['roofline']['frac']})")
 
 
 if __name__ == "__main__":

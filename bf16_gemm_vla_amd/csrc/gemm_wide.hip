@@ -531,9 +531,11 @@ void wide_gemm_kernel(KArgs a) {
                 for (int ms = 0; ms < C::MSUB; ++ms)
                     if (((handed >> ms) & 1u) || ms >= a.ksplit) mine |= 1u << ms;
             }
+            uint32_t poison = 0;
             if (wait_own) {
-                // bounded: an owner that gives up leaves its slice unwritten
-                // and records that in the workspace's status word
+                // bounded: an owner that gives up writes NaN over its slice
+                // (the incomplete output shows in the data) and records the
+                // cause in the workspace's status word
                 bool arrived = false;
                 for (uint32_t it = 0; it < a.wait_polls; ++it) {
                     if ((__hip_atomic_load(ctr + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFFFFu) == ks) {
@@ -542,8 +544,11 @@ void wide_gemm_kernel(KArgs a) {
                     }
                     __builtin_amdgcn_s_sleep(2);
                 }
-                if (arrived) mine |= 1u << own;
-                else report_wait_timeout(a.err, kStatusWideSplitK);
+                mine |= 1u << own;
+                if (!arrived) {
+                    poison = 1u << own;
+                    report_wait_timeout(a.err, kStatusWideSplitK);
+                }
             }
             // no counter of the tile is read after this point; the last
             // workgroup past it clears them for the next call
@@ -553,13 +558,20 @@ void wide_gemm_kernel(KArgs a) {
                 __hip_atomic_store(ctr + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             flags[0] = static_cast<int>(mine);
+            flags[1] = static_cast<int>(poison);
         }
         __syncthreads();
         todo = static_cast<uint32_t>(flags[0]);
+        const uint32_t poisoned = static_cast<uint32_t>(flags[1]);
         if (todo == 0) return;
 #pragma unroll
         for (int ms = 0; ms < C::MSUB; ++ms) {
             if (!(todo & (1u << ms))) continue;
+            if (poisoned & (1u << ms)) {
+#pragma unroll
+                for (int ns = 0; ns < C::NSUB; ++ns) acc[ns][ms] = Acc{} + __builtin_nanf("");
+                continue;
+            }
             // two splits' loads in flight at a time, summed in split order
             f32x4_t sum[C::NSUB][4];
             for (int sp = 0; sp < a.ksplit; sp += 2) {

@@ -71,8 +71,8 @@ const char *vla_last_error(void);
 
 /* Bounded in-kernel waits.  Kernels that wait for other workgroups (the wide
  * GEMM's split-K hand-over, the fused chain's phase barriers) poll at most
- * `polls` times (about 0.5 us per poll), then give up, leave the output they
- * were waiting to produce unwritten, record the cause in the workspace's
+ * `polls` times (about 0.5 us per poll), then give up, write NaN over the
+ * output they were waiting to produce, record the cause in the workspace's
  * status word and exit normally, so no wait can hang the device.  0 restores
  * the default (2^22 polls, never reached by a grid that is resident).  The
  * bound is read when a call is enqueued (or captured).  Process-wide. */

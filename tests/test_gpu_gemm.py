@@ -277,8 +277,9 @@ def test_wide_splitk_wait_is_bounded():
     """The wide kernel's split-K owners wait for the other splits' partials
     with a bounded poll.  With the bound forced down to one poll from the
     host, owners that would wait give up: every workgroup still exits, the
-    call completes, the workspace's counters are cleared, and the status
-    query reports the incomplete output.  With the bound restored the same
+    call completes, the workspace's counters are cleared, the slices left
+    unfinished read NaN, and the status query reports them.  With the bound
+    restored the same
     workspace gives the full, correct result."""
     M, N, K = 768, 2048, 16384
     info = plan(M, N, K)
@@ -296,6 +297,7 @@ def test_wide_splitk_wait_is_bounded():
         vla.vla_set_wait_limit(0)
     torch.cuda.synchronize()
     assert int(host(ws[:61440]).view(np.uint32).sum()) == 0
+    assert np.isnan(bf16_f64(host(Y, np.uint16))).any()      # the unfinished slices read NaN
     with pytest.raises(RuntimeError, match="wait gave up"):
         vla.vla_workspace_status(ws)
     vla.vla_workspace_status(ws)                             # the query cleared the word
