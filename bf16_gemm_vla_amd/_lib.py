@@ -56,6 +56,7 @@ SIGNATURES = {
     "vla_gemm_workspace_bytes": (SZ, [I64, I64, I64, INT]),
     "vla_gemm_supported": (INT, [I64, I64, I64, INT, INT, INT]),
     "vla_gemm_fp8w": (INT, [P, P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
+    "vla_gemm_fp8w_noalloc": (INT, [P, P, P, P, P, P, P, I64, I64, I64, P]),
     "vla_gemm_bf16": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_gemm_mxfp4w": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_gemm_fp8w_gelu_mul": (INT, [P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
@@ -211,6 +212,11 @@ def vla_gemm_fp8w(A, s_a, Wq, s_w, bias, residual, Y, ws, ws_bytes, M, N, K, str
     _check(load().vla_gemm_fp8w(_ptr(A), _ptr(s_a), _ptr(Wq), _ptr(s_w), _ptr(bias),
                                 _ptr(residual), _ptr(Y), _ptr(ws), ws_bytes, M, N, K,
                                 _stream(stream)), "vla_gemm_fp8w")
+
+
+def vla_gemm_fp8w_noalloc(A, s_a, Wq, s_w, bias, residual, Y, M, N, K, stream=None):
+    _check(load().vla_gemm_fp8w_noalloc(_ptr(A), _ptr(s_a), _ptr(Wq), _ptr(s_w), _ptr(bias), _ptr(residual),
+                                        _ptr(Y), M, N, K, _stream(stream)), "vla_gemm_fp8w_noalloc")
 
 
 def vla_gemm_bf16(A, Wq, bias, residual, Y, ws, ws_bytes, M, N, K, stream=None):

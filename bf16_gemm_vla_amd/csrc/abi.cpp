@@ -593,6 +593,39 @@ int vla_gemm_fp8w(const void* A, const float* s_a, const uint8_t* Wq, const floa
     return run_gemm(fn, p, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+int vla_gemm_fp8w_noalloc(const void* A, const float* s_a, const uint8_t* Wq, const float* s_w,
+                          const uint16_t* bias, const uint16_t* residual, uint16_t* Y, int64_t M, int64_t N,
+                          int64_t K, void* stream) {
+    const char* fn = "vla_gemm_fp8w_noalloc";
+    if (int rc = check_mnk(fn, M, N, K)) return rc;
+    REQUIRE_PTR(A);
+    OPTIONAL_PTR(s_a);
+    REQUIRE_PTR(Wq);
+    REQUIRE_PTR(s_w);
+    OPTIONAL_PTR(bias);
+    OPTIONAL_PTR(residual);
+    REQUIRE_PTR(Y);
+    vla::GemmProblem p{};
+    p.A = A; p.s_a = s_a; p.W = Wq; p.s_w = s_w; p.bias = bias; p.resid = residual; p.Y = Y;
+    p.M = M; p.N = N; p.K = K;
+    p.atype = s_a ? vla::AType::FP8 : vla::AType::BF16;
+    p.wtype = vla::WType::FP8;
+    p.epi = vla::Epi::PLAIN;
+    // refuse what the library's workspace cannot hold before any device work
+    const vla::GemmPlan plan = vla::plan_gemm(M, N, K, p.atype, p.wtype, p.epi);
+    if (!vla::plan_dispatchable(plan, p.atype, p.wtype, p.epi))
+        return fail(VLA_ESHAPE, fn, "M=%lld N=%lld K=%lld exceeds the kernels' limits", (long long)M, (long long)N,
+                    (long long)K);
+    const size_t need = vla::gemm_ws_bytes(plan, M, N);
+    if (need > vla::kNoAllocWorkspaceBytes)
+        return fail(VLA_EWORKSPACE, fn, "M=%lld N=%lld K=%lld needs a %zu-byte workspace; the library's holds %zu",
+                    (long long)M, (long long)N, (long long)K, need, vla::kNoAllocWorkspaceBytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = vla::noalloc_workspace(s, &p.ws);
+    if (e != hipSuccess) return hip_fail(fn, "workspace set-up", e);
+    return run_gemm(fn, p, vla::kNoAllocWorkspaceBytes, s);
+}
+
 int vla_gemm_bf16(const uint16_t* A, const uint16_t* Wq, const uint16_t* bias,
                   const uint16_t* residual, uint16_t* Y, void* ws, size_t ws_bytes, int64_t M,
                   int64_t N, int64_t K, void* stream) {

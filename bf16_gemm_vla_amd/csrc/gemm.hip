@@ -18,6 +18,7 @@
 // partials and counts its arrival; the last to arrive sums the partials in
 // split order (bitwise repeatable) and runs the epilogue.
 #include <algorithm>
+#include <mutex>
 
 #include "gemm_common.h"
 
@@ -534,6 +535,60 @@ bool plan_dispatchable(const GemmPlan& p, AType at, WType wt, Epi epi) {
     VLA_SKINNY_CONFIGS(VLA_CASE)
 #undef VLA_CASE
     return false;
+}
+
+// ------------------------------------------------ library-owned workspace
+
+namespace {
+
+// The workspace of vla_gemm_fp8w_noalloc: one per GPU, in the code object's
+// device memory, held until the process ends.  In host code `scratch` is
+// only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed to
+// kernels.
+static __device__ __align__(256) uint8_t scratch[kNoAllocWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_clear[kMaxDevices] = {};
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+}  // namespace
+
+hipError_t noalloc_workspace(hipStream_t s, void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    if (!g_scratch_clear[dev]) {
+        // the split-K counters and the status word must start at zero (every
+        // completed call leaves the counters at zero again); cleared by a
+        // kernel, not a memset, so a capturing caller records a kernel node
+        zero_words_kernel<<<16, 256, 0, s>>>(static_cast<uint32_t*>(g_scratch_ptr[dev]),
+                                             static_cast<int>(kCounterBytes / 4));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(s, &cs);
+        if (e != hipSuccess) return e;
+        // under capture the clear runs only when the graph does: keep clearing
+        // until a call runs eagerly
+        if (cs == hipStreamCaptureStatusNone) g_scratch_clear[dev] = true;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace vla

@@ -89,6 +89,13 @@ constexpr uint64_t kMaxPartBytes = uint64_t(1) << 32;
 constexpr uint32_t kDefaultWaitPolls = 1u << 22;
 uint32_t wait_polls();                  // current bound (vla_set_wait_limit)
 
+// vla_gemm_fp8w_noalloc's workspace: counters (64 KiB) + up to 32 MiB of
+// split-K partials, enough for the encoder GEMMs at 768 rows.
+constexpr size_t kNoAllocWorkspaceBytes = kCounterBytes + (size_t(32) << 20);
+// Device address of the library's workspace on the current device (set up
+// on first use per device; its counters are cleared by a kernel on `s`).
+hipError_t noalloc_workspace(hipStream_t s, void** ptr);
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi);
 size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N);
 hipError_t launch_gemm(const GemmProblem& pr, hipStream_t s);

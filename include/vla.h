@@ -259,6 +259,26 @@ int vla_gemm_fp8w(const void *A, const float *s_a, const uint8_t *Wq, const floa
                   const uint16_t *bias, const uint16_t *residual, uint16_t *Y, void *ws,
                   size_t ws_bytes, int64_t M, int64_t N, int64_t K, void *stream);
 
+/* vla_gemm_fp8w without a workspace argument, for callers that cannot
+ * allocate device memory (code recorded under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * arithmetic, kernels and results as vla_gemm_fp8w.  The split-K counters
+ * and partials live in an array the library holds in each GPU's memory
+ * (65536 + 32 MiB bytes per GPU, until the process ends), set up on the
+ * first call on a device (its counters cleared by a kernel on `stream`);
+ * nothing is allocated and no hipMalloc, hipFree or allocating library call
+ * is made.  Shapes whose workspace (vla_gemm_workspace_bytes) exceeds that
+ * array fail with VLA_EWORKSPACE before any device work; every shape at or
+ * below 768 rows of the encoder sizes fits.  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (concurrent streams, or
+ * graphs replayed concurrently) race and give wrong results; calls that run
+ * one after another are safe.  A bounded split-K wait that gives up writes
+ * NaN over the output it could not finish (the status word is not
+ * reported for this variant). */
+int vla_gemm_fp8w_noalloc(const void *A, const float *s_a, const uint8_t *Wq, const float *s_w,
+                          const uint16_t *bias, const uint16_t *residual, uint16_t *Y, int64_t M,
+                          int64_t N, int64_t K, void *stream);
+
 /* As vla_gemm_fp8w with BF16 weights (VLA_LAYOUT_MFMA) and no weight scale:
  * Y = bf16( sum_k A[m,k] * Wq[n,k] + bias[n] ) (+ residual). */
 int vla_gemm_bf16(const uint16_t *A, const uint16_t *Wq, const uint16_t *bias,
