@@ -61,6 +61,7 @@ SIGNATURES = {
     "vla_gemm_mxfp4w": (INT, [P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_gemm_fp8w_gelu_mul": (INT, [P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_mlp_chain_scratch_bytes": (SZ, [I64, I64, I64]),
+    "vla_mlp_chain_fused_supported": (INT, [I64, I64, I64, INT]),
     "vla_mlp_chain_enqueue": (INT, [P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P]),
     "vla_mlp_chain_create": (INT, [P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P, P]),
     "vla_mlp_chain_replay": (INT, [P, P]),
@@ -163,6 +164,11 @@ def vla_workspace_status(ws, stream=None) -> None:
 
 def vla_mlp_chain_scratch_bytes(M: int, H: int, I: int) -> int:
     return load().vla_mlp_chain_scratch_bytes(M, H, I)
+
+
+def vla_mlp_chain_fused_supported(M: int, H: int, I: int, L: int) -> bool:
+    """Whether the chain runs as one persistent launch on the current device."""
+    return bool(load().vla_mlp_chain_fused_supported(M, H, I, L))
 
 
 # ----------------------------------------------------------------- codecs

@@ -21,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["codec.hip", "gemm.hip", "gemm_wide.hip", "boundary.hip", "probe.hip", "abi.cpp"]
+SOURCES = ["codec.hip", "gemm.hip", "gemm_wide.hip", "chain.hip", "boundary.hip", "probe.hip", "abi.cpp"]
 HIPFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -52,6 +52,14 @@ def build() -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
+    # A kernel template whose body the host pass cannot instantiate loses its
+    # launch stub without a diagnostic; the library would then fail to load.
+    # Refuse to install a library with undefined symbols of its own.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    own = [l.split()[-1] for l in nm.stdout.splitlines() if "_ZN3vla" in l]
+    if nm.returncode != 0 or own:
+        os.remove(tmp)
+        raise RuntimeError("libvla.so has undefined symbols of its own: " + ", ".join(own[:8]))
     os.replace(tmp, LIB)
     return LIB
 

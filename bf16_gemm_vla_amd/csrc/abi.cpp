@@ -91,9 +91,13 @@ std::mutex g_chain_mu;
 std::unordered_set<const vla_mlp_chain*> g_chains;
 
 // Chain scratch: GEMM workspace (first, so its status word sits at the
-// same offset as in a plain GEMM workspace) | x | act.
+// same offset as in a plain GEMM workspace) | the fused chain's barrier
+// words | x | act.  The x and act areas
+// hold one buffer per layer for up to kMaxChainLayers layers: the fused
+// chain writes every intermediate once per launch (the graph of GEMMs uses
+// the first of each).
 struct ChainLayout {
-    size_t ws_off, x_off, act_off, total, ws_bytes;
+    size_t ws_off, sync_off, x_off, act_off, total, ws_bytes, x_stride, act_stride;
 };
 
 size_t round256(size_t v) { return (v + 255) / 256 * 256; }
@@ -109,9 +113,12 @@ ChainLayout chain_layout(int64_t M, int64_t H, int64_t I) {
     ChainLayout c{};
     c.ws_off = 0;
     c.ws_bytes = chain_ws_bytes(M, H, I);
-    c.x_off = c.ws_bytes;
-    c.act_off = c.x_off + round256(static_cast<size_t>(M) * H * 2);
-    c.total = c.act_off + round256(static_cast<size_t>(M) * I * 2);
+    c.x_stride = round256(static_cast<size_t>(M) * H * 2);
+    c.act_stride = round256(static_cast<size_t>(M) * I * 2);
+    c.sync_off = c.ws_bytes;
+    c.x_off = c.sync_off + vla::kChainSyncBytes;
+    c.act_off = c.x_off + (vla::kMaxChainLayers - 1) * c.x_stride;
+    c.total = c.act_off + vla::kMaxChainLayers * c.act_stride;
     return c;
 }
 
@@ -166,6 +173,33 @@ int enqueue_chain(const char* fn, const uint8_t* const* wgu, const float* const*
     uint16_t* act_buf = reinterpret_cast<uint16_t*>(base + c.act_off);
     void* ws = base + c.ws_off;
     const size_t mh = static_cast<size_t>(M) * H, mi = static_cast<size_t>(M) * I;
+    // The fused launch writes each layer's intermediates to their own
+    // buffers; no two layers' buffers may share a cache line (a line read for
+    // one layer would hold the next layer's bytes before they are written),
+    // so it needs 256-byte aligned buffers (every compiled configuration has
+    // per-layer sizes that are multiples of 256 bytes).
+    auto a256 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; };
+    const bool aligned = a256(scratch) && a256(st.gu) && a256(st.act) && a256(st.down) && a256(st.x) &&
+                         (mh * 2) % 256 == 0 && (mi * 2) % 256 == 0;
+    int npa = 0;
+    if (aligned && vla::chain_fused_plan(M, H, I, L, &npa) && vla::chain_fused_resident(H, I, npa)) {
+        // one persistent launch for every layer
+        vla::ChainLaunch cl{};
+        cl.wgu = wgu; cl.sgu = sgu; cl.wd = wd; cl.sd = sd;
+        cl.x_in = x_in; cl.x_out = x_out;
+        cl.xbuf = st.x ? st.x : xbuf;
+        cl.xstride = st.x ? static_cast<int64_t>(mh) : static_cast<int64_t>(c.x_stride / 2);
+        cl.xlast = st.x ? st.x + (L - 1) * mh : nullptr;
+        cl.actbuf = st.act ? st.act : act_buf;
+        // the kernel places act_l at actbuf + l * M * I; the scratch pads
+        // each to 256 bytes, which M * I * 2 already is when M * I % 128 == 0
+        cl.gu_out = st.gu; cl.down_out = st.down;
+        cl.sync = reinterpret_cast<uint32_t*>(base + c.sync_off);
+        cl.err = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + vla::kStatusOffset);
+        cl.L = L; cl.M = M; cl.H = H; cl.I = I;
+        hipError_t e = vla::launch_mlp_chain_fused(cl, s);
+        return e == hipSuccess ? VLA_OK : hip_fail(fn, "fused chain launch", e);
+    }
     const uint16_t* x = x_in;
     for (int l = 0; l < L; ++l) {
         uint16_t* act = st.act ? st.act + l * mi : act_buf;
@@ -745,6 +779,11 @@ int vla_mlp_chain_create(const uint8_t* const* wgu, const float* const* sgu,
     return capture_chain(fn, capture_stream, L, out, [&](hipStream_t s) {
         return enqueue_chain(fn, wgu, sgu, wd, sd, x_in, x_out, scratch, L, M, H, I, ChainStages{}, s);
     });
+}
+
+int vla_mlp_chain_fused_supported(int64_t M, int64_t H, int64_t I, int L) {
+    int npa = 0;
+    return (vla::chain_fused_plan(M, H, I, L, &npa) && vla::chain_fused_resident(H, I, npa)) ? 1 : 0;
 }
 
 size_t vla_decoder_chain_scratch_bytes(int64_t M, int64_t H, int64_t I) {

@@ -39,6 +39,10 @@ struct KArgs {
     int msplit;     // skinny kernel: activation row blocks (grid z)
 };
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (lgkmcnt and expcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 // ------------------------------------------------------------- epilogue
 
 // Epilogue inputs of one output fragment (row m, output columns n..n+3),

@@ -87,9 +87,6 @@ struct WideCfg {
     static_assert(WT != WType::FP4 || (AT == AType::BF16 && BK == 64), "MXFP4 weights: bf16 activations, 64 K per stage");
 };
 
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// are outstanding (lgkmcnt and expcnt left unconstrained).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // Global 16-row weight tile held in LDS tile slot tt of group g, or -1 when
 // the slot lies past the weight matrix.  For the fused gate/up epilogue

@@ -146,19 +146,32 @@ __device__ __forceinline__ float group_max(float v) {
 // GELU, tanh form, times u: 0.5 g (1 + tanh(z)) u, z = sqrt(2/pi) (g +
 // 0.044715 g^3), evaluated as g / (1 + exp(-2z)) * u (the same function:
 // 1 + tanh(z) = 2 / (1 + exp(-2z))), which keeps its relative accuracy for
-// negative g, where 1 + tanh(z) cancels to a few ulps or to zero in fp32;
-// the IEEE division keeps tiny results.  For z < -40 (g below about -9.2)
-// gelu(g) is below ~1e-34: in fp32 it reaches the subnormals (and exp(-2z)
-// overflows near g = -10.1) while gelu(g) * u can still be a normal number
-// when |u| is large, so that tail is evaluated in fp64, as
-// g e^{2z} / (1 + e^{2z}) * u.  Rare in practice (a wave takes the branch
-// only if one of its lanes needs it).
+// negative g, where 1 + tanh(z) cancels to a few ulps or to zero in fp32.
+// exp and the reciprocal are gfx950's exp2 and reciprocal instructions
+// (about 1 ulp of fp32 each): the result is rounded to bf16, 2^16 times
+// coarser, so they move it by at most one bf16 ulp, and only next to a
+// rounding boundary.
+// For z < -40 (g below about -9.2) gelu(g) = g e^{2z} / (1 + e^{2z}) is
+// below ~1e-34, where 1 + e^{2z} is 1 in fp32: the value is g u e^{2z},
+// whose factors would overflow (g u) or leave the normal range (e^{2z},
+// exp(-2z) overflowing near g = -10.1) while the product can still be a
+// normal number when |u| is large.  It is formed with exact exponents:
+// g = mg 2^eg, u = mu 2^eu (frexp), 2z log2(e) = ti + tf with ti an
+// integer and tf in [0, 1), then (mg mu 2^tf) 2^(eg + eu + ti) with one
+// rounding in ldexp.  Rare in practice (a wave takes the branch only if one
+// of its lanes needs it).
 __device__ __forceinline__ float gelu_mul(float g, float u) {
     const float c = 0.7978845608028654f;  // sqrt(2/pi)
     const float z = c * (g + 0.044715f * g * g * g);
-    if (z > -40.0f) return g / (1.0f + expf(-2.0f * z)) * u;
-    const double e = exp(2.0 * static_cast<double>(z));
-    return static_cast<float>(static_cast<double>(g) * e / (1.0 + e) * static_cast<double>(u));
+    if (z > -40.0f) {
+        const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * z);    // exp(-2z), -2 log2(e) z < 116
+        return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+    }
+    const float t = fmaxf(2.0f * z * 1.4426950408889634f, -2048.0f);   // log2 e^{2z}; below -2048 all underflow
+    const float ti = floorf(t);
+    int eg, eu;
+    const float mg = frexpf(g, &eg), mu = frexpf(u, &eu);
+    return ldexpf(mg * mu * exp2f(t - ti), eg + eu + static_cast<int>(ti));
 }
 
 }  // namespace vla

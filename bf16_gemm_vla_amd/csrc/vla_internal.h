@@ -96,6 +96,41 @@ constexpr size_t kNoAllocWorkspaceBytes = kCounterBytes + (size_t(32) << 20);
 // on first use per device; its counters are cleared by a kernel on `s`).
 hipError_t noalloc_workspace(hipStream_t s, void** ptr);
 
+// ------------------------------------------------------------ fused chain
+// One persistent launch of kChainGrid workgroups runs every layer of the
+// gated-MLP chain (chain.hip); the weight pointers travel in the kernel
+// arguments, so at most kMaxChainLayers layers.
+constexpr int kChainGrid = 256;
+constexpr int kMaxChainLayers = 32;
+// Barrier words of the fused chain (34 lines of 128 bytes), zero between
+// launches; the chain scratch holds them after its GEMM workspace.
+constexpr size_t kChainSyncBytes = 8192;
+
+struct ChainLaunch {
+    const uint8_t* const* wgu;     // host arrays of L device pointers
+    const float* const* sgu;
+    const uint8_t* const* wd;
+    const float* const* sd;
+    const uint16_t* x_in;
+    uint16_t* x_out;
+    uint16_t* xbuf;                // x after layers 0..L-2, xstride elements apart
+    uint16_t* actbuf;              // act of layers 0..L-1, M * I elements apart
+    uint16_t* gu_out;              // nullable per-layer stage outputs
+    uint16_t* down_out;
+    uint16_t* xlast;               // nullable second copy of the final x
+    uint32_t* sync;
+    uint32_t* err;
+    int64_t xstride;
+    int L;
+    int64_t M, H, I;
+};
+// Whether a compiled fused configuration covers (M, H, I, L); npa receives
+// the gate/up pairs per workgroup.
+bool chain_fused_plan(int64_t M, int64_t H, int64_t I, int L, int* npa);
+// Whether the fused grid can be resident at once on the current device.
+bool chain_fused_resident(int64_t H, int64_t I, int npa);
+hipError_t launch_mlp_chain_fused(const ChainLaunch& c, hipStream_t s);
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, AType at, WType wt, Epi epi);
 size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N);
 hipError_t launch_gemm(const GemmProblem& pr, hipStream_t s);

@@ -331,10 +331,25 @@ int vla_gemm_mxfp4w(const uint16_t *A, const uint8_t *Wq, const uint16_t *bias, 
  *   x_in      device bf16 M x H input (read only).
  *   x_out     device bf16 M x H output (must not overlap x_in or scratch).
  *   scratch   device, vla_mlp_chain_scratch_bytes(M, H, I) bytes,
- *             ZERO-FILLED before first use (it embeds a GEMM workspace).
+ *             ZERO-FILLED before first use (it embeds a GEMM workspace; its
+ *             per-layer buffers cover up to 32 layers).
  * Every device pointer must stay valid, at the same address, for the life
  * of a handle. */
 size_t vla_mlp_chain_scratch_bytes(int64_t M, int64_t H, int64_t I);
+
+/* 1 when the chain of this shape runs as one persistent launch on the
+ * current device, else 0 (then each layer runs as two GEMM launches).  The
+ * single launch covers M <= 64 rows with (H, I) = (1024, 4096) or
+ * (256, 512) and L <= 32, on a device whose 256 compute units can each hold
+ * one of its workgroups; the enqueue/create calls also need the scratch
+ * buffer (and any stage outputs) 256-byte aligned to take it.  It meets at a
+ * grid barrier between the gate/up and the down phase of each layer (every
+ * wait bounded, see vla_set_wait_limit; a give-up leaves NaN in x_out and
+ * sets the scratch buffer's status word) and streams each phase's weights
+ * while the previous phase finishes.  Both forms compute the same stages;
+ * their fp32 summation orders differ, so results may differ in the last
+ * bit.  Host query: reads device attributes, enqueues nothing. */
+int vla_mlp_chain_fused_supported(int64_t M, int64_t H, int64_t I, int L);
 
 /* Enqueue the chain's 2L kernels directly (no graph). */
 int vla_mlp_chain_enqueue(const uint8_t *const *wgu, const float *const *sgu,

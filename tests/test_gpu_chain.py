@@ -182,6 +182,7 @@ def check_stages(cw, x_in, st, M, tag):
 
 def test_chain_small_stagewise():
     L, M, H, I = 3, 50, 256, 512
+    assert vla.vla_mlp_chain_fused_supported(M, H, I, L)
     cw, x, xin, xout, scratch = make_chain(L, M, H, I, seed=1)
     got = eager(cw, xin, xout, scratch, M)
     staged_out, st = stage_outputs(cw, xin, M, scratch)
@@ -189,10 +190,65 @@ def test_chain_small_stagewise():
     assert check_stages(cw, x, st, M, "small") == L
 
 
+@pytest.mark.parametrize("M", [1, 10, 16, 17, 33, 50, 64])
+def test_fused_chain_rows_stagewise(M):
+    """The single-launch chain at the decoder's H = 1024, I = 4096 for every
+    row-count class (1-16 rows: one gate/up pair per workgroup; 17-32: two;
+    33-64: four; ragged last row tile), two layers, every stage on its own
+    inputs."""
+    L, H, I = 2, 1024, 4096
+    assert vla.vla_mlp_chain_fused_supported(M, H, I, L)
+    cw, x, xin, xout, scratch = make_chain(L, M, H, I, seed=10 + M)
+    got = eager(cw, xin, xout, scratch, M)
+    staged_out, st = stage_outputs(cw, xin, M, scratch)
+    assert np.array_equal(staged_out, got)
+    assert check_stages(cw, x, st, M, f"fused M={M}") == L
+    vla.vla_workspace_status(scratch)
+
+
+def test_fused_chain_barrier_wait_is_bounded():
+    """With the wait bound forced down to one poll, grid barriers give up:
+    the launch still completes, x_out reads NaN, the status query reports
+    it, and the barrier counters are cleared, so the same scratch then gives
+    the correct chain again."""
+    L, M, H, I = 3, 50, 1024, 4096
+    assert vla.vla_mlp_chain_fused_supported(M, H, I, L)
+    cw, x, xin, xout, scratch = make_chain(L, M, H, I, seed=7)
+    vla.vla_set_wait_limit(1)
+    try:
+        for _ in range(3):
+            vla.vla_mlp_chain_enqueue(cw.wgu, cw.sgu, cw.wd, cw.sd, xin, xout, scratch, scratch.numel(), L, M, H, I)
+        torch.cuda.synchronize()
+    finally:
+        vla.vla_set_wait_limit(0)
+    assert np.isnan(bf16_f64(host(xout).view(np.uint16))).any()
+    with pytest.raises(RuntimeError, match="fused chain phase barrier"):
+        vla.vla_workspace_status(scratch)
+    assert int(host(scratch[61440 + 256:61440 + 1024]).view(np.uint32).sum()) == 0
+    staged_out, st = stage_outputs(cw, xin, M, scratch)
+    assert check_stages(cw, x, st, M, "after give-up") == L
+    vla.vla_workspace_status(scratch)
+
+
+def test_chain_unaligned_scratch_takes_the_graph_path():
+    """A scratch buffer that is not 256-byte aligned runs the chain as two
+    GEMM launches per layer; every stage still matches."""
+    L, M, H, I = 2, 50, 1024, 4096
+    cw, x, xin, xout, _ = make_chain(L, M, H, I, seed=8)
+    nbytes = vla.vla_mlp_chain_scratch_bytes(M, H, I)
+    raw = torch.zeros(nbytes + 256, dtype=torch.uint8, device="cuda")
+    scratch = raw[16:16 + nbytes]
+    staged_out, st = stage_outputs(cw, xin, M, scratch)
+    assert check_stages(cw, x, st, M, "graph path") == L
+    vla.vla_workspace_status(scratch)
+
+
 @pytest.mark.parametrize("M,H,I", [(17, 96, 160), (130, 256, 512)])
 def test_chain_ragged_and_wide_stagewise(M, H, I):
-    """Ragged rows and tiles, and M > 64 (the wide kernel's fused epilogues)."""
+    """Ragged rows and tiles, and M > 64 (the wide kernel's fused epilogues):
+    shapes the single launch does not cover."""
     L = 2
+    assert not vla.vla_mlp_chain_fused_supported(M, H, I, L)
     cw, x, xin, xout, scratch = make_chain(L, M, H, I, seed=3)
     got = eager(cw, xin, xout, scratch, M)
     staged_out, st = stage_outputs(cw, xin, M, scratch)
@@ -206,6 +262,7 @@ def test_chain_config_replay_eager_purity():
     pure function of its device inputs); replay after destroy raises."""
     L, M, H, I = 18, 50, 1024, 4096
     print("chain config: building weights", flush=True)
+    assert vla.vla_mlp_chain_fused_supported(M, H, I, L)
     cw, x, xin, xout, scratch = make_chain(L, M, H, I)
     ref_eager = eager(cw, xin, xout, scratch, M)
     stream = torch.cuda.Stream()
