@@ -30,21 +30,28 @@ FNUZ = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZE=1 loads a build instrumented with AddressSanitizer and
+# UndefinedBehaviorSanitizer (the process must preload the ASan runtime).
+_SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
           "-std=c11", "-D_GNU_SOURCE", "-Wall", "-Wextra"]
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc into liboracle.so next to it."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: bool | None = None) -> str:
+    """Compile oracle.c with gcc into liboracle.so next to it (with sanitize,
+    or ORACLE_SANITIZE=1: liboracle_san.so, instrumented with ASan + UBSan)."""
+    san = _SANITIZE if sanitize is None else sanitize
+    lib = os.path.join(_HERE, "liboracle_san.so" if san else "liboracle.so")
+    if force or not os.path.exists(lib):
+        tmp = lib + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, *(SANITIZE_FLAGS if san else []), _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
