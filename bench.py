@@ -80,9 +80,28 @@ def main():
                     help="summarize a rocprofv3 kernel trace of this script (no GPU work): the dispatches "
                          "between the two marker kernels, i.e. the headline's timed replay, and exit")
     ap.add_argument("--bench-json", metavar="FILE", help="with --trace-summary: the bench's output, to compare")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="summarize rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this script (no GPU work): "
+                         "HBM bytes per dispatch of --kernel, scaled by a --calibrate-copy run of each, and exit")
+    ap.add_argument("--kernel", default="skinny_gemm_kernel", help="with --pmc-summary: kernel name filter")
+    ap.add_argument("--mfma-trace-summary", metavar="DIR",
+                    help="summarize a rocprofv3 kernel trace of --mfma-only (no GPU work) and exit")
+    ap.add_argument("--algorithmic-bytes", type=int, help="with --pmc-summary: algorithmic bytes per launch")
+    ap.add_argument("--mfma-only", action="store_true",
+                    help="only run the matrix-core rate probe (zero and GEMM-like operands, four forms), print its "
+                         "JSON and exit")
+    ap.add_argument("--wide-shape", choices=["up", "down", "both"], default="both",
+                    help="with --wide-only: the 2048 -> 16384 up-projection, the 16384 -> 2048 down-projection, "
+                         "or both")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(args.trace_summary, args.bench_json)
+        return
+    if args.mfma_trace_summary:
+        mfma_trace_summary(args.mfma_trace_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.kernel, args.algorithmic_bytes)
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -120,9 +139,14 @@ def main():
         vla.vla_quantize_pack(up_bits(W), q, s, N, K, wfmt, vla.VLA_LAYOUT_MFMA)
         return q, s
 
+    if args.mfma_only:
+        print(json.dumps({"mfma_rate_TFLOPs": mfma_rates(vla, torch, dev)}))
+        return
+
     if args.wide_only:
         Mw = 768
-        for n, k in ((16384, 2048), (2048, 16384)):
+        shapes = {"up": [(16384, 2048)], "down": [(2048, 16384)], "both": [(16384, 2048), (2048, 16384)]}
+        for n, k in shapes[args.wide_shape]:
             A = up_bits(synthetic.activations(Mw, k, 910 + n))
             q, s = quantize(synthetic.weights(n, k, 911 + n))
             qa = torch.empty(Mw * k, dtype=torch.uint8, device=dev)
@@ -394,6 +418,9 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
         out[f"{name}_GBps"] = round(alg_bytes_bf16w(m, n, k) / (us * 1e-6) / 1e9, 1)
         del qs
 
+    log("secondary: matrix-instruction rates")
+    out["mfma_rate_TFLOPs"] = mfma_rates(vla, torch, dev)
+
     log("secondary: wide GEMMs")
     for Mw, prefix in ((768, "wide"), (571, "wide_m571")):
         for name, (n, k) in ((prefix + "_up", (16384, 2048)), (prefix + "_down", (2048, 16384))):
@@ -427,6 +454,8 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
                 out[f"{name}_{tag}_us"] = round(us, 2)
                 out[f"{name}_{tag}_TFLOPs"] = round(tf, 1)
                 out[f"{name}_{tag}_frac"] = round(tf / peak, 4)
+                rate = out["mfma_rate_TFLOPs"]["bf16_32x32x16" if tag == "w8a16" else "fp8_32x32x64"]["normal"]
+                out[f"{name}_{tag}_frac_of_mfma_rate"] = round(tf / rate, 4)
             ms = time_graph(actq, 20)
             out[f"{name}_act_quant_us"] = round(ms * 1000.0 / 20, 2)
 
@@ -475,32 +504,36 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
     xin = up_bits(synthetic.activations(M, H, synthetic.IDS["chain.x"]))
     xout = torch.empty(M * H, dtype=torch.int16, device=dev)
     sb = vla.vla_mlp_chain_scratch_bytes(M, H, I)
-    scratch = torch.zeros(sb, dtype=torch.uint8, device=dev)
+    scratch = torch.zeros(sb + 256, dtype=torch.uint8, device=dev)
     cs = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    h = vla.vla_mlp_chain_create(wgu, sgu, wd, sd, xin, xout, scratch, sb, L, M, H, I, cs)
-    try:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        for _ in range(5):
-            vla.vla_mlp_chain_replay(h, cs)
-        cs.synchronize()
-        warm, cold = [], []
-        for i in range(40):
-            if i % 2 == 1:
-                flush.fill_(i & 0xFF)            # evict the 216 MiB of weights from cache
-                torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(cs)
-            vla.vla_mlp_chain_replay(h, cs)
-            e1.record(cs)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    chain_bytes = L * (2 * I * H + 8 * I + H * I + 4 * H) + 2 * 2 * M * H
+    # the fused single launch (256-byte aligned scratch), then the graph of
+    # 2L GEMM launches that a scratch without that alignment falls back to
+    for prefix, sc in (("chain", scratch[:sb]), ("chain_graph_path", scratch[16:16 + sb])):
+        torch.cuda.synchronize()
+        h = vla.vla_mlp_chain_create(wgu, sgu, wd, sd, xin, xout, sc, sb, L, M, H, I, cs)
+        try:
+            for _ in range(5):
+                vla.vla_mlp_chain_replay(h, cs)
             cs.synchronize()
-            (cold if i % 2 == 1 else warm).append(e0.elapsed_time(e1) * 1000.0)
-        out["chain_us_per_replay_warm"] = round(float(np.median(warm)), 2)
-        out["chain_us_per_replay_cold"] = round(float(np.median(cold)), 2)
-        chain_bytes = L * (2 * I * H + 8 * I + H * I + 4 * H) + 2 * 2 * M * H
-        out["chain_cold_GBps"] = round(chain_bytes / (np.median(cold) * 1e-6) / 1e9, 1)
-    finally:
-        vla.vla_mlp_chain_destroy(h)
+            warm, cold = [], []
+            for i in range(40):
+                if i % 2 == 1:
+                    flush.fill_(i & 0xFF)            # evict the 216 MiB of weights from cache
+                    torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(cs)
+                vla.vla_mlp_chain_replay(h, cs)
+                e1.record(cs)
+                cs.synchronize()
+                (cold if i % 2 == 1 else warm).append(e0.elapsed_time(e1) * 1000.0)
+            out[f"{prefix}_us_per_replay_warm"] = round(float(np.median(warm)), 2)
+            out[f"{prefix}_us_per_replay_cold"] = round(float(np.median(cold)), 2)
+            out[f"{prefix}_cold_GBps"] = round(chain_bytes / (np.median(cold) * 1e-6) / 1e9, 1)
+        finally:
+            vla.vla_mlp_chain_destroy(h)
+    out["chain_fused_launch"] = bool(vla.vla_mlp_chain_fused_supported(M, H, I, L))
 
     log("secondary: 18-layer decoder-block chain (MLP + fused boundary per layer)")
     dx, dh, dg, dstyle = synthetic.decoder_chain_inputs(L, M, H, M)
@@ -554,20 +587,116 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "skinny_fp8_m50_pmc_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "bf16_gemm_vla_amd", "csrc", "gemm.hip")
+# every source the skinny kernel is compiled from: a change to any of them
+# invalidates the committed counter figures
+KERNEL_SOURCES = [os.path.join(ROOT, "bf16_gemm_vla_amd", "csrc", f)
+                  for f in ("gemm.hip", "gemm_common.h", "vla_device.h")]
+
+
+def kernel_sources_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+MFMA_FORMS = (   # name, VLA_MFMA_* value, m*n*k, operand type, published dense peak (TFLOP/s)
+    ("bf16_32x32x16", 0, 32 * 32 * 16, "bf16", BF16_PEAK_TFLOPS),
+    ("bf16_16x16x32", 1, 16 * 16 * 32, "bf16", BF16_PEAK_TFLOPS),
+    ("fp8_32x32x64", 2, 32 * 32 * 64, "fp8", FP8_PEAK_TFLOPS),
+    ("fp8_16x16x128", 3, 16 * 16 * 128, "fp8", FP8_PEAK_TFLOPS),
+)
+
+
+def mfma_operands(torch, dev, kind, dtype, seed=1234):
+    """The rate probe's 64 KiB operand buffer: zeros, or values distributed like
+    the wide GEMMs' operands (bf16: N(0, 1) activations; FP8: E4M3 codes of
+    absmax-scaled N(0, 1) data, i.e. N(0, ~100) clamped to the E4M3 range)."""
+    if kind == "zero":
+        return torch.zeros(256 * 64, dtype=torch.int32, device=dev)
+    g = torch.Generator().manual_seed(seed)
+    if dtype == "bf16":
+        v = torch.randn(256 * 128, generator=g).to(torch.bfloat16).view(torch.int16)
+    else:
+        v = (torch.randn(256 * 256, generator=g) * 100.0).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return v.view(torch.int32).to(dev)
+
+
+def mfma_iters(mnk, blocks=512):
+    return max(1, int(2e12 / (blocks * 4 * 4 * 2.0 * mnk)))   # ~2 TFLOP per launch
+
+
+def mfma_trace_summary(trace_dir, blocks=512, reps=5):
+    """Matrix-core rates from a rocprofv3 kernel trace of --mfma-only: the
+    probe's dispatches in launch order, one untimed and `reps` timed per
+    (form, operands), in the order mfma_rates issues them."""
+    import csv
+    import glob
+    import statistics
+
+    files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        sys.exit(f"no *kernel_trace.csv under {trace_dir}")
+    rows = [r for r in csv.DictReader(open(files[0])) if "mfma_rate_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = reps + 1
+    if len(rows) != per * 2 * len(MFMA_FORMS):
+        sys.exit(f"expected {per * 2 * len(MFMA_FORMS)} probe dispatches, found {len(rows)}")
+    print(f"# rocprofv3 kernel trace: {os.path.relpath(files[0], trace_dir)}; {blocks} workgroups x 256 threads")
+    i = 0
+    for name, form, mnk, dt, peak in MFMA_FORMS:
+        iters = mfma_iters(mnk, blocks)
+        flops = blocks * 4 * 4 * 2.0 * mnk * iters
+        for kind in ("zero", "normal"):
+            d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[i + 1:i + per]]
+            i += per
+            med = statistics.median(d)
+            tf = flops / (med * 1e-9) / 1e12
+            print(f"{name} {kind:6s}: iters {iters}, median kernel {med / 1e3:.1f} us over {len(d)} launches "
+                  f"-> {tf:.1f} TFLOP/s = {tf / peak:.4f} of the published {peak:.0f}")
+
+
+def mfma_rates(vla, torch, dev, blocks=512, reps=5):
+    """Issue rate of each matrix instruction the GEMMs use, on zero operands
+    and on operands like the GEMMs' own (vla_probe_mfma_rate; two workgroups of
+    four waves per CU, two waves per SIMD as in the wide kernel).  The rate
+    depends on the data, so the wide GEMMs' fractions are read against the
+    'normal' figures as well as against the published peaks."""
+    res = {}
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    for name, form, mnk, dt, peak in MFMA_FORMS:
+        per_iter = blocks * 4 * 4 * 2.0 * mnk           # workgroups x waves x chains x flops
+        iters = mfma_iters(mnk, blocks)
+        r = {"iters": iters, "blocks": blocks}
+        for kind in ("zero", "normal"):
+            ops = mfma_operands(torch, dev, kind, dt)
+            vla.vla_probe_mfma_rate(form, ops, iters, out, blocks)
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                vla.vla_probe_mfma_rate(form, ops, iters, out, blocks)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = sorted(ts)[len(ts) // 2]
+            tf = per_iter * iters / (ms * 1e-3) / 1e12
+            r[kind] = round(tf, 1)
+            r[kind + "_frac_of_peak"] = round(tf / peak, 4)
+        res[name] = r
+    return res
 
 
 def measured_traffic():
     """HBM bytes per launch of the skinny kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE runs, scaled by a plain copy's counters; None if
     the summary is missing or the kernel source changed since it was taken."""
-    import hashlib
-
     try:
         kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line and not line.startswith("#"))
         kv = {k.strip(): v.strip() for k, v in kv.items()}
-        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-        if kv.get("kernel_source_sha256") != sha:
+        if kv.get("kernel_source_sha256") != kernel_sources_sha256():
             return None
         return int(float(kv["hbm_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
@@ -705,7 +834,7 @@ def trace_summary(trace_dir, bench_json=None):
     print(f"dispatches in the timed replay: {len(timed)}")
     total = 0.0
     for (name, groups, wg), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        short = name.split("(")[0][:160]
+        short = short_kernel_name(name)
         total += sum(d)
         print(f"kernel: {short}")
         print(f"  workgroups {groups} x {wg} threads; dispatches {len(d)}; mean {statistics.mean(d) / 1e3:.3f} us; "
@@ -727,6 +856,93 @@ def trace_summary(trace_dir, bench_json=None):
               f"{nbytes / (total / len(timed)):.1f} GB/s ({nbytes / (total / len(timed)) / HBM_PEAK_GBS:.4f} of "
               f"8 TB/s); over the event time per call {nbytes / (ev_us * 1e3):.1f} GB/s "
               f"({nbytes / (ev_us * 1e3) / HBM_PEAK_GBS:.4f}, the bench's roofline.frac {b['roofline']['frac']})")
+
+
+def short_kernel_name(name):
+    """A kernel name without its trailing parameter list (names may contain
+    parentheses of their own, as in '(anonymous namespace)')."""
+    name = name.strip()
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                name = name[:i]
+                break
+    return name[:160]
+
+
+def pmc_summary(dirs, kernel, algorithmic=None):
+    """Summarize rocprofv3 --pmc runs of FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch): dirs = [fetch, write, copy fetch, copy write]; the last two are
+    runs of --calibrate-copy, whose 256 MiB copy scales each counter to bytes.
+    Dispatches whose kernel name contains `kernel` are averaged per (name,
+    launch shape) and over all of them."""
+    import csv
+    import glob
+    import statistics
+
+    def load_runs(d, counter):
+        files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+        if not files:
+            sys.exit(f"no *counter_collection.csv under {d}")
+        out = []
+        for r in csv.DictReader(open(files[0])):
+            if r.get("Counter_Name", "").strip() != counter:
+                continue
+            grid = int(float(r.get("Grid_Size", 0) or 0))
+            wg = int(float(r.get("Workgroup_Size", 1) or 1))
+            out.append((int(r.get("Dispatch_Id", len(out))), r["Kernel_Name"], grid, wg, float(r["Counter_Value"])))
+        return out
+
+    fetch, write, cfetch, cwrite = (load_runs(d, c) for d, c in zip(
+        dirs, ("FETCH_SIZE", "WRITE_SIZE", "FETCH_SIZE", "WRITE_SIZE")))
+    copy_kib = (256 << 20) / 1024.0
+
+    def copy_scale(rows):
+        v = [x[4] for x in rows if "copy" in x[1].lower()]
+        if not v:
+            sys.exit("no copy dispatches in the calibration run")
+        return copy_kib / statistics.mean(v), statistics.mean(v)
+
+    fs, fraw = copy_scale(cfetch)
+    ws, wraw = copy_scale(cwrite)
+    print(f"# calibration: a plain 256 MiB device copy reads FETCH_SIZE {fraw:.1f} KiB and WRITE_SIZE "
+          f"{wraw:.1f} KiB per dispatch against {copy_kib:.0f} KiB moved each way: fetch scale {fs:.4f}, "
+          f"write scale {ws:.4f}")
+
+    def group(rows):
+        g = {}
+        for _, name, grid, wg, v in rows:
+            if kernel in name:
+                groups = grid // wg if grid >= wg and wg > 0 else grid
+                g.setdefault((short_kernel_name(name), groups, wg), []).append(v)
+        return g
+    gf, gw = group(fetch), group(write)
+    allf = [v for vs in gf.values() for v in vs]
+    allw = [v for vs in gw.values() for v in vs]
+    if not allf or not allw:
+        sys.exit(f"no dispatches of {kernel}")
+    for key in sorted(gf):
+        f, w = statistics.mean(gf[key]), statistics.mean(gw.get(key, [float("nan")]))
+        print(f"kernel: {key[0]}")
+        print(f"  workgroups {key[1]} x {key[2]} threads; dispatches {len(gf[key])} / {len(gw.get(key, []))}; "
+              f"FETCH_SIZE {f:.1f} KiB, WRITE_SIZE {w:.1f} KiB per dispatch; HBM bytes per launch "
+              f"{f * 1024 * fs + w * 1024 * ws:.0f} (read {f * 1024 * fs:.0f}, write {w * 1024 * ws:.0f})")
+    f, w = statistics.mean(allf), statistics.mean(allw)
+    hbm = f * 1024 * fs + w * 1024 * ws
+    print(f"{kernel}_dispatches_fetch: {len(allf)}")
+    print(f"{kernel}_dispatches_write: {len(allw)}")
+    print(f"fetch_kib_per_launch_raw: {f:.1f}")
+    print(f"write_kib_per_launch_raw: {w:.1f}")
+    print(f"fetch_scale: {fs:.4f}")
+    print(f"write_scale: {ws:.4f}")
+    print(f"hbm_bytes_per_launch: {hbm:.0f}")
+    if algorithmic:
+        print(f"algorithmic_bytes_per_launch: {algorithmic}")
+        print(f"traffic_over_algorithmic: {hbm / algorithmic:.3f}")
+    if kernel == "skinny_gemm_kernel":
+        print(f"kernel_source_sha256: {kernel_sources_sha256()}")
 
 
 if __name__ == "__main__":

@@ -7,6 +7,7 @@
 
 #include <cstdint>
 
+#include "vla_device.h"
 #include "vla_internal.h"
 
 namespace vla {
@@ -39,6 +40,128 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4*
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s) {
     stream_read_kernel<<<blocks, kProbeThreads, 0, s>>>(static_cast<const uint4*>(src),
                                                         static_cast<int64_t>(bytes / 16), sink);
+    return hipGetLastError();
+}
+
+}  // namespace vla
+
+// ------------------------------------------------------------------------
+// Matrix-core rate probe: every wave runs `iters` rounds of four independent
+// MFMA chains on operands held in registers, so nothing but the matrix pipe
+// limits it.  The operands come from a caller buffer (zeros, ones, random
+// codes): the issue rate of these instructions depends on the data, and the
+// ceiling a GEMM of these shapes can reach is the rate on operands like its
+// own, not the published peak.  The four chains use four different operand
+// sets, so the inputs change from one instruction to the next as they do in
+// a GEMM.  Each lane writes the sum of its accumulators, which lets a test
+// check that the launch did exactly the multiply-adds it is credited with.
+
+namespace vla {
+namespace {
+
+constexpr int kRateChains = 4;
+constexpr int kRateThreads = 256;
+constexpr int kRateWordsPerLane = 64;   // four operand sets of A and B, 8 dwords each
+
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+template <int FORM>
+struct RateForm;
+template <>
+struct RateForm<VLA_MFMA_BF16_32X32X16> {
+    typedef f32x16_t Acc;
+    static __device__ __forceinline__ Acc step(const uint32_t* a, const uint32_t* b, Acc c) {
+        const u32x4_t av = {a[0], a[1], a[2], a[3]}, bv = {b[0], b[1], b[2], b[3]};
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), c, 0, 0, 0);
+    }
+};
+template <>
+struct RateForm<VLA_MFMA_BF16_16X16X32> {
+    typedef f32x4_t Acc;
+    static __device__ __forceinline__ Acc step(const uint32_t* a, const uint32_t* b, Acc c) {
+        const u32x4_t av = {a[0], a[1], a[2], a[3]}, bv = {b[0], b[1], b[2], b[3]};
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), c, 0, 0, 0);
+    }
+};
+template <>
+struct RateForm<VLA_MFMA_FP8_32X32X64> {
+    typedef f32x16_t Acc;
+    static __device__ __forceinline__ Acc step(const uint32_t* a, const uint32_t* b, Acc c) {
+        i32x8_t av, bv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            av[i] = static_cast<int>(a[i]);
+            bv[i] = static_cast<int>(b[i]);
+        }
+        // E4M3 x E4M3 (format 0 for both), unit E8M0 scales (127)
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+    }
+};
+template <>
+struct RateForm<VLA_MFMA_FP8_16X16X128> {
+    typedef f32x4_t Acc;
+    static __device__ __forceinline__ Acc step(const uint32_t* a, const uint32_t* b, Acc c) {
+        i32x8_t av, bv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            av[i] = static_cast<int>(a[i]);
+            bv[i] = static_cast<int>(b[i]);
+        }
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+    }
+};
+
+template <int FORM>
+__global__ __launch_bounds__(kRateThreads) void mfma_rate_kernel(const uint32_t* __restrict__ src, int iters,
+                                                                 float* __restrict__ out) {
+    typedef typename RateForm<FORM>::Acc Acc;
+    uint32_t ops[kRateWordsPerLane];
+    const uint32_t* p = src + threadIdx.x * kRateWordsPerLane;
+#pragma unroll
+    for (int i = 0; i < kRateWordsPerLane; ++i) ops[i] = p[i];
+    // four named chains: with an array of vector accumulators the register
+    // allocator rotates them through copies inside the loop
+    Acc c0{}, c1{}, c2{}, c3{};
+    static_assert(kRateChains == 4, "four chains");
+    asm volatile("" : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3));
+    for (int it = 0; it < iters; ++it) {
+        c0 = RateForm<FORM>::step(ops + 0, ops + 8, c0);
+        c1 = RateForm<FORM>::step(ops + 16, ops + 24, c1);
+        c2 = RateForm<FORM>::step(ops + 32, ops + 40, c2);
+        c3 = RateForm<FORM>::step(ops + 48, ops + 56, c3);
+        // pins each chain to its own registers across iterations (no code)
+        asm volatile("" : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3));
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < static_cast<int>(sizeof(Acc) / sizeof(float)); ++e) s += c0[e];
+#pragma unroll
+    for (int e = 0; e < static_cast<int>(sizeof(Acc) / sizeof(float)); ++e) s += c1[e];
+#pragma unroll
+    for (int e = 0; e < static_cast<int>(sizeof(Acc) / sizeof(float)); ++e) s += c2[e];
+#pragma unroll
+    for (int e = 0; e < static_cast<int>(sizeof(Acc) / sizeof(float)); ++e) s += c3[e];
+    out[static_cast<int64_t>(blockIdx.x) * kRateThreads + threadIdx.x] = s;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_rate(int form, const uint32_t* src, int iters, float* out, int blocks, hipStream_t s) {
+    switch (form) {
+        case VLA_MFMA_BF16_32X32X16:
+            mfma_rate_kernel<VLA_MFMA_BF16_32X32X16><<<blocks, kRateThreads, 0, s>>>(src, iters, out);
+            break;
+        case VLA_MFMA_BF16_16X16X32:
+            mfma_rate_kernel<VLA_MFMA_BF16_16X16X32><<<blocks, kRateThreads, 0, s>>>(src, iters, out);
+            break;
+        case VLA_MFMA_FP8_32X32X64:
+            mfma_rate_kernel<VLA_MFMA_FP8_32X32X64><<<blocks, kRateThreads, 0, s>>>(src, iters, out);
+            break;
+        default:
+            mfma_rate_kernel<VLA_MFMA_FP8_16X16X128><<<blocks, kRateThreads, 0, s>>>(src, iters, out);
+            break;
+    }
     return hipGetLastError();
 }
 

@@ -201,6 +201,34 @@ int vla_gate_residual_ada_norm(const uint16_t *residual, const uint16_t *out, co
  *   blocks 1..65536, else VLA_EINVAL. */
 int vla_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blocks, void *stream);
 
+/* Matrix-core rate probe: one launch of `blocks` workgroups of 256 threads;
+ * every wave runs `iters` rounds of four independent MFMA chains of the
+ * given form on operands it holds in registers, so the launch measures the
+ * issue rate of that instruction on that data.  The skinny and wide GEMMs
+ * are built on these instructions ("Real-time VLA inference on AMD
+ * hardware", section "How FlashRT works": the GEMMs are shaped around the
+ * matrix instruction), and the rate they can reach depends on the operand
+ * values, so a GEMM's roofline fraction is read against this rate on
+ * operands like its own as well as against the published peak.
+ *   form      VLA_MFMA_* below, else VLA_EINVAL;
+ *   operands  device uint32[256 * 64], 16-byte aligned: lane t of every
+ *             workgroup takes words 64t .. 64t+63 as four operand sets
+ *             (A in words 16j .. 16j+7, B in 16j+8 .. 16j+15 of set j; the
+ *             bf16 forms use the first four words of each: 8 bf16 values;
+ *             the FP8 forms all eight: 32 OCP E4M3 codes);
+ *   iters     1 .. 2^24 (VLA_EINVAL otherwise);
+ *   out       device float[blocks * 256], 16-byte aligned: lane t of
+ *             workgroup b writes the sum of its four accumulators at
+ *             b*256 + t (accumulators start at zero);
+ *   blocks    1 .. 65536, else VLA_EINVAL.
+ * One launch does blocks * 4 * iters * 4 instructions, each of
+ * 2*m*n*k floating-point operations for its m x n x k form. */
+#define VLA_MFMA_BF16_32X32X16 0  /* v_mfma_f32_32x32x16_bf16 (wide GEMM, bf16 activations) */
+#define VLA_MFMA_BF16_16X16X32 1  /* v_mfma_f32_16x16x32_bf16 (skinny GEMM, gated-MLP chain) */
+#define VLA_MFMA_FP8_32X32X64 2   /* v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3 (wide GEMM, FP8 x FP8) */
+#define VLA_MFMA_FP8_16X16X128 3  /* v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x E4M3 */
+int vla_probe_mfma_rate(int form, const uint32_t *operands, int iters, float *out, int blocks, void *stream);
+
 /* ------------------------------------------------------------------ GEMM */
 
 /* Workspace for vla_gemm_fp8w / vla_gemm_bf16 / vla_gemm_fp8w_gelu_mul at
