@@ -157,25 +157,35 @@ def test_reencode_dialect_workload_values():
 
 # ------------------------------------------------------------------ packer
 
-def _page_cdna3_layout(W_kn: np.ndarray) -> np.ndarray:
-    """Packed order described on the page for CDNA3's 16x16x16 MFMA.
+def _cdna3_operand_layout(W_kn: np.ndarray) -> np.ndarray:
+    """Packed order for CDNA3's 16x16x16 MFMA, built element by element from
+    the instruction's operand lane map ("Real-time VLA inference on AMD
+    hardware", section "Packing around the instruction": weights are stored
+    in the order the instruction's lanes consume them).
 
-    W is K x N (the page multiplies A x W).  K splits into (MFMA K step,
-    group of 4 lanes, 4 contiguous values) and N into (output tile, 16
-    lanes); the packed axes are [output tile][K step][lane group][lane in
-    tile][4 values].
+    W is K x N (the page multiplies A x W).  In one 16x16x16 step, lane l
+    supplies output column l % 16 and the four consecutive K values
+    4 * (l // 16) .. +3 of that step; steps run over K within an output tile
+    of 16 columns, tiles over N.  Element (k, n) therefore lands at
+    ((tile * steps_per_tile + step) * 64 + lane) * 4 + (k % 4).
     """
     K, N = W_kn.shape
-    t = W_kn.reshape(K // 16, 4, 4, N // 16, 16)          # [kstep, kgroup, kval, ntile, nlane]
-    return np.ascontiguousarray(t.transpose(3, 0, 1, 4, 2)).reshape(-1)
+    out = np.empty(K * N, dtype=W_kn.dtype)
+    steps = K // 16
+    for k in range(K):
+        for n in range(N):
+            tile, step = n // 16, k // 16
+            lane = 16 * ((k % 16) // 4) + n % 16
+            out[((tile * steps + step) * 64 + lane) * 4 + k % 4] = W_kn[k, n]
+    return out
 
 
-def test_pack_kl4_matches_page_cdna3_expression():
+def test_pack_kl4_matches_cdna3_operand_layout():
     g = rng(700)
     K, N = 64, 48
     W_kn = g.integers(0, 65535, (K, N)).astype(np.uint16)
     ours = oracle.pack(np.ascontiguousarray(W_kn.T), KL=4)
-    assert np.array_equal(ours, _page_cdna3_layout(W_kn))
+    assert np.array_equal(ours, _cdna3_operand_layout(W_kn))
 
 
 def test_pack_kl8_lane_slices():
