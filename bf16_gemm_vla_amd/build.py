@@ -30,10 +30,22 @@ HIPFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *HIPFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the checking
+# build (libvla_san.so): only the host pass is instrumented; the library is
+# linked without a sanitizer runtime, which the process preloads.
+SAN_OBJDIR = os.path.join(ROOT, "_build_san")
+SAN_LIB = os.path.join(PKG, "libvla_san.so")
+HOST_SANITIZE = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    objdir = SAN_OBJDIR if sanitize else OBJDIR
+    os.makedirs(objdir, exist_ok=True)
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *HIPFLAGS, *(HOST_SANITIZE if sanitize else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
@@ -44,10 +56,13 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
+def build(sanitize: bool = False) -> str:
+    """Compile and link libvla.so; with sanitize, the host-instrumented
+    checking build libvla_san.so instead (the product never loads it)."""
+    lib = SAN_LIB if sanitize else LIB
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -59,9 +74,9 @@ def build() -> str:
     own = [l.split()[-1] for l in nm.stdout.splitlines() if "_ZN3vla" in l]
     if nm.returncode != 0 or own:
         os.remove(tmp)
-        raise RuntimeError("libvla.so has undefined symbols of its own: " + ", ".join(own[:8]))
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(os.path.basename(lib) + " has undefined symbols of its own: " + ", ".join(own[:8]))
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
