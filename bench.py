@@ -84,6 +84,12 @@ def main():
                     help="summarize rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this script (no GPU work): "
                          "HBM bytes per dispatch of --kernel, scaled by a --calibrate-copy run of each, and exit")
     ap.add_argument("--kernel", default="skinny_gemm_kernel", help="with --pmc-summary: kernel name filter")
+    ap.add_argument("--all-kernels-summary", metavar="DIR",
+                    help="tabulate every launch configuration of a rocprofv3 kernel trace of this script (no GPU "
+                         "work) and exit")
+    ap.add_argument("--pmc-table", nargs="+", metavar="DIR",
+                    help="mean per dispatch of every counter in rocprofv3 --pmc runs of this script, per launch "
+                         "shape of --kernel (no GPU work), and exit")
     ap.add_argument("--mfma-trace-summary", metavar="DIR",
                     help="summarize a rocprofv3 kernel trace of --mfma-only (no GPU work) and exit")
     ap.add_argument("--algorithmic-bytes", type=int, help="with --pmc-summary: algorithmic bytes per launch")
@@ -96,6 +102,12 @@ def main():
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(args.trace_summary, args.bench_json)
+        return
+    if args.all_kernels_summary:
+        all_kernels_summary(args.all_kernels_summary)
+        return
+    if args.pmc_table:
+        pmc_table(args.pmc_table, args.kernel)
         return
     if args.mfma_trace_summary:
         mfma_trace_summary(args.mfma_trace_summary)
@@ -870,6 +882,67 @@ def short_kernel_name(name):
                 name = name[:i]
                 break
     return name[:160]
+
+
+def all_kernels_summary(trace_dir):
+    """One row per launch configuration of a rocprofv3 kernel trace (kernel,
+    workgroup size, grid in workgroups, LDS bytes, VGPR+AGPR, scratch bytes):
+    launches and their mean / median / min duration, by total time."""
+    import csv
+    import glob
+    import statistics
+
+    files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        sys.exit(f"no *kernel_trace.csv under {trace_dir}")
+    by = {}
+    for r in csv.DictReader(open(files[0])):
+        wg = [int(r.get(f"Workgroup_Size_{a}", 1) or 1) for a in "XYZ"]
+        grid = tuple(int(r.get(f"Grid_Size_{a}", 1) or 1) // max(1, w) for a, w in zip("XYZ", wg))
+        key = (short_kernel_name(r["Kernel_Name"]), wg[0] * wg[1] * wg[2], grid, int(r.get("LDS_Block_Size", 0) or 0),
+               int(r.get("VGPR_Count", 0) or 0), int(r.get("Accum_VGPR_Count", 0) or 0),
+               int(r.get("Scratch_Size", 0) or 0))
+        by.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"# rocprofv3 kernel trace: {os.path.relpath(files[0], trace_dir)}")
+    print(f"  {'kernel':34s} | {'wg':>5s} | {'grid':15s} | {'lds':>6s} | {'vgpr':7s} | {'scr':>3s} | {'calls':>5s} | "
+          f"{'mean us':>9s} | {'median us':>9s} | {'min us':>8s}")
+    for key, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        name, wg, grid, lds, vg, ag, scr = key
+        print(f"  {name[:34]:34s} | {wg:5d} | {str(grid):15s} | {lds:6d} | {f'{vg}+{ag}':7s} | {scr:3d} | {len(d):5d} | "
+              f"{statistics.mean(d):9.2f} | {statistics.median(d):9.2f} | {min(d):8.2f}")
+
+
+def pmc_table(dirs, kernel):
+    """Mean value per dispatch of every counter in rocprofv3 --pmc runs (one
+    directory per run), per launch shape of the kernels whose name contains
+    `kernel`; _sum counters also per compute unit (256)."""
+    import csv
+    import glob
+    import statistics
+
+    vals = {}
+    for d in dirs:
+        files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+        if not files:
+            sys.exit(f"no *counter_collection.csv under {d}")
+        for r in csv.DictReader(open(files[0])):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            grid = int(float(r.get("Grid_Size", 0) or 0))
+            wg = int(float(r.get("Workgroup_Size", 1) or 1))
+            key = (short_kernel_name(r["Kernel_Name"]), grid // wg if grid >= wg > 0 else grid, wg)
+            vals.setdefault(key, {}).setdefault(r["Counter_Name"].strip(), []).append(float(r["Counter_Value"]))
+    for (name, groups, wg), cs in sorted(vals.items()):
+        print(f"{name}: {groups} workgroups x {wg} threads")
+        for c in sorted(cs):
+            v = statistics.mean(cs[c])
+            per_cu = f"  ({v / 256:.1f} per CU)" if c.endswith("_sum") else ""
+            print(f"  {c:34s} {v:14.1f}{per_cu}   [{len(cs[c])} dispatches]")
+        if "TCP_TCC_READ_REQ_sum" in cs:
+            req = statistics.mean(cs["TCP_TCC_READ_REQ_sum"])
+            print(f"  L1 -> L2 read requests x 128 B: {req * 128 / 2**20:.1f} MiB per dispatch")
+            if "TCP_TCC_READ_REQ_LATENCY_sum" in cs and req > 0:
+                print(f"  mean L1 -> L2 read latency: {statistics.mean(cs['TCP_TCC_READ_REQ_LATENCY_sum']) / req:.0f} cycles")
 
 
 def pmc_summary(dirs, kernel, algorithmic=None):
