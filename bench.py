@@ -208,16 +208,24 @@ def main():
             flush_val[0] = (flush_val[0] + 1) & 0xFF
             flush_buf.fill_(flush_val[0])
 
+    def read_flush():
+        """Read the same 1 GiB instead: evicts the caches and leaves no dirty
+        lines to be written back during the timed replay (reported beside
+        the protocol's write flush, never as the headline)."""
+        if flush_buf is not None:
+            vla.vla_probe_stream_read(flush_buf, flush_buf.numel(), marker_sink[32:], 2048)
+
     def marker():
         # one workgroup of the streaming-read probe over 16 bytes: the only
         # one-workgroup dispatch this script makes, so a kernel trace can
         # find the timed replay between two of them
         vla.vla_probe_stream_read(marker_sink, 16, marker_sink[16:], 1)
 
-    def time_graph_all(fn, n, reps=1, cold=None, mark=False):
+    def time_graph_all(fn, n, reps=1, cold=None, mark=False, flusher=None):
         """Record fn(0..n-1) into one graph, replay once untimed, then `reps`
         times, each after the cache flush (cold regime) and between HIP
         events; returns the ms of each timed replay."""
+        flusher = flusher or flush
         cold = (args.cache == "cold") if cold is None else cold
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -231,7 +239,7 @@ def main():
         out = []
         for r in range(reps):
             if cold:
-                flush()
+                flusher()
             if mark and r == 0:
                 marker()
             torch.cuda.synchronize()
@@ -267,6 +275,7 @@ def main():
     reps = time_graph_all(step, args.steps, reps=7, mark=True)
     ms_graph = reps[0]                  # the headline: exactly K steps, one replay
     us_reps = np.array(reps) * 1000.0 / (2 * args.steps)
+    us_read_flush = np.array(time_graph_all(step, args.steps, reps=5, flusher=read_flush)) * 1000.0 / (2 * args.steps)
     ms_eager = time_eager(step, args.steps)
     us_call = ms_graph * 1000.0 / (2 * args.steps)
     bytes_step = alg_bytes_fp8w(*UP) + alg_bytes_fp8w(*DOWN)
@@ -285,6 +294,7 @@ def main():
     best_blocks = min(read_us, key=read_us.get)
     extra = {
         "us_per_call_p10_p50_p90": [round(float(np.percentile(us_reps, q)), 3) for q in (10, 50, 90)],
+        "us_per_call_after_read_flush_p50": round(float(np.median(us_read_flush)), 3),
         "timed_replays_for_spread": len(reps),
         "us_per_call_eager": round(ms_eager * 1000.0 / (2 * args.steps), 3),
         "graph_launch_floor_us": round(floor_us, 3),
@@ -519,6 +529,7 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
     scratch = torch.zeros(sb + 256, dtype=torch.uint8, device=dev)
     cs = torch.cuda.Stream()
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    rf_sink = torch.zeros(64, dtype=torch.int32, device=dev)
     chain_bytes = L * (2 * I * H + 8 * I + H * I + 4 * H) + 2 * 2 * M * H
     # the fused single launch (256-byte aligned scratch), then the graph of
     # 2L GEMM launches that a scratch without that alignment falls back to
@@ -529,19 +540,23 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
             for _ in range(5):
                 vla.vla_mlp_chain_replay(h, cs)
             cs.synchronize()
-            warm, cold = [], []
-            for i in range(40):
-                if i % 2 == 1:
+            warm, cold, rcold = [], [], []
+            for i in range(60):
+                if i % 3 == 1:
                     flush.fill_(i & 0xFF)            # evict the 216 MiB of weights from cache
                     torch.cuda.synchronize()
+                elif i % 3 == 2:                     # the same, reading: no dirty lines left behind
+                    vla.vla_probe_stream_read(flush, flush.numel(), rf_sink, 2048, cs)
+                    cs.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(cs)
                 vla.vla_mlp_chain_replay(h, cs)
                 e1.record(cs)
                 cs.synchronize()
-                (cold if i % 2 == 1 else warm).append(e0.elapsed_time(e1) * 1000.0)
+                (warm, cold, rcold)[i % 3].append(e0.elapsed_time(e1) * 1000.0)
             out[f"{prefix}_us_per_replay_warm"] = round(float(np.median(warm)), 2)
             out[f"{prefix}_us_per_replay_cold"] = round(float(np.median(cold)), 2)
+            out[f"{prefix}_us_per_replay_after_read_flush"] = round(float(np.median(rcold)), 2)
             out[f"{prefix}_cold_GBps"] = round(chain_bytes / (np.median(cold) * 1e-6) / 1e9, 1)
         finally:
             vla.vla_mlp_chain_destroy(h)
@@ -914,8 +929,10 @@ def all_kernels_summary(trace_dir):
 
 def pmc_table(dirs, kernel):
     """Mean value per dispatch of every counter in rocprofv3 --pmc runs (one
-    directory per run), per launch shape of the kernels whose name contains
-    `kernel`; _sum counters also per compute unit (256)."""
+    directory per run), per launch shape (grid, workgroup, LDS, VGPRs: this
+    also separates template instances that share a truncated name) of the
+    kernels whose name contains `kernel`; _sum counters also per compute
+    unit (256)."""
     import csv
     import glob
     import statistics
@@ -930,10 +947,11 @@ def pmc_table(dirs, kernel):
                 continue
             grid = int(float(r.get("Grid_Size", 0) or 0))
             wg = int(float(r.get("Workgroup_Size", 1) or 1))
-            key = (short_kernel_name(r["Kernel_Name"]), grid // wg if grid >= wg > 0 else grid, wg)
+            key = (short_kernel_name(r["Kernel_Name"]), grid // wg if grid >= wg > 0 else grid, wg,
+                   int(float(r.get("LDS_Block_Size", 0) or 0)), int(float(r.get("VGPR_Count", 0) or 0)))
             vals.setdefault(key, {}).setdefault(r["Counter_Name"].strip(), []).append(float(r["Counter_Value"]))
-    for (name, groups, wg), cs in sorted(vals.items()):
-        print(f"{name}: {groups} workgroups x {wg} threads")
+    for (name, groups, wg, lds, vgpr), cs in sorted(vals.items()):
+        print(f"{name}: {groups} workgroups x {wg} threads, LDS {lds} B, {vgpr} VGPRs")
         for c in sorted(cs):
             v = statistics.mean(cs[c])
             per_cu = f"  ({v / 256:.1f} per CU)" if c.endswith("_sum") else ""
