@@ -190,6 +190,23 @@ def test_chain_small_stagewise():
     assert check_stages(cw, x, st, M, "small") == L
 
 
+@pytest.mark.parametrize("L", [32, 33])
+def test_chain_layer_count_limit(L):
+    """32 layers is the most the single launch takes (its kernel arguments
+    carry every layer's pointers); 33 runs as the graph of GEMM launches.
+    Both checked stage by stage (H = 256, I = 512, 20 rows)."""
+    M, H, I = 20, 256, 512
+    assert vla.vla_mlp_chain_fused_supported(M, H, I, L) == (L <= 32)
+    cw, x, xin, xout, scratch = make_chain(L, M, H, I, seed=40 + L)
+    got = eager(cw, xin, xout, scratch, M)
+    staged_out, st = stage_outputs(cw, xin, M, scratch)
+    assert np.array_equal(staged_out, got)
+    checked = check_stages(cw, x, st, M, f"L={L}")
+    print(f"L={L}: {checked} layers checked stage by stage", flush=True)
+    assert checked >= 12
+    vla.vla_workspace_status(scratch)
+
+
 @pytest.mark.parametrize("M", [1, 10, 16, 17, 33, 50, 64])
 def test_fused_chain_rows_stagewise(M):
     """The single-launch chain at the decoder's H = 1024, I = 4096 for every
