@@ -563,34 +563,49 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
     out["chain_fused_launch"] = bool(vla.vla_mlp_chain_fused_supported(M, H, I, L))
 
     log("secondary: 18-layer decoder-block chain (MLP + fused boundary per layer)")
-    dx, dh, dg, dstyle = synthetic.decoder_chain_inputs(L, M, H, M)
-    d_in = [up_bits(a) for a in (dx, dh, dg)]
-    d_style = [up_bits(s_) for s_ in dstyle]
     d_out = [torch.empty(M * H, dtype=torch.int16, device=dev) for _ in range(3)]
     dsb = vla.vla_decoder_chain_scratch_bytes(M, H, I)
-    dscratch = torch.zeros(dsb, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    h = vla.vla_decoder_chain_create(wgu, sgu, wd, sd, d_style, True, 1e-6, *d_in, *d_out, dscratch, dsb,
-                                     L, M, H, I, cs)
-    try:
-        for _ in range(5):
-            vla.vla_mlp_chain_replay(h, cs)
-        cs.synchronize()
-        warm, cold = [], []
-        for i in range(40):
-            if i % 2 == 1:
-                flush.fill_(i & 0xFF)
-                torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(cs)
-            vla.vla_mlp_chain_replay(h, cs)
-            e1.record(cs)
+    dscratch = torch.zeros(dsb + 256, dtype=torch.uint8, device=dev)
+    styled = {}
+    for per_row in (False, True):
+        dx, dh, dg, dstyle = synthetic.decoder_chain_inputs(L, M, H, M if per_row else 1)
+        styled[per_row] = ([up_bits(a) for a in (dx, dh, dg)], [up_bits(s_) for s_ in dstyle])
+    # one style row for all rows (one sample's conditioning): the single
+    # launch (256-byte aligned scratch) and the graph of three launches per
+    # layer that an unaligned scratch falls back to; a style row per row
+    # (the graph of launches at this M)
+    for prefix, sc, per_row in (("decoder_chain", dscratch[:dsb], False),
+                                ("decoder_chain_graph_path", dscratch[16:16 + dsb], False),
+                                ("decoder_chain_style_per_row", dscratch[:dsb], True)):
+        d_in, d_style = styled[per_row]
+        out[f"{prefix}_fused_launch"] = bool(vla.vla_decoder_chain_fused_supported(M, H, I, L, per_row)) and \
+            sc.data_ptr() % 256 == 0
+        torch.cuda.synchronize()
+        h = vla.vla_decoder_chain_create(wgu, sgu, wd, sd, d_style, per_row, 1e-6, *d_in, *d_out, sc, dsb,
+                                         L, M, H, I, cs)
+        try:
+            for _ in range(5):
+                vla.vla_mlp_chain_replay(h, cs)
             cs.synchronize()
-            (cold if i % 2 == 1 else warm).append(e0.elapsed_time(e1) * 1000.0)
-        out["decoder_chain_us_per_replay_warm"] = round(float(np.median(warm)), 2)
-        out["decoder_chain_us_per_replay_cold"] = round(float(np.median(cold)), 2)
-    finally:
-        vla.vla_mlp_chain_destroy(h)
+            warm, cold, rcold = [], [], []
+            for i in range(60):
+                if i % 3 == 1:
+                    flush.fill_(i & 0xFF)
+                    torch.cuda.synchronize()
+                elif i % 3 == 2:
+                    vla.vla_probe_stream_read(flush, flush.numel(), rf_sink, 2048, cs)
+                    cs.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(cs)
+                vla.vla_mlp_chain_replay(h, cs)
+                e1.record(cs)
+                cs.synchronize()
+                (warm, cold, rcold)[i % 3].append(e0.elapsed_time(e1) * 1000.0)
+            out[f"{prefix}_us_per_replay_warm"] = round(float(np.median(warm)), 2)
+            out[f"{prefix}_us_per_replay_cold"] = round(float(np.median(cold)), 2)
+            out[f"{prefix}_us_per_replay_after_read_flush"] = round(float(np.median(rcold)), 2)
+        finally:
+            vla.vla_mlp_chain_destroy(h)
     del flush
 
     log("secondary: dialect conversion 16384 x 2048")

@@ -63,12 +63,15 @@ SIGNATURES = {
     "vla_gemm_fp8w_gelu_mul": (INT, [P, P, P, P, P, P, P, SZ, I64, I64, I64, P]),
     "vla_mlp_chain_scratch_bytes": (SZ, [I64, I64, I64]),
     "vla_mlp_chain_fused_supported": (INT, [I64, I64, I64, INT]),
+    "vla_decoder_chain_fused_supported": (INT, [I64, I64, I64, INT, INT]),
     "vla_mlp_chain_enqueue": (INT, [P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P]),
     "vla_mlp_chain_create": (INT, [P, P, P, P, P, P, P, SZ, INT, I64, I64, I64, P, P]),
     "vla_mlp_chain_replay": (INT, [P, P]),
     "vla_decoder_chain_scratch_bytes": (SZ, [I64, I64, I64]),
     "vla_decoder_chain_enqueue": (INT, [P, P, P, P, P, INT, ctypes.c_float, P, P, P, P, P, P, P, SZ, INT, I64, I64,
                                         I64, P]),
+    "vla_decoder_chain_enqueue_staged": (INT, [P, P, P, P, P, INT, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, P,
+                                               P, SZ, INT, I64, I64, I64, P]),
     "vla_decoder_chain_create": (INT, [P, P, P, P, P, INT, ctypes.c_float, P, P, P, P, P, P, P, SZ, INT, I64, I64,
                                        I64, P, P]),
     "vla_mlp_chain_destroy": (INT, [P]),
@@ -170,6 +173,11 @@ def vla_mlp_chain_scratch_bytes(M: int, H: int, I: int) -> int:
 def vla_mlp_chain_fused_supported(M: int, H: int, I: int, L: int) -> bool:
     """Whether the chain runs as one persistent launch on the current device."""
     return bool(load().vla_mlp_chain_fused_supported(M, H, I, L))
+
+
+def vla_decoder_chain_fused_supported(M: int, H: int, I: int, L: int, style_per_row: bool) -> bool:
+    """Whether the decoder-block chain of this shape takes the single launch."""
+    return bool(load().vla_decoder_chain_fused_supported(M, H, I, L, 1 if style_per_row else 0))
 
 
 # ----------------------------------------------------------------- codecs
@@ -301,6 +309,16 @@ def vla_decoder_chain_enqueue(wgu, sgu, wd, sd, style, style_per_row, eps, x_in,
                                                            gate_in, x_out, h_out, gate_out, scratch, scratch_bytes,
                                                            L, M, H, I), _stream(stream)),
            "vla_decoder_chain_enqueue")
+
+
+def vla_decoder_chain_enqueue_staged(wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out,
+                                     h_out, gate_out, gu_out, act_out, down_out, x_layers, h_layers, scratch,
+                                     scratch_bytes, L, M, H, I, stream=None):
+    _check(load().vla_decoder_chain_enqueue_staged(
+        _ptr_array(wgu), _ptr_array(sgu), _ptr_array(wd), _ptr_array(sd), _ptr_array(style), int(bool(style_per_row)),
+        float(eps), _ptr(x_in), _ptr(h_in), _ptr(gate_in), _ptr(x_out), _ptr(h_out), _ptr(gate_out), _ptr(gu_out),
+        _ptr(act_out), _ptr(down_out), _ptr(x_layers), _ptr(h_layers), _ptr(scratch), scratch_bytes, L, M, H, I,
+        _stream(stream)), "vla_decoder_chain_enqueue_staged")
 
 
 def vla_decoder_chain_create(wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <utility>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -228,10 +229,14 @@ int enqueue_chain(const char* fn, const uint8_t* const* wgu, const float* const*
     return VLA_OK;
 }
 
-// Decoder-block chain scratch: GEMM workspace | x | h | gate (two,
-// alternating) | down output | act.
+// Decoder-block chain scratch, laid out for both paths.  Graph of launches:
+// GEMM workspace | (barrier words) | x | h | gate (two, alternating) | down
+// output | act.
+// Single launch: the gated-MLP chain's layout (GEMM workspace | barrier
+// words | x per layer | act per layer) followed by the per-layer partial
+// sums of squares (L x M x H/16 fp64).
 struct DecoderLayout {
-    size_t ws_off, x_off, h_off, g_off[2], d_off, act_off, total, ws_bytes;
+    size_t ws_off, x_off, h_off, g_off[2], d_off, act_off, ssp_off, total, ws_bytes;
 };
 
 DecoderLayout decoder_layout(int64_t M, int64_t H, int64_t I) {
@@ -239,13 +244,19 @@ DecoderLayout decoder_layout(int64_t M, int64_t H, int64_t I) {
     DecoderLayout c{};
     c.ws_off = 0;
     c.ws_bytes = chain_ws_bytes(M, H, I);
-    c.x_off = c.ws_bytes;
+    // the graph path's buffers start past the single launch's barrier
+    // words, which must stay zero between launches
+    c.x_off = c.ws_bytes + vla::kChainSyncBytes;
     c.h_off = c.x_off + mh;
     c.g_off[0] = c.x_off + 2 * mh;
     c.g_off[1] = c.x_off + 3 * mh;
     c.d_off = c.x_off + 4 * mh;
     c.act_off = c.x_off + 5 * mh;
-    c.total = c.act_off + round256(static_cast<size_t>(M) * I * 2);
+    const size_t graph_total = c.act_off + round256(static_cast<size_t>(M) * I * 2);
+    const ChainLayout f = chain_layout(M, H, I);
+    c.ssp_off = f.total;
+    const size_t fused_total = c.ssp_off + round256(static_cast<size_t>(vla::kMaxChainLayers) * M * (H / 16) * 8);
+    c.total = graph_total > fused_total ? graph_total : fused_total;
     return c;
 }
 
@@ -298,13 +309,59 @@ int check_decoder(const char* fn, const uint8_t* const* wgu, const float* const*
     return VLA_OK;
 }
 
+// Per-layer stage outputs of the decoder-block chain (each nullable): those
+// of the gated-MLP chain plus h after each layer (L x M x H).
+struct DecoderStages {
+    ChainStages mlp;
+    uint16_t* h = nullptr;
+};
+
+// Whether the decoder-block chain of this shape takes the single launch
+// (given aligned buffers): the gated-MLP chain's conditions, H at most 1024
+// (a row's partial sums of squares fit one load), and, with a style row per
+// activation row, at most one 16-row tile - beyond that every workgroup
+// stages 16 rows of scale and shift per layer and the graph of launches
+// measured faster.
+bool decoder_fused(int64_t M, int64_t H, int64_t I, int L, int style_per_row) {
+    int npa = 0;
+    return H <= 1024 && !(style_per_row && M > 16) && vla::chain_fused_plan(M, H, I, L, &npa) &&
+           vla::chain_fused_resident(H, I, npa);
+}
+
 int enqueue_decoder(const char* fn, const uint8_t* const* wgu, const float* const* sgu, const uint8_t* const* wd,
                     const float* const* sd, const uint16_t* const* style, int style_per_row, float eps,
                     const uint16_t* x_in, const uint16_t* h_in, const uint16_t* gate_in, uint16_t* x_out,
                     uint16_t* h_out, uint16_t* gate_out, void* scratch, int L, int64_t M, int64_t H, int64_t I,
-                    hipStream_t s) {
+                    const DecoderStages& st, hipStream_t s) {
     const DecoderLayout c = decoder_layout(M, H, I);
     uint8_t* base = static_cast<uint8_t*>(scratch);
+    const size_t mh = static_cast<size_t>(M) * H, mi = static_cast<size_t>(M) * I;
+    // One persistent launch for every layer (the gated-MLP chain's kernel
+    // with the boundary after each layer) where decoder_fused allows it and
+    // every buffer it writes is 256-byte aligned.
+    auto a256 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; };
+    const ChainStages& ms = st.mlp;
+    const bool aligned = a256(scratch) && a256(ms.gu) && a256(ms.act) && a256(ms.down) && a256(ms.x) && a256(st.h) &&
+                         (mh * 2) % 256 == 0 && (mi * 2) % 256 == 0;
+    if (aligned && decoder_fused(M, H, I, L, style_per_row)) {
+        const ChainLayout f = chain_layout(M, H, I);
+        vla::ChainLaunch cl{};
+        cl.wgu = wgu; cl.sgu = sgu; cl.wd = wd; cl.sd = sd;
+        cl.x_in = x_in; cl.x_out = x_out;
+        cl.xbuf = ms.x ? ms.x : reinterpret_cast<uint16_t*>(base + f.x_off);
+        cl.xstride = ms.x ? static_cast<int64_t>(mh) : static_cast<int64_t>(f.x_stride / 2);
+        cl.xlast = ms.x ? ms.x + (L - 1) * mh : nullptr;
+        cl.actbuf = ms.act ? ms.act : reinterpret_cast<uint16_t*>(base + f.act_off);
+        cl.gu_out = ms.gu; cl.down_out = ms.down;
+        cl.sync = reinterpret_cast<uint32_t*>(base + f.sync_off);
+        cl.err = reinterpret_cast<uint32_t*>(base + c.ws_off + vla::kStatusOffset);
+        cl.L = L; cl.M = M; cl.H = H; cl.I = I;
+        cl.style = style; cl.style_per_row = style_per_row ? 1 : 0; cl.eps = eps;
+        cl.h_in = h_in; cl.g_in = gate_in; cl.h_out = h_out; cl.g_out = gate_out; cl.hbuf = st.h;
+        cl.sspart = reinterpret_cast<double*>(base + c.ssp_off);
+        hipError_t e = vla::launch_mlp_chain_fused(cl, s);
+        return e == hipSuccess ? VLA_OK : hip_fail(fn, "fused decoder chain launch", e);
+    }
     uint16_t* xs = reinterpret_cast<uint16_t*>(base + c.x_off);
     uint16_t* hs = reinterpret_cast<uint16_t*>(base + c.h_off);
     uint16_t* gs[2] = {reinterpret_cast<uint16_t*>(base + c.g_off[0]), reinterpret_cast<uint16_t*>(base + c.g_off[1])};
@@ -313,24 +370,36 @@ int enqueue_decoder(const char* fn, const uint8_t* const* wgu, const float* cons
     void* ws = base + c.ws_off;
     const uint16_t *x = x_in, *h = h_in, *g = gate_in;
     for (int l = 0; l < L; ++l) {
+        uint16_t* actl = ms.act ? ms.act + l * mi : act;
+        uint16_t* dl = ms.down ? ms.down + l * mh : dbuf;
         vla::GemmProblem gp{};
-        gp.A = h; gp.W = wgu[l]; gp.s_w = sgu[l]; gp.Y = act; gp.ws = ws;
+        gp.A = h; gp.W = wgu[l]; gp.s_w = sgu[l]; gp.Y = actl; gp.ws = ws;
+        gp.gu = ms.gu ? ms.gu + l * 2 * mi : nullptr;
         gp.M = M; gp.N = 2 * I; gp.K = H;
         gp.atype = vla::AType::BF16; gp.wtype = vla::WType::FP8; gp.epi = vla::Epi::GELU_MUL;
         if (int rc = run_gemm(fn, gp, c.ws_bytes, s)) return rc;
         vla::GemmProblem dp{};
-        dp.A = act; dp.W = wd[l]; dp.s_w = sd[l]; dp.Y = dbuf; dp.ws = ws;
+        dp.A = actl; dp.W = wd[l]; dp.s_w = sd[l]; dp.Y = dl; dp.ws = ws;
         dp.M = M; dp.N = H; dp.K = I;
         dp.atype = vla::AType::BF16; dp.wtype = vla::WType::FP8; dp.epi = vla::Epi::PLAIN;
         if (int rc = run_gemm(fn, dp, c.ws_bytes, s)) return rc;
         const bool last = l == L - 1;
-        uint16_t* xo = last ? x_out : xs;        // in place from the second layer on
-        uint16_t* ho = last ? h_out : hs;        // this layer's GEMM has read h already
+        // per-layer stage buffers when given (the last ones then copied
+        // out), else x and h in place from the second layer on (this
+        // layer's GEMM has read h already) and the gate alternating
+        uint16_t* xo = ms.x ? ms.x + l * mh : (last ? x_out : xs);
+        uint16_t* ho = st.h ? st.h + l * mh : (last ? h_out : hs);
         uint16_t* go = last ? gate_out : gs[l & 1];
-        hipError_t e = vla::launch_gate_residual_ada_norm(x, dbuf, g, style[l], style_per_row ? 1 : 0, eps, xo, ho, go,
+        hipError_t e = vla::launch_gate_residual_ada_norm(x, dl, g, style[l], style_per_row ? 1 : 0, eps, xo, ho, go,
                                                           M, H, s);
         if (e != hipSuccess) return hip_fail(fn, "boundary launch", e);
         x = xo; h = ho; g = go;
+    }
+    for (auto [dst, src] : {std::pair<uint16_t*, const uint16_t*>{x_out, ms.x ? x : nullptr},
+                            std::pair<uint16_t*, const uint16_t*>{h_out, st.h ? h : nullptr}}) {
+        if (!src) continue;
+        hipError_t e = hipMemcpyAsync(dst, src, mh * 2, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(fn, "hipMemcpyAsync", e);
     }
     return VLA_OK;
 }
@@ -798,6 +867,10 @@ int vla_mlp_chain_fused_supported(int64_t M, int64_t H, int64_t I, int L) {
     return (vla::chain_fused_plan(M, H, I, L, &npa) && vla::chain_fused_resident(H, I, npa)) ? 1 : 0;
 }
 
+int vla_decoder_chain_fused_supported(int64_t M, int64_t H, int64_t I, int L, int style_per_row) {
+    return decoder_fused(M, H, I, L, style_per_row) ? 1 : 0;
+}
+
 size_t vla_decoder_chain_scratch_bytes(int64_t M, int64_t H, int64_t I) {
     if (M <= 0 || H <= 0 || I <= 0) return 0;
     return decoder_layout(M, H, I).total;
@@ -813,7 +886,47 @@ int vla_decoder_chain_enqueue(const uint8_t* const* wgu, const float* const* sgu
                                gate_out, scratch, scratch_bytes, L, M, H, I))
         return rc;
     return enqueue_decoder(fn, wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
-                           gate_out, scratch, L, M, H, I, static_cast<hipStream_t>(stream));
+                           gate_out, scratch, L, M, H, I, DecoderStages{}, static_cast<hipStream_t>(stream));
+}
+
+int vla_decoder_chain_enqueue_staged(const uint8_t* const* wgu, const float* const* sgu, const uint8_t* const* wd,
+                                     const float* const* sd, const uint16_t* const* style, int style_per_row,
+                                     float eps, const uint16_t* x_in, const uint16_t* h_in, const uint16_t* gate_in,
+                                     uint16_t* x_out, uint16_t* h_out, uint16_t* gate_out, uint16_t* gu_out,
+                                     uint16_t* act_out, uint16_t* down_out, uint16_t* x_layers, uint16_t* h_layers,
+                                     void* scratch, size_t scratch_bytes, int L, int64_t M, int64_t H, int64_t I,
+                                     void* stream) {
+    const char* fn = "vla_decoder_chain_enqueue_staged";
+    if (int rc = check_decoder(fn, wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
+                               gate_out, scratch, scratch_bytes, L, M, H, I))
+        return rc;
+    OPTIONAL_PTR(gu_out);
+    OPTIONAL_PTR(act_out);
+    OPTIONAL_PTR(down_out);
+    OPTIONAL_PTR(x_layers);
+    OPTIONAL_PTR(h_layers);
+    const size_t mh = static_cast<size_t>(M) * H * 2, mhl = mh * L, mil = static_cast<size_t>(M) * I * 2 * L;
+    struct Range { const void* p; size_t n; };
+    const Range outs[5] = {{gu_out, 2 * mil}, {act_out, mil}, {down_out, mhl}, {x_layers, mhl}, {h_layers, mhl}};
+    const Range others[7] = {{x_in, mh}, {h_in, mh}, {gate_in, mh}, {x_out, mh}, {h_out, mh}, {gate_out, mh},
+                             {scratch, decoder_layout(M, H, I).total}};
+    auto overlap = [](const Range& x, const Range& y) {
+        const uint8_t *a = static_cast<const uint8_t*>(x.p), *b = static_cast<const uint8_t*>(y.p);
+        return a && b && a < b + y.n && b < a + x.n;
+    };
+    const size_t sty = static_cast<size_t>(style_per_row ? M : 1) * 3 * H * 2;
+    for (int i = 0; i < 5; ++i) {
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(outs[i], outs[j])) return fail(VLA_EINVAL, fn, "stage outputs %d and %d overlap", i, j);
+        for (int j = 0; j < 7; ++j)
+            if (overlap(outs[i], others[j])) return fail(VLA_EINVAL, fn, "stage output %d overlaps an input, output or the scratch", i);
+        for (int l = 0; l < L; ++l)
+            if (overlap(outs[i], Range{style[l], sty})) return fail(VLA_EINVAL, fn, "stage output %d overlaps style %d", i, l);
+    }
+    DecoderStages st;
+    st.mlp.gu = gu_out; st.mlp.act = act_out; st.mlp.down = down_out; st.mlp.x = x_layers; st.h = h_layers;
+    return enqueue_decoder(fn, wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
+                           gate_out, scratch, L, M, H, I, st, static_cast<hipStream_t>(stream));
 }
 
 int vla_decoder_chain_create(const uint8_t* const* wgu, const float* const* sgu, const uint8_t* const* wd,
@@ -830,7 +943,7 @@ int vla_decoder_chain_create(const uint8_t* const* wgu, const float* const* sgu,
         return rc;
     return capture_chain(fn, capture_stream, L, out, [&](hipStream_t s) {
         return enqueue_decoder(fn, wgu, sgu, wd, sd, style, style_per_row, eps, x_in, h_in, gate_in, x_out, h_out,
-                               gate_out, scratch, L, M, H, I, s);
+                               gate_out, scratch, L, M, H, I, DecoderStages{}, s);
     });
 }
 

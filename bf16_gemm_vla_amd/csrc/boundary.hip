@@ -19,6 +19,7 @@
 
 #include <cstdint>
 
+#include "vla_device.h"
 #include "vla_internal.h"
 
 namespace vla {
@@ -38,19 +39,6 @@ struct BArgs {
     int style_per_row;
     float eps;
 };
-
-__device__ __forceinline__ double bf16_f64(uint32_t bits16) { return static_cast<double>(__uint_as_float(bits16 << 16)); }
-
-// Nearest-even bf16 of an fp64 value with one rounding: truncate to fp32,
-// set the lowest bit if that was inexact (round to odd keeps the 29 dropped
-// bits' information in a sticky bit), then round the fp32 bits to bf16.
-__device__ __forceinline__ uint32_t f64_to_bf16(double v) {
-    const float t = __double2float_rz(v);
-    uint32_t b = __float_as_uint(t);
-    if (static_cast<double>(t) != v) b |= 1u;
-    b += 0x7FFFu + ((b >> 16) & 1u);
-    return b >> 16;
-}
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -91,9 +79,8 @@ __global__ __launch_bounds__(kBThreads) void gate_residual_ada_norm_kernel(BArgs
         uint32_t rw[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const double v0 = bf16_f64(xw[h] & 0xFFFFu) + bf16_f64(yw[h] & 0xFFFFu) * bf16_f64(gw[h] & 0xFFFFu);
-            const double v1 = bf16_f64(xw[h] >> 16) + bf16_f64(yw[h] >> 16) * bf16_f64(gw[h] >> 16);
-            const uint32_t b0 = f64_to_bf16(v0), b1 = f64_to_bf16(v1);
+            const uint32_t b0 = gated_residual_bf16(xw[h] & 0xFFFFu, yw[h] & 0xFFFFu, gw[h] & 0xFFFFu);
+            const uint32_t b1 = gated_residual_bf16(xw[h] >> 16, yw[h] >> 16, gw[h] >> 16);
             rw[h] = b0 | (b1 << 16);
             r[c][2 * h] = bf16_f64(b0);
             r[c][2 * h + 1] = bf16_f64(b1);

@@ -78,6 +78,16 @@ struct ChainArgs {
     int64_t xstride;          // elements between consecutive xbuf layers
     uint32_t wait_polls;
     int L, M, MT;
+    // decoder-block chain: the boundary closes every layer
+    const uint16_t* style[kMaxChainLayers];   // per layer: rows of [scale | shift | next gate], 3H each
+    const uint16_t* h_in;     // M x H: the first layer's normalized input
+    const uint16_t* g_in;     // M x H: the first layer's gate
+    uint16_t* h_out;          // M x H
+    uint16_t* g_out;          // M x H
+    uint16_t* hbuf;           // nullable: h after each layer, L x M x H
+    double* sspart;           // per layer, row and 16-column tile: sum of squares of the residual, L x M x H/16
+    float eps;
+    int style_per_row;
 };
 
 // 8-byte store of four bf16 at element `elem` of a buffer of `n` elements
@@ -93,7 +103,7 @@ __device__ __forceinline__ void store_b64_coherent(uint16_t* base, int64_t n, in
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, static_cast<int>(elem * 2), 0, kCpolSC1);
 }
 
-template <int SA, int SB, int NPA>
+template <int SA, int SB, int NPA, bool DEC>
 __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
     constexpr int WPA = kCW / NPA;           // compute waves per gate/up pair
     constexpr int H = SA * WPA * 32;         // phase A depth (hidden size)
@@ -105,8 +115,21 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
     // phase A: gate and up scales of the NPA pairs after the reduction area;
     // phase B: the tile's 16 scales and its 16 x 16 residual block
     constexpr int SCL_A = ACT_A + RED_A, SCL_B = ACT_B + RED_B;
-    constexpr int END_A = SCL_A + 2 * NPA * 64, END_B = SCL_B + 64 + 16 * 32;
+    constexpr int END_A0 = SCL_A + 2 * NPA * 64, END_B0 = SCL_B + 64 + 16 * 32;
+    // decoder-block chain: phase A also holds the tile's style rows (scale |
+    // shift, 4H bytes each) and the rows' 1/rms; phase B the tile's gate
+    // block and (after the last layer) 1/rms again
+    constexpr int RSS = 4 * H + 16;
+    constexpr int G = H / 16;                // 16-column tiles of a row (sum-of-squares partials per row)
+    constexpr int SSR = G * 8 + 16;          // LDS row stride of the partials (+16 B: rows on different banks)
+    constexpr int SSP = 16 * SSR;            // the tile rows' partials
+    constexpr int STY_A = END_A0, INV_A = STY_A + 16 * RSS, SSP_A = INV_A + 128 + 64 * 8;
+    constexpr int GB_B = END_B0, INV_B = GB_B + 16 * 32;
+    constexpr int END_A = DEC ? SSP_A + SSP : END_A0, END_B = DEC ? INV_B + 128 + 64 * 8 : END_B0;
     constexpr int LDS_BYTES = END_A > END_B ? END_A : END_B;
+    static_assert(SSP <= ACT_B, "the last layer's partials fit the free phase-B activation area");
+    static_assert(!DEC || 16 * 4 * 8 <= 128 + 64 * 8, "the phase-B row partial quarters fit the 1/rms area");
+    static_assert(!DEC || (G <= 64 && G % 4 == 0), "a row's partials in one load and four quarters");
     static_assert(LDS_BYTES <= 160 * 1024, "a phase's activation rows and reduction fit the LDS");
     static_assert(2 * SA + 2 <= 63 && SB + 2 <= 63, "the prefetch counts fit the vmcnt field");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
@@ -188,6 +211,18 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
             const uint8_t* xr = reinterpret_cast<const uint8_t*>(xl_ptr(l) + static_cast<int64_t>(m0 + row) * H + grp * 16 + 8 * half);
             if (lane >= 4 && lane < 36 && row < mrows)
                 __builtin_amdgcn_global_load_lds(xr, (__attribute__((address_space(3))) void*)(lds + SCL_B), 16, 0, 0);
+            if constexpr (DEC) {
+                // the layer's gate block: the given gate for layer 0, else
+                // the previous layer's style (its third block)
+                const int grow = lane >> 1, ghalf = lane & 1;            // lanes 0 .. 31: rows 0 .. 15
+                const uint16_t* gbase = l == 0 ? a.g_in + static_cast<int64_t>(m0) * H
+                                               : a.style[l - 1] + (a.style_per_row ? static_cast<int64_t>(m0) * 3 * H : 0) + 2 * H;
+                const int gstride = (l == 0 || a.style_per_row) ? (l == 0 ? H : 3 * H) : 0;   // elements between rows
+                const uint32_t goff = static_cast<uint32_t>((grow * gstride + grp * 16 + 8 * ghalf) * 2);
+                if (lane < 32 && grow < mrows)
+                    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(gbase) + goff,
+                                                     (__attribute__((address_space(3))) void*)(lds + GB_B), 16, 0, 0);
+            }
         }
     };
     // The control wave loads no weights; giving its copies a value on its
@@ -204,17 +239,21 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
     // Stage activation rows m0 .. m0+mrows-1 (RB bytes each) of src into LDS
     // rows of stride RS with direct global -> LDS loads, 1 KiB per wave
     // instruction, shared by all nine waves.
-    auto stage = [&](const uint16_t* src, int RB, int RS) __attribute__((always_inline)) {
+    auto stage_rows = [&](const uint8_t* base, int64_t sstride, int nrows, int RB, int dst, int RS)
+                          __attribute__((always_inline)) {
         const int pieces = (RB + 1023) / 1024;
-        for (int pc = wave; pc < mrows * pieces; pc += kCW + 1) {
+        for (int pc = wave; pc < nrows * pieces; pc += kCW + 1) {
             const int row = pc / pieces, p = pc % pieces;
             const int byte = p * 1024 + lane * 16;
             if (byte < RB) {
-                const uint8_t* g = reinterpret_cast<const uint8_t*>(src) + (static_cast<int64_t>(m0 + row) * RB + byte);
-                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + row * RS + p * 1024),
+                const uint8_t* g = base + (static_cast<int64_t>(row) * sstride + byte);
+                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + dst + row * RS + p * 1024),
                                                  16, 0, 0);
             }
         }
+    };
+    auto stage = [&](const uint16_t* src, int RB, int RS) __attribute__((always_inline)) {
+        stage_rows(reinterpret_cast<const uint8_t*>(src) + static_cast<int64_t>(m0) * RB, RB, mrows, RB, 0, RS);
     };
     // Barrier number b (0-based) of this workgroup's row-tile group: phase A
     // of tile t reads only rows of tile t of x, which phase B of the same
@@ -261,6 +300,87 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
     };
 
+    // ---- decoder boundary pieces (DEC) ----
+    // The style rows (scale | shift) of layer lp for the tile's rows (one
+    // shared row when the style is not per row) -> LDS at STY_A.
+    auto stage_style = [&](int lp) __attribute__((always_inline)) {
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(a.style[lp] + (a.style_per_row ? static_cast<int64_t>(m0) * 3 * H : 0));
+        stage_rows(base, static_cast<int64_t>(6) * H, a.style_per_row ? mrows : 1, 4 * H, STY_A, RSS);
+    };
+    // The G per-tile partial sums of squares of the tile's rows after layer
+    // lp's residual update (written by other workgroups in this launch:
+    // device-coherent loads) -> LDS at dst, by the control wave.
+    auto stage_partials = [&](int lp, int dst) __attribute__((always_inline)) {
+        if (wave == kCW) {
+            // one load per row (G * 8 <= 512 bytes: lanes 0 .. G/2-1), rows SSR apart in LDS
+            const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sspart + (static_cast<int64_t>(lp) * a.M + m0) * G);
+            for (int rr = 0; rr < mrows; ++rr)
+                if (lane * 16 < G * 8)
+                    __builtin_amdgcn_global_load_lds(base + rr * G * 8 + lane * 16,
+                                                     (__attribute__((address_space(3))) void*)(lds + dst + rr * SSR), 16, 0,
+                                                     kCpolSC1);
+        }
+    };
+    // 1/rms of each staged row from its partials in LDS (src): lane rr sums
+    // row rr's G partials in column order (no cross-lane steps: a chain of
+    // shuffles per row would cost a round trip through the LDS crossbar per
+    // step); fp64 values at LDS offset dst.
+    auto row_inv = [&](int src, int dst) __attribute__((always_inline)) {
+        // lane 4 rr + k sums quarter k of row rr's partials, then lane rr
+        // adds the four quarters in order (through LDS: the quarters go to
+        // dst + 128, read back by the same wave)
+        constexpr int GQ = G / 4;
+        const int rr = lane >> 2, k = lane & 3;
+        double part = 0.0;
+        if (rr < mrows) {
+            const double* pp = reinterpret_cast<const double*>(lds + src + rr * SSR) + k * GQ;
+#pragma unroll
+            for (int j = 0; j < GQ; ++j) part += pp[j];
+        }
+        double* const quart = reinterpret_cast<double*>(lds + dst + 128);
+        quart[lane] = part;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+        if (lane < mrows) {
+            const double tot = ((quart[4 * lane] + quart[4 * lane + 1]) + quart[4 * lane + 2]) + quart[4 * lane + 3];
+            *reinterpret_cast<double*>(lds + dst + lane * 8) = 1.0 / sqrt(tot / static_cast<double>(H) + static_cast<double>(a.eps));
+        }
+    };
+    // h = bf16(r * (1/rms) * (1 + scale) + shift), fp32, one output value
+    auto norm1 = [](float r, float inv, float sc, float sh) __attribute__((always_inline)) {
+        return r * inv * (1.0f + sc) + sh;
+    };
+    // Normalize the staged rows of x (the residual after layer lp) in place:
+    // they become h, the next GEMM's input.
+    auto normalize = [&](int lp) __attribute__((always_inline)) {
+        (void)lp;
+        constexpr int C8 = H / 8;                                   // 16-byte chunks per row
+        for (int c = tid; wave <= kCW && c < mrows * C8; c += (kCW + 1) * 64) {
+            const int row = c / C8, k8 = c % C8;
+            const int srow = a.style_per_row ? row : 0;
+            u32x4_t rv = *reinterpret_cast<const u32x4_t*>(lds + row * RSA + k8 * 16);
+            const u32x4_t sc = *reinterpret_cast<const u32x4_t*>(lds + STY_A + srow * RSS + k8 * 16);
+            const u32x4_t sh = *reinterpret_cast<const u32x4_t*>(lds + STY_A + srow * RSS + 2 * H + k8 * 16);
+            const float inv = static_cast<float>(*reinterpret_cast<const double*>(lds + INV_A + row * 8));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                rv[i] = f32x2_to_bf16x2(norm1(bf16_to_f32(lo16(rv[i])), inv, bf16_to_f32(lo16(sc[i])), bf16_to_f32(lo16(sh[i]))),
+                                        norm1(bf16_to_f32(hi16(rv[i])), inv, bf16_to_f32(hi16(sc[i])), bf16_to_f32(hi16(sh[i]))));
+            *reinterpret_cast<u32x4_t*>(lds + row * RSA + k8 * 16) = rv;
+        }
+    };
+    // The staged h rows of layer lp -> hbuf (per-layer stage output).
+    auto write_h = [&](int lp) __attribute__((always_inline)) {
+        constexpr int C8 = H / 8;
+        const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+            a.hbuf + (static_cast<int64_t>(lp) * a.M + m0) * H, 0, mrows * H * 2, kRsrcWord3);
+        for (int c = tid; wave <= kCW && c < mrows * C8; c += (kCW + 1) * 64) {
+            const int row = c / C8, k8 = c % C8;
+            __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(lds + row * RSA + k8 * 16), rh,
+                                                   static_cast<uint32_t>((row * H + k8 * 8) * 2), 0, 0);
+        }
+    };
+
     auto red_a = reinterpret_cast<f32x4_t(*)[2][64]>(lds + ACT_A);
     auto red_b = reinterpret_cast<f32x4_t(*)[64]>(lds + ACT_B);
 
@@ -276,11 +396,29 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
         const uint16_t* xl = xl_ptr(l);
         uint16_t* act = a.actbuf + static_cast<int64_t>(l) * a.M * I;
         // ---------------- phase A: gate/up GEMM + GELU * up (its weights
-        // were requested before the barrier that opens it)
-        stage(xl, H * 2, RSA);
+        // were requested before the barrier that opens it).  Decoder-block
+        // chain: the input is h, the first layer's given, later the staged
+        // residual normalized here with the previous layer's style.
+        const bool norm_in = DEC && l > 0;
+        stage((DEC && l == 0) ? a.h_in : xl, H * 2, RSA);
         stage_epi_a(l);
+        if constexpr (DEC) {
+            if (norm_in) {
+                stage_style(l - 1);
+                stage_partials(l - 1, SSP_A);
+            }
+        }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         lds_barrier();
+        if constexpr (DEC) {
+            if (norm_in) {
+                if (wave == kCW) row_inv(SSP_A, INV_A);
+                lds_barrier();
+                normalize(l - 1);
+                lds_barrier();
+                if (a.hbuf && grp == 0) write_h(l - 1);
+            }
+        }
         if (compute) {
             f32x4_t acc[2] = {f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}};
             const uint8_t* arow = lds + mrow * RSA + (kh * SA * 32 + 8 * q) * 2;
@@ -376,7 +514,38 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
             const uint2 xres = *reinterpret_cast<const uint2*>(lds + SCL_B + 64 + mrow * 32 + 8 * q);
             const float y0 = v[0] * sdb.x, y1 = v[1] * sdb.y, y2 = v[2] * sdb.z, y3 = v[3] * sdb.w;
             const uint2 y = make_uint2(f32x2_to_bf16x2(y0, y1), f32x2_to_bf16x2(y2, y3));
-            const uint2 xn = make_uint2(add_resid2(y.x, xres.x), add_resid2(y.y, xres.y));
+            uint2 xn;
+            if constexpr (DEC) {
+                // gated residual bf16(x + y * gate), exact in fp64, rounded once
+                const uint2 gt = *reinterpret_cast<const uint2*>(lds + GB_B + mrow * 32 + 8 * q);
+                const uint32_t r0 = gated_residual_bf16(xres.x & 0xFFFFu, y.x & 0xFFFFu, gt.x & 0xFFFFu);
+                const uint32_t r1 = gated_residual_bf16(xres.x >> 16, y.x >> 16, gt.x >> 16);
+                const uint32_t r2 = gated_residual_bf16(xres.y & 0xFFFFu, y.y & 0xFFFFu, gt.y & 0xFFFFu);
+                const uint32_t r3 = gated_residual_bf16(xres.y >> 16, y.y >> 16, gt.y >> 16);
+                xn = make_uint2(r0 | (r1 << 16), r2 | (r3 << 16));
+                // the row's sum of squares over these 16 columns (lanes
+                // mrow + 16 q), in one fixed order, as this tile's partial
+                double ss = 0.0;
+                ss += bf16_f64(r0) * bf16_f64(r0);
+                ss += bf16_f64(r1) * bf16_f64(r1);
+                ss += bf16_f64(r2) * bf16_f64(r2);
+                ss += bf16_f64(r3) * bf16_f64(r3);
+                // through LDS (the row's four lanes' values, then summed in
+                // q order by lane q == 0): cheaper than shuffle round trips
+                double* const sq = reinterpret_cast<double*>(lds + INV_B);       // 16 x 4 doubles, free here
+                sq[mrow * 4 + q] = ss;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __builtin_amdgcn_wave_barrier();
+                const double rs = ((sq[mrow * 4] + sq[mrow * 4 + 1]) + sq[mrow * 4 + 2]) + sq[mrow * 4 + 3];
+                if (q == 0) {
+                    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+                        a.sspart + static_cast<int64_t>(l) * a.M * G, 0, a.M * G * 8, kRsrcWord3);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, rs), rp,
+                                                          static_cast<int>(((m0 + mrow) * G + grp) * 8), 0, kCpolSC1);
+                }
+            } else {
+                xn = make_uint2(add_resid2(y.x, xres.x), add_resid2(y.y, xres.y));
+            }
             const int64_t e = static_cast<int64_t>(m0 + mrow) * H + nb;
             const int64_t mh = static_cast<int64_t>(a.M) * H;
             if (!more) {
@@ -387,7 +556,46 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
             }
             if (a.down_out) store_b64(a.down_out + static_cast<int64_t>(l) * mh, mh, e, y);
         }
-        if (!more) break;
+        if (!more) {
+            if constexpr (DEC) {
+                // h and the next gate of the last layer: every partial of
+                // the tile's rows is in after one more barrier
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                ok = group_barrier(b++);
+                if (ok) {
+                    stage_partials(l, 0);
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    lds_barrier();
+                    if (wave == kCW) row_inv(0, INV_B);
+                    lds_barrier();
+                    if (wave == 0 && vb && mrow < mrows) {
+                        // this lane's residual values, stored by this wave above (complete)
+                        const int64_t mhb = static_cast<int64_t>(a.M) * H * 2;
+                        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(a.x_out, 0, static_cast<int>(mhb), kRsrcWord3);
+                        const uint2 xn_keep = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                            rx, static_cast<uint32_t>(((m0 + mrow) * H + nb) * 2), 0, 0));
+                        const float inv = static_cast<float>(*reinterpret_cast<const double*>(lds + INV_B + mrow * 8));
+                        const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
+                            const_cast<uint16_t*>(a.style[l]), 0, (a.style_per_row ? a.M : 1) * 3 * H * 2, kRsrcWord3);
+                        const uint32_t so = static_cast<uint32_t>(((a.style_per_row ? (m0 + mrow) * 3 * H : 0) + nb) * 2);
+                        const uint2 sc = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rst, so, 0, 0));
+                        const uint2 sh = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rst, so + 2 * H, 0, 0));
+                        const uint2 ng = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rst, so + 4 * H, 0, 0));
+                        const uint2 hv = make_uint2(
+                            f32x2_to_bf16x2(norm1(bf16_to_f32(lo16(xn_keep.x)), inv, bf16_to_f32(lo16(sc.x)), bf16_to_f32(lo16(sh.x))),
+                                            norm1(bf16_to_f32(hi16(xn_keep.x)), inv, bf16_to_f32(hi16(sc.x)), bf16_to_f32(hi16(sh.x)))),
+                            f32x2_to_bf16x2(norm1(bf16_to_f32(lo16(xn_keep.y)), inv, bf16_to_f32(lo16(sc.y)), bf16_to_f32(lo16(sh.y))),
+                                            norm1(bf16_to_f32(hi16(xn_keep.y)), inv, bf16_to_f32(hi16(sc.y)), bf16_to_f32(hi16(sh.y)))));
+                        const int64_t e = static_cast<int64_t>(m0 + mrow) * H + nb;
+                        const int64_t mh = static_cast<int64_t>(a.M) * H;
+                        store_b64(a.h_out, mh, e, hv);
+                        store_b64(a.g_out, mh, e, ng);
+                        if (a.hbuf) store_b64(a.hbuf + static_cast<int64_t>(l) * mh, mh, e, hv);
+                    }
+                }
+            }
+            break;
+        }
         // this wave's stores complete, then the next layer's phase-A weights
         // are requested (phase B's weights are dead by now: the two phases'
         // fragments never hold registers at once); they stream in during the
@@ -406,6 +614,7 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
         const int64_t e = static_cast<int64_t>(m0 + mrow) * H + nb;
         store_b64(a.x_out, static_cast<int64_t>(a.M) * H, e, nan2);
         if (a.xlast) store_b64(a.xlast, static_cast<int64_t>(a.M) * H, e, nan2);
+        if (DEC) store_b64(a.h_out, static_cast<int64_t>(a.M) * H, e, nan2);
     }
     // the last workgroup out clears the counters and the abort word for the
     // next launch
@@ -470,9 +679,16 @@ hipError_t launch_mlp_chain_fused(const ChainLaunch& c, hipStream_t s) {
     a.sync = c.sync; a.err = c.err; a.xstride = c.xstride;
     a.wait_polls = wait_polls();
     a.L = c.L; a.M = static_cast<int>(c.M); a.MT = static_cast<int>((c.M + 15) / 16);
+    const bool dec = c.style != nullptr;
+    if (dec) {
+        for (int l = 0; l < c.L; ++l) a.style[l] = c.style[l];
+        a.h_in = c.h_in; a.g_in = c.g_in; a.h_out = c.h_out; a.g_out = c.g_out; a.hbuf = c.hbuf;
+        a.sspart = c.sspart; a.eps = c.eps; a.style_per_row = c.style_per_row;
+    }
 #define VLA_CASE(SA_, SB_, NPA_)                                                                                \
     if (NPA_ == npa && ChainCfg<SA_, SB_, NPA_>::H == c.H && ChainCfg<SA_, SB_, NPA_>::I == c.I) {              \
-        mlp_chain_kernel<SA_, SB_, NPA_><<<kChainGrid, kThreads, 0, s>>>(a);                                   \
+        if (dec) mlp_chain_kernel<SA_, SB_, NPA_, true><<<kChainGrid, kThreads, 0, s>>>(a);                    \
+        else mlp_chain_kernel<SA_, SB_, NPA_, false><<<kChainGrid, kThreads, 0, s>>>(a);                       \
         return hipGetLastError();                                                                               \
     }
     VLA_CHAIN_CONFIGS(VLA_CASE)
@@ -494,9 +710,11 @@ bool chain_fused_resident(int64_t H, int64_t I, int npa) {
         // every compiled configuration must fit one workgroup per compute unit
 #define VLA_CASE(SA_, SB_, NPA_)                                                                                \
     if (ok) {                                                                                                   \
-        int n = 0;                                                                                              \
-        ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mlp_chain_kernel<SA_, SB_, NPA_>, kThreads, 0) == \
-                 hipSuccess && n >= 1;                                                                          \
+        int n = 0, nd = 0;                                                                                      \
+        ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mlp_chain_kernel<SA_, SB_, NPA_, false>, kThreads, \
+                                                          0) == hipSuccess && n >= 1 &&                         \
+             hipOccupancyMaxActiveBlocksPerMultiprocessor(&nd, mlp_chain_kernel<SA_, SB_, NPA_, true>, kThreads, \
+                                                          0) == hipSuccess && nd >= 1;                          \
     }
         VLA_CHAIN_CONFIGS(VLA_CASE)
 #undef VLA_CASE

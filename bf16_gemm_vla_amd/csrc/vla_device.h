@@ -174,4 +174,24 @@ __device__ __forceinline__ float gelu_mul(float g, float u) {
     return ldexpf(mg * mu * exp2f(t - ti), eg + eu + static_cast<int>(ti));
 }
 
+// bf16 bits -> fp64 (exact).
+__device__ __forceinline__ double bf16_f64(uint32_t bits16) { return static_cast<double>(__uint_as_float(bits16 << 16)); }
+
+// Nearest-even bf16 of an fp64 value with one rounding: truncate to fp32,
+// set the lowest bit if that was inexact (round to odd keeps the 29 dropped
+// bits' information in a sticky bit), then round the fp32 bits to bf16.
+__device__ __forceinline__ uint32_t f64_to_bf16(double v) {
+    const float t = __double2float_rz(v);
+    uint32_t b = __float_as_uint(t);
+    if (static_cast<double>(t) != v) b |= 1u;
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return b >> 16;
+}
+
+// Gated residual of the decoder boundary for one value: bf16(x + y * g),
+// the product and sum exact in fp64 (bf16 significands) and rounded once.
+__device__ __forceinline__ uint32_t gated_residual_bf16(uint32_t x16, uint32_t y16, uint32_t g16) {
+    return f64_to_bf16(bf16_f64(x16) + bf16_f64(y16) * bf16_f64(g16));
+}
+
 }  // namespace vla

@@ -124,6 +124,16 @@ struct ChainLaunch {
     int64_t xstride;
     int L;
     int64_t M, H, I;
+    // decoder-block chain (style != nullptr): the boundary closes every layer
+    const uint16_t* const* style = nullptr;   // host array of L device pointers
+    int style_per_row = 0;
+    float eps = 0.0f;
+    const uint16_t* h_in = nullptr;
+    const uint16_t* g_in = nullptr;
+    uint16_t* h_out = nullptr;
+    uint16_t* g_out = nullptr;
+    uint16_t* hbuf = nullptr;                 // nullable per-layer stage output
+    double* sspart = nullptr;                 // L x M x H/16 partial sums of squares
 };
 // Whether a compiled fused configuration covers (M, H, I, L); npa receives
 // the gate/up pairs per workgroup.

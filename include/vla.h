@@ -435,8 +435,16 @@ int vla_mlp_chain_destroy(vla_mlp_chain *chain);
  *   act       = gelu_mul(h @ [Wgate_l; Wup_l]^T)    (vla_gemm_fp8w_gelu_mul)
  *   d         = bf16(act @ Wdown_l^T)               (vla_gemm_fp8w)
  *   (x, h, g) = vla_gate_residual_ada_norm(x, d, g, style_l, eps)
- * three kernels per layer, recorded once as a HIP graph like the gated-MLP
- * chain.  The final x, h and g are the outputs.
+ * The final x, h and g are the outputs.  Where
+ * vla_decoder_chain_fused_supported says so and the scratch and stage
+ * buffers are 256-byte aligned, the chain is one persistent launch: the gated
+ * residual is formed in the down-projection's epilogue together with each
+ * 16-column tile's partial sum of squares of the new residual, and the next
+ * layer normalizes its staged input rows from those partials (fp32 after the
+ * fp64 sum; 1/rms in fp64), so the layers meet only at the chain's own
+ * phase barriers.  Otherwise three kernels per layer are recorded once as a
+ * HIP graph like the gated-MLP chain's.  The residual is bit-exact on both
+ * paths; h agrees with the fp64 boundary within one bf16 ulp.
  *   wgu, sgu, wd, sd  as for the gated-MLP chain.
  *   style        host array of L device pointers: bf16 (style_per_row ? M : 1)
  *                x 3H, [scale | shift | next gate] (see the boundary).
@@ -452,12 +460,39 @@ int vla_mlp_chain_destroy(vla_mlp_chain *chain);
  * vla_mlp_chain_replay / vla_mlp_chain_destroy. */
 size_t vla_decoder_chain_scratch_bytes(int64_t M, int64_t H, int64_t I);
 
+/* 1 if the decoder-block chain of this shape runs as one persistent launch
+ * on the current device (given 256-byte aligned scratch and stage
+ * buffers), 0 if it takes the graph of launches: the gated-MLP chain's
+ * conditions (vla_mlp_chain_fused_supported), H <= 1024, and with a style
+ * row per activation row (style_per_row != 0) M <= 16, beyond which the
+ * graph of launches measured faster.  Never fails. */
+int vla_decoder_chain_fused_supported(int64_t M, int64_t H, int64_t I, int L, int style_per_row);
+
 int vla_decoder_chain_enqueue(const uint8_t *const *wgu, const float *const *sgu,
                               const uint8_t *const *wd, const float *const *sd,
                               const uint16_t *const *style, int style_per_row, float eps,
                               const uint16_t *x_in, const uint16_t *h_in, const uint16_t *gate_in,
                               uint16_t *x_out, uint16_t *h_out, uint16_t *gate_out, void *scratch,
                               size_t scratch_bytes, int L, int64_t M, int64_t H, int64_t I, void *stream);
+
+/* vla_decoder_chain_enqueue, keeping every stage of every layer (for parity
+ * checks): each of these may be NULL; non-NULL ones are device bf16, 16-byte
+ * aligned, and must not overlap each other, an input, an output, a style
+ * array or the scratch (VLA_EINVAL):
+ *   gu_out    L x M x 2I  [g | u] of the merged gate/up GEMM, layer after layer;
+ *   act_out   L x M x I   GELU(g) * u;
+ *   down_out  L x M x H   the down-projection d (before the boundary);
+ *   x_layers  L x M x H   the residual x after each layer;
+ *   h_layers  L x M x H   the normalized h after each layer.
+ * x_out, h_out and gate_out are written as by vla_decoder_chain_enqueue. */
+int vla_decoder_chain_enqueue_staged(const uint8_t *const *wgu, const float *const *sgu,
+                                     const uint8_t *const *wd, const float *const *sd,
+                                     const uint16_t *const *style, int style_per_row, float eps,
+                                     const uint16_t *x_in, const uint16_t *h_in, const uint16_t *gate_in,
+                                     uint16_t *x_out, uint16_t *h_out, uint16_t *gate_out, uint16_t *gu_out,
+                                     uint16_t *act_out, uint16_t *down_out, uint16_t *x_layers, uint16_t *h_layers,
+                                     void *scratch, size_t scratch_bytes, int L, int64_t M, int64_t H, int64_t I,
+                                     void *stream);
 
 int vla_decoder_chain_create(const uint8_t *const *wgu, const float *const *sgu,
                              const uint8_t *const *wd, const float *const *sd,
