@@ -703,11 +703,16 @@ def mfma_trace_summary(trace_dir, blocks=512, reps=5):
 def mfma_rates(vla, torch, dev, blocks=512, reps=5):
     """Issue rate of each matrix instruction the GEMMs use, on zero operands
     and on operands like the GEMMs' own (vla_probe_mfma_rate; two workgroups of
-    four waves per CU, two waves per SIMD as in the wide kernel).  The rate
-    depends on the data, so the wide GEMMs' fractions are read against the
-    'normal' figures as well as against the published peaks."""
+    four waves per CU, two waves per SIMD as in the wide kernel), with the
+    shader clock each loop ran at.  The rate depends on the data through the
+    clock (busy non-zero operands draw more power and the chip clocks down),
+    so the wide GEMMs' fractions are read against the 'normal' figures as
+    well as against the published peaks."""
+    import numpy as np
+
     res = {}
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
     for name, form, mnk, dt, peak in MFMA_FORMS:
         per_iter = blocks * 4 * 4 * 2.0 * mnk           # workgroups x waves x chains x flops
         iters = mfma_iters(mnk, blocks)
@@ -715,18 +720,25 @@ def mfma_rates(vla, torch, dev, blocks=512, reps=5):
         for kind in ("zero", "normal"):
             ops = mfma_operands(torch, dev, kind, dt)
             vla.vla_probe_mfma_rate(form, ops, iters, out, blocks)
-            ts = []
+            ts, ghz = [], []
             for _ in range(reps):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                vla.vla_probe_mfma_rate(form, ops, iters, out, blocks)
+                vla.vla_probe_mfma_rate(form, ops, iters, out, blocks, clocks=clocks)
                 e1.record()
                 torch.cuda.synchronize()
                 ts.append(e0.elapsed_time(e1))
+                c = clocks.cpu().numpy().astype(np.float64)
+                ghz.append(float(np.median(c[0::2] / (c[1::2] * 10.0))))
             ms = sorted(ts)[len(ts) // 2]
             tf = per_iter * iters / (ms * 1e-3) / 1e12
+            clk = sorted(ghz)[len(ghz) // 2]
             r[kind] = round(tf, 1)
             r[kind + "_frac_of_peak"] = round(tf / peak, 4)
+            # the shader clock the loop ran at (the published peak assumes
+            # 2.4 GHz) and the rate per clock against the peak's
+            r[kind + "_clock_GHz"] = round(clk, 3)
+            r[kind + "_frac_of_peak_per_clock"] = round(tf / (peak * clk / 2.4), 4)
         res[name] = r
     return res
 

@@ -52,7 +52,7 @@ SIGNATURES = {
     "vla_quantize_act": (INT, [P, P, P, P, SZ, I64, I64, P]),
     "vla_quantize_act_static": (INT, [P, P, P, I64, I64, P]),
     "vla_probe_stream_read": (INT, [P, SZ, P, INT, P]),
-    "vla_probe_mfma_rate": (INT, [INT, P, INT, P, INT, P]),
+    "vla_probe_mfma_rate": (INT, [INT, P, INT, P, P, INT, P]),
     "vla_gate_residual_ada_norm": (INT, [P, P, P, P, INT, ctypes.c_float, P, P, P, I64, I64, P]),
     "vla_gemm_workspace_bytes": (SZ, [I64, I64, I64, INT]),
     "vla_gemm_supported": (INT, [I64, I64, I64, INT, INT, INT]),
@@ -219,8 +219,8 @@ def vla_probe_stream_read(src, nbytes, sink, blocks, stream=None):
 VLA_MFMA_BF16_32X32X16, VLA_MFMA_BF16_16X16X32, VLA_MFMA_FP8_32X32X64, VLA_MFMA_FP8_16X16X128 = 0, 1, 2, 3
 
 
-def vla_probe_mfma_rate(form, operands, iters, out, blocks, stream=None):
-    _check(load().vla_probe_mfma_rate(form, _ptr(operands), iters, _ptr(out), blocks, _stream(stream)),
+def vla_probe_mfma_rate(form, operands, iters, out, blocks, stream=None, clocks=None):
+    _check(load().vla_probe_mfma_rate(form, _ptr(operands), iters, _ptr(out), _ptr(clocks), blocks, _stream(stream)),
            "vla_probe_mfma_rate")
 
 

@@ -620,15 +620,17 @@ int vla_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, int blo
     return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
 }
 
-int vla_probe_mfma_rate(int form, const uint32_t* operands, int iters, float* out, int blocks, void* stream) {
+int vla_probe_mfma_rate(int form, const uint32_t* operands, int iters, float* out, uint64_t* clocks, int blocks,
+                        void* stream) {
     const char* fn = "vla_probe_mfma_rate";
     REQUIRE_PTR(operands);
     REQUIRE_PTR(out);
+    if (clocks && (reinterpret_cast<uintptr_t>(clocks) & 7u)) return fail(VLA_EALIGN, fn, "clocks is not 8-byte aligned");
     if (form < VLA_MFMA_BF16_32X32X16 || form > VLA_MFMA_FP8_16X16X128)
         return fail(VLA_EINVAL, fn, "form=%d is not a VLA_MFMA_* value", form);
     if (iters <= 0 || iters > (1 << 24)) return fail(VLA_EINVAL, fn, "iters=%d outside 1..2^24", iters);
     if (blocks <= 0 || blocks > 65536) return fail(VLA_EINVAL, fn, "blocks=%d outside 1..65536", blocks);
-    hipError_t e = vla::launch_mfma_rate(form, operands, iters, out, blocks, static_cast<hipStream_t>(stream));
+    hipError_t e = vla::launch_mfma_rate(form, operands, iters, out, clocks, blocks, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? VLA_OK : hip_fail(fn, "kernel launch", e);
 }
 

@@ -114,7 +114,7 @@ struct RateForm<VLA_MFMA_FP8_16X16X128> {
 
 template <int FORM>
 __global__ __launch_bounds__(kRateThreads) void mfma_rate_kernel(const uint32_t* __restrict__ src, int iters,
-                                                                 float* __restrict__ out) {
+                                                                 float* __restrict__ out, uint64_t* __restrict__ clocks) {
     typedef typename RateForm<FORM>::Acc Acc;
     uint32_t ops[kRateWordsPerLane];
     const uint32_t* p = src + threadIdx.x * kRateWordsPerLane;
@@ -125,6 +125,9 @@ __global__ __launch_bounds__(kRateThreads) void mfma_rate_kernel(const uint32_t*
     Acc c0{}, c1{}, c2{}, c3{};
     static_assert(kRateChains == 4, "four chains");
     asm volatile("" : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3));
+    // shader-clock cycles and 100 MHz real-time ticks around the loop: their
+    // ratio is the clock the instructions ran at
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
         c0 = RateForm<FORM>::step(ops + 0, ops + 8, c0);
         c1 = RateForm<FORM>::step(ops + 16, ops + 24, c1);
@@ -132,6 +135,11 @@ __global__ __launch_bounds__(kRateThreads) void mfma_rate_kernel(const uint32_t*
         c3 = RateForm<FORM>::step(ops + 48, ops + 56, c3);
         // pins each chain to its own registers across iterations (no code)
         asm volatile("" : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3));
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (clocks && threadIdx.x == 0) {
+        clocks[2 * blockIdx.x] = t1 - t0;
+        clocks[2 * blockIdx.x + 1] = r1 - r0;
     }
     float s = 0.0f;
 #pragma unroll
@@ -147,19 +155,20 @@ __global__ __launch_bounds__(kRateThreads) void mfma_rate_kernel(const uint32_t*
 
 }  // namespace
 
-hipError_t launch_mfma_rate(int form, const uint32_t* src, int iters, float* out, int blocks, hipStream_t s) {
+hipError_t launch_mfma_rate(int form, const uint32_t* src, int iters, float* out, uint64_t* clocks, int blocks,
+                            hipStream_t s) {
     switch (form) {
         case VLA_MFMA_BF16_32X32X16:
-            mfma_rate_kernel<VLA_MFMA_BF16_32X32X16><<<blocks, kRateThreads, 0, s>>>(src, iters, out);
+            mfma_rate_kernel<VLA_MFMA_BF16_32X32X16><<<blocks, kRateThreads, 0, s>>>(src, iters, out, clocks);
             break;
         case VLA_MFMA_BF16_16X16X32:
-            mfma_rate_kernel<VLA_MFMA_BF16_16X16X32><<<blocks, kRateThreads, 0, s>>>(src, iters, out);
+            mfma_rate_kernel<VLA_MFMA_BF16_16X16X32><<<blocks, kRateThreads, 0, s>>>(src, iters, out, clocks);
             break;
         case VLA_MFMA_FP8_32X32X64:
-            mfma_rate_kernel<VLA_MFMA_FP8_32X32X64><<<blocks, kRateThreads, 0, s>>>(src, iters, out);
+            mfma_rate_kernel<VLA_MFMA_FP8_32X32X64><<<blocks, kRateThreads, 0, s>>>(src, iters, out, clocks);
             break;
         default:
-            mfma_rate_kernel<VLA_MFMA_FP8_16X16X128><<<blocks, kRateThreads, 0, s>>>(src, iters, out);
+            mfma_rate_kernel<VLA_MFMA_FP8_16X16X128><<<blocks, kRateThreads, 0, s>>>(src, iters, out, clocks);
             break;
     }
     return hipGetLastError();

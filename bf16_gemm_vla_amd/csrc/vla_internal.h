@@ -28,7 +28,8 @@ hipError_t launch_gate_residual_ada_norm(const uint16_t* resid, const uint16_t* 
                                          uint16_t* h_out, uint16_t* ng_out, int64_t M, int64_t D, hipStream_t s);
 bool boundary_width_ok(int64_t D);   // D a positive multiple of 4, at most 8192
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
-hipError_t launch_mfma_rate(int form, const uint32_t* src, int iters, float* out, int blocks, hipStream_t s);
+hipError_t launch_mfma_rate(int form, const uint32_t* src, int iters, float* out, uint64_t* clocks, int blocks,
+                            hipStream_t s);
 hipError_t launch_quantize_act_static(const uint16_t* A, const float* s_a, uint8_t* qa, int64_t M, int64_t K,
                                       hipStream_t s);
 

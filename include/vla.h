@@ -220,6 +220,12 @@ int vla_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blo
  *   out       device float[blocks * 256], 16-byte aligned: lane t of
  *             workgroup b writes the sum of its four accumulators at
  *             b*256 + t (accumulators start at zero);
+ *   clocks    NULL, or device uint64[2 * blocks], 8-byte aligned
+ *             (VLA_EALIGN): workgroup b's first wave writes the shader-clock
+ *             cycles (s_memtime) and the 100 MHz real-time ticks
+ *             (s_memrealtime) its instruction loop took at 2b and 2b + 1;
+ *             cycles / (ticks * 10 ns) is the clock the loop ran at, which
+ *             falls under the chip's power limit on busy, non-zero operands;
  *   blocks    1 .. 65536, else VLA_EINVAL.
  * One launch does blocks * 4 * iters * 4 instructions, each of
  * 2*m*n*k floating-point operations for its m x n x k form. */
@@ -227,7 +233,8 @@ int vla_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blo
 #define VLA_MFMA_BF16_16X16X32 1  /* v_mfma_f32_16x16x32_bf16 (skinny GEMM, gated-MLP chain) */
 #define VLA_MFMA_FP8_32X32X64 2   /* v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3 (wide GEMM, FP8 x FP8) */
 #define VLA_MFMA_FP8_16X16X128 3  /* v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x E4M3 */
-int vla_probe_mfma_rate(int form, const uint32_t *operands, int iters, float *out, int blocks, void *stream);
+int vla_probe_mfma_rate(int form, const uint32_t *operands, int iters, float *out, uint64_t *clocks, int blocks,
+                        void *stream);
 
 /* ------------------------------------------------------------------ GEMM */
 

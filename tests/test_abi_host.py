@@ -113,9 +113,10 @@ def test_codec_errors(lib):
     assert rc_of("vla_probe_stream_read", A16 + 8, 1 << 22, A16, 256, None) == vla.VLA_EALIGN
     assert rc_of("vla_probe_stream_read", None, 1 << 22, A16, 256, None) == vla.VLA_EINVAL
     for form, iters, blocks in ((4, 1, 1), (-1, 1, 1), (0, 0, 1), (0, 1, 0), (0, (1 << 24) + 1, 1), (3, 1, 65537)):
-        assert rc_of("vla_probe_mfma_rate", form, A16, iters, A16, blocks, None) == vla.VLA_EINVAL
-    assert rc_of("vla_probe_mfma_rate", 0, A16 + 4, 1, A16, 1, None) == vla.VLA_EALIGN
-    assert rc_of("vla_probe_mfma_rate", 0, A16, 1, None, 1, None) == vla.VLA_EINVAL
+        assert rc_of("vla_probe_mfma_rate", form, A16, iters, A16, None, blocks, None) == vla.VLA_EINVAL
+    assert rc_of("vla_probe_mfma_rate", 0, A16 + 4, 1, A16, None, 1, None) == vla.VLA_EALIGN
+    assert rc_of("vla_probe_mfma_rate", 0, A16, 1, A16, A16 + 4, 1, None) == vla.VLA_EALIGN
+    assert rc_of("vla_probe_mfma_rate", 0, A16, 1, None, None, 1, None) == vla.VLA_EINVAL
     assert rc_of("vla_quantize_act_static", A16, A16 + 4, A16, 50, 1024, None) == vla.VLA_EALIGN
     assert rc_of("vla_quantize_act_static", A16, A16, A16, 50, 1000, None) == vla.VLA_ESHAPE
     assert rc_of("vla_quantize_act_static", A16, A16, A16, 0, 1024, None) == vla.VLA_EINVAL

@@ -48,3 +48,28 @@ def test_mfma_rate_probe_counts(name, form, mnk, dt):
     per_lane = iters * (m * n // 64) * k * (1 + 2 + 4 + 8)
     assert np.all(got == per_lane), name
 
+
+
+def test_mfma_rate_probe_clocks():
+    """The optional clock output: one (cycles, 100 MHz ticks) pair per
+    workgroup, nothing written past them, and a plausible shader clock."""
+    words = np.zeros((256, 64), dtype=np.uint32)
+    for j in range(4):
+        words[:, 16 * j:16 * j + 8] = power_of_two_word(0, "bf16")
+        words[:, 16 * j + 8:16 * j + 16] = power_of_two_word(j, "bf16")
+    ops = torch.from_numpy(words.view(np.int32)).cuda()
+    blocks, iters = 8, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.full((2 * blocks + 2,), -7, dtype=torch.int64, device="cuda")
+    vla.vla_probe_mfma_rate(vla.VLA_MFMA_BF16_32X32X16, ops, iters, out, blocks, clocks=clocks)
+    torch.cuda.synchronize()
+    c = clocks.cpu().numpy()
+    assert np.all(c[2 * blocks:] == -7)
+    cycles, ticks = c[0:2 * blocks:2].astype(np.float64), c[1:2 * blocks:2].astype(np.float64)
+    # four chains of 32-cycle instructions, one wave per SIMD: at least the
+    # instructions' own cycles
+    assert np.all(cycles >= iters * 4 * 32), cycles
+    assert np.all(ticks > 0)
+    ghz = cycles / (ticks * 10.0)
+    assert np.all((ghz > 0.5) & (ghz < 3.0)), ghz
+    assert np.all(out.cpu().numpy() == iters * (32 * 32 // 64) * 16 * 15)
