@@ -154,6 +154,20 @@ def test_decoder_chain_stagewise(M, per_row):
     vla.vla_workspace_status(dec.scratch)
 
 
+@pytest.mark.parametrize("M,per_row", [(10, True), (24, False), (64, False)])
+def test_decoder_chain_full_width_fused_stagewise(M, per_row):
+    """The single launch at the decoder's own widths (H = 1024, I = 4096),
+    three layers, one configuration per row-tile count class (one, two and
+    four gate/up pairs per workgroup): every stage against the oracle, and
+    the plain launch equal to the staged one bit for bit."""
+    dec = Decoder(3, M, 1024, 4096, per_row=per_row, seed=40 + M)
+    assert dec.fused()
+    outs, st = dec.staged()
+    assert check_staged(dec, outs, st, f"fused full width M={M} per_row={per_row}") == dec.L
+    assert all(np.array_equal(a, b) for a, b in zip(outs, dec.eager()))
+    vla.vla_workspace_status(dec.scratch)
+
+
 @pytest.mark.parametrize("per_row", [True, False])
 def test_decoder_chain_small_layerwise(per_row):
     """The graph of launches (unaligned scratch) equals the layers run one
