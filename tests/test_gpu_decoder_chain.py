@@ -232,3 +232,41 @@ def test_decoder_chain_config_replay_purity_and_layers(graph_path):
     for name, a, b in (("x", ref[0], e2e[0]), ("h", ref[1], e2e[1])):
         print(f"end to end {name}: cosine={close(a, b):.7f} (reported)", flush=True)
     vla.vla_workspace_status(dec.scratch)
+
+
+@pytest.mark.parametrize("L", [1, 32, 33])
+def test_decoder_chain_layer_count_limit(L):
+    """One layer (the single launch's last-layer path only), 32 (the most
+    the single launch takes) and 33 (the graph of launches), 10 rows with a
+    style row per row, H = 256, I = 512: every stage against the oracle."""
+    dec = Decoder(L, 10, 256, 512, per_row=True, seed=60 + L)
+    assert dec.fused() == (L <= 32)
+    outs, st = dec.staged()
+    checked = check_staged(dec, outs, st, f"L={L}")
+    assert checked == L
+    assert all(np.array_equal(a, b) for a, b in zip(outs, dec.eager()))
+    vla.vla_workspace_status(dec.scratch)
+
+
+def test_fused_decoder_chain_barrier_wait_is_bounded():
+    """With the wait bound forced down to one poll the single launch's
+    barriers give up: the launch completes, x_out and h_out read NaN, the
+    status query names the cause, and the same scratch then gives the
+    correct chain again."""
+    dec = Decoder(3, 50, 1024, 4096, per_row=False, seed=9)
+    assert dec.fused()
+    vla.vla_set_wait_limit(1)
+    try:
+        for _ in range(3):
+            vla.vla_decoder_chain_enqueue(*dec.args())
+        torch.cuda.synchronize()
+    finally:
+        vla.vla_set_wait_limit(0)
+    x_out, h_out, _ = (host(o).view(np.uint16) for o in dec.d_out)
+    assert np.isnan(bf16_f64(x_out)).any() and np.isnan(bf16_f64(h_out)).any()
+    with pytest.raises(RuntimeError, match="fused chain phase barrier"):
+        vla.vla_workspace_status(dec.scratch)
+    outs, st = dec.staged()
+    assert check_staged(dec, outs, st, "after give-up") == dec.L
+    assert all(np.array_equal(a, b) for a, b in zip(outs, dec.eager()))
+    vla.vla_workspace_status(dec.scratch)
