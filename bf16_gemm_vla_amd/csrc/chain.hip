@@ -40,6 +40,16 @@
 // up sets the abort word, which releases every other waiter; all
 // workgroups then write NaN over their slice of the output, the cause goes
 // to the workspace's status word, and every workgroup exits normally.
+//
+// Decoder-block chain (DEC): the same phases with the decoder boundary
+// ("Fusing the BF16 decoder boundary") split over them.  Phase B's epilogue
+// forms the gated residual x_l+1 = bf16(x_l + d * g) exactly in fp64 and
+// stores, per row and 16-column tile, the fp64 sum of squares of its new
+// values; phase A of the next layer stages x_l+1 with the previous layer's
+// scale and shift rows and the tile's partial sums, forms 1/rms per row
+// and normalizes the staged rows in place before its MFMAs read them.  The
+// first layer reads the given h; after the last, one more barrier lets the
+// phase-B workgroups write h_out and the next gate for their tiles.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -321,14 +331,13 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
                                                      kCpolSC1);
         }
     };
-    // 1/rms of each staged row from its partials in LDS (src): lane rr sums
-    // row rr's G partials in column order (no cross-lane steps: a chain of
-    // shuffles per row would cost a round trip through the LDS crossbar per
-    // step); fp64 values at LDS offset dst.
+    // 1/rms of each staged row from its partials in LDS (src, rows SSR
+    // apart), as fp64 values at LDS offset dst: lane 4 rr + k sums quarter k
+    // of row rr's G partials in column order, then lane rr adds the four
+    // quarters in order (a fixed order: bitwise repeatable).  The quarters
+    // pass through LDS at dst + 128, read back by the same wave; fp64
+    // shuffles would each cost a round trip through the LDS crossbar.
     auto row_inv = [&](int src, int dst) __attribute__((always_inline)) {
-        // lane 4 rr + k sums quarter k of row rr's partials, then lane rr
-        // adds the four quarters in order (through LDS: the quarters go to
-        // dst + 128, read back by the same wave)
         constexpr int GQ = G / 4;
         const int rr = lane >> 2, k = lane & 3;
         double part = 0.0;
