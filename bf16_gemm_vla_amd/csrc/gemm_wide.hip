@@ -393,9 +393,19 @@ void wide_gemm_kernel(KArgs a) {
     //      out first, interleaved with the first half of the MFMAs, and the
     //      next step's weight conversions fill the gaps of the second half.
     //      The stage's last step issues half of its MFMAs before the barrier,
-    //      so the matrix pipe is busy while the waves meet.  MFMA blocks run
-    //      at raised wave priority, so a wave with MFMAs ready issues ahead of
-    //      its SIMD partner's memory work.
+    //      so the matrix pipe is busy while the waves meet.  With bf16
+    //      activations on 128-column tiles the MFMA blocks run at raised
+    //      wave priority, so a wave with MFMAs ready issues ahead of its SIMD
+    //      partner's memory work; the other tilings measured faster without
+    //      (M = 768 and 571, alternating runs: FP8 x FP8 1-4%, W8A16 on
+    //      256-column tiles 2%, while W8A16 on 128-column tiles lost 2%).
+    constexpr bool PRIO = AT == AType::BF16 && BN == 128;
+    auto prio_on = [&]() __attribute__((always_inline)) {
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+    };
+    auto prio_off = [&]() __attribute__((always_inline)) {
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+    };
     constexpr int NM = C::NSUB * C::MSUB;        // MFMAs per step
     constexpr int HALF = NM / 2;
     F f0, f1;
@@ -410,9 +420,9 @@ void wide_gemm_kernel(KArgs a) {
             if (ks + 1 < C::NKS) {
                 __builtin_amdgcn_sched_barrier(0);
                 read_step(cur, ks + 1, of);
-                __builtin_amdgcn_s_setprio(1);
+                prio_on();
                 mfmas(cf, 0, NM);
-                __builtin_amdgcn_s_setprio(0);
+                prio_off();
                 convert(of, UC, kt_begin + i, ks + 1);
 #pragma unroll
                 for (int j = 0; j < HALF; ++j) {
@@ -427,9 +437,9 @@ void wide_gemm_kernel(KArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_setprio(1);
+                prio_on();
                 mfmas(cf, 0, HALF);
-                __builtin_amdgcn_s_setprio(0);
+                prio_off();
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 3) * C::LV));
                 __builtin_amdgcn_s_barrier();
@@ -437,9 +447,9 @@ void wide_gemm_kernel(KArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
                 read_step(bufs[(u + 1) % S], 0, of);
                 issue(std::integral_constant<int, (u + S - 1) % S>{}, kt_begin + i + S - 1, i + S - 1 < nkt);
-                __builtin_amdgcn_s_setprio(1);
+                prio_on();
                 mfmas(cf, HALF, NM);
-                __builtin_amdgcn_s_setprio(0);
+                prio_off();
                 convert(of, std::integral_constant<int, (u + 1) % S>{}, kt_begin + i + 1, 0);
 #pragma unroll
                 for (int j = HALF; j < NM; ++j) {
