@@ -191,6 +191,32 @@ def test_decoder_chain_errors(lib):
                  M, H, I, None, ctypes.byref(out)) == vla.VLA_EINVAL
 
 
+def test_decoder_chain_staged_errors(lib):
+    """The staged decoder chain's own checks (every case fails before any
+    device work): stage outputs that overlap one another, an input, an
+    output, the scratch or a style array, and unaligned stage outputs."""
+    arr = (ctypes.c_void_p * 2)(A16, A16)
+    M, H, I, L = 50, 1024, 4096, 2
+    need = vla.vla_decoder_chain_scratch_bytes(M, H, I)
+    mat = M * H * 2
+    XI, HI, GI = 1 << 33, (1 << 33) + mat, (1 << 33) + 2 * mat
+    XO, HO, GO = 1 << 34, (1 << 34) + mat, (1 << 34) + 2 * mat
+    SC = 1 << 35
+    GU, ACT, DN, XL, HL = (1 << 36), (1 << 36) + (1 << 30), (1 << 36) + (2 << 30), (1 << 36) + (3 << 30), (1 << 36) + (4 << 30)
+
+    def rc(gu=GU, act=ACT, dn=DN, xl=XL, hl=HL, style=arr):
+        return rc_of("vla_decoder_chain_enqueue_staged", arr, arr, arr, arr, style, 1, 1e-6, XI, HI, GI, XO, HO, GO,
+                     gu, act, dn, xl, hl, SC, need, L, M, H, I, None)
+    assert rc(act=GU + 64) == vla.VLA_EINVAL                    # two stage outputs overlap
+    assert rc(hl=XL + L * mat - 16) == vla.VLA_EINVAL           # h stages run into the x stages
+    assert rc(dn=XI + 16) == vla.VLA_EINVAL                     # over an input
+    assert rc(xl=HO) == vla.VLA_EINVAL                          # over an output
+    assert rc(gu=SC + 4096) == vla.VLA_EINVAL                   # inside the scratch
+    assert rc(style=(ctypes.c_void_p * 2)(A16, HL + 512)) == vla.VLA_EINVAL    # a style array inside the h stages
+    assert rc(act=ACT + 8) == vla.VLA_EALIGN
+    assert rc(hl=HL + 4) == vla.VLA_EALIGN
+
+
 def test_chain_errors(lib):
     arr = (ctypes.c_void_p * 2)(A16, A16)
     need = vla.vla_mlp_chain_scratch_bytes(50, 1024, 4096)
