@@ -314,6 +314,17 @@ def main():
     # a call's time against the best time of a launch that only streams its
     # 4 MiB of weights (same cold rotation): the share of the single-call floor reached
     extra["read_floor_over_call"] = round(read_us[best_blocks] / (0.5 * (extra["up_us"] + extra["down_us"])), 3)
+    if not args.no_extra:
+        # one GPU's share of the up-projection split by output columns over
+        # eight GPUs (no exchange): N/8 channels, a prefix of the packed
+        # weights and scales, same cold rotation
+        UPS = (M, I // 8, H)
+        ws_s = torch.zeros(vla.vla_gemm_workspace_bytes(*UPS, 1), dtype=torch.uint8, device=dev)
+
+        def up_shard(i):
+            vla.vla_gemm_fp8w(A_up, None, qs_up[i % copies], s_up, None, None, Y_up, ws_s, ws_s.numel(), *UPS)
+        ms = time_graph(up_shard, args.steps)
+        extra["up_shard8_us"] = round(ms * 1000.0 / args.steps, 3)
 
     if not args.no_extra:
         # MXFP4 weights (E2M1 + an E8M0 scale per 32 values: 0.53 of the FP8
@@ -480,6 +491,18 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
                 out[f"{name}_{tag}_frac_of_mfma_rate"] = round(tf / rate, 4)
             ms = time_graph(actq, 20)
             out[f"{name}_act_quant_us"] = round(ms * 1000.0 / 20, 2)
+            if Mw == 768 and name.endswith("_up"):
+                # one GPU's share when the encoder up-projection is split by
+                # output columns over eight GPUs: N/8 channels, W8A16
+                n8 = n // 8
+                wss = torch.zeros(vla.vla_gemm_workspace_bytes(Mw, n8, k, 1), dtype=torch.uint8, device=dev)
+
+                def w8a16_shard(i):
+                    vla.vla_gemm_fp8w(A, None, q, s, None, None, Y, wss, wss.numel(), Mw, n8, k)
+                ms = time_graph(w8a16_shard, 20)
+                us = ms * 1000.0 / 20
+                out[f"{name}_w8a16_shard8_us"] = round(us, 2)
+                out[f"{name}_w8a16_shard8_frac"] = round(2.0 * Mw * n8 * k / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
 
             def actq_static(i):   # frozen scale (the one just calibrated): one pass, no absmax
                 vla.vla_quantize_act_static(A, sa, qa, Mw, k)
