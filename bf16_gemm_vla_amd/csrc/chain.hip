@@ -364,6 +364,35 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
     auto normalize = [&](int lp) __attribute__((always_inline)) {
         (void)lp;
         constexpr int C8 = H / 8;                                   // 16-byte chunks per row
+        if (!a.style_per_row) {
+            // one style row: each compute-wave thread takes one 8-column
+            // chunk and the rows 512 / C8 apart, converting the chunk's
+            // 1 + scale and shift once (the same fp32 values norm1 forms)
+            static_assert((kCW * 64) % C8 == 0, "whole rows per pass of the compute waves");
+            if (wave < kCW) {
+                const int k8 = tid % C8;
+                const u32x4_t sc = *reinterpret_cast<const u32x4_t*>(lds + STY_A + k8 * 16);
+                const u32x4_t sh = *reinterpret_cast<const u32x4_t*>(lds + STY_A + 2 * H + k8 * 16);
+                float sa[8], sb[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sa[2 * i] = 1.0f + bf16_to_f32(lo16(sc[i]));
+                    sa[2 * i + 1] = 1.0f + bf16_to_f32(hi16(sc[i]));
+                    sb[2 * i] = bf16_to_f32(lo16(sh[i]));
+                    sb[2 * i + 1] = bf16_to_f32(hi16(sh[i]));
+                }
+                for (int row = tid / C8; row < mrows; row += kCW * 64 / C8) {
+                    u32x4_t rv = *reinterpret_cast<const u32x4_t*>(lds + row * RSA + k8 * 16);
+                    const float inv = static_cast<float>(*reinterpret_cast<const double*>(lds + INV_A + row * 8));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        rv[i] = f32x2_to_bf16x2(bf16_to_f32(lo16(rv[i])) * inv * sa[2 * i] + sb[2 * i],
+                                                bf16_to_f32(hi16(rv[i])) * inv * sa[2 * i + 1] + sb[2 * i + 1]);
+                    *reinterpret_cast<u32x4_t*>(lds + row * RSA + k8 * 16) = rv;
+                }
+            }
+            return;
+        }
         for (int c = tid; wave <= kCW && c < mrows * C8; c += (kCW + 1) * 64) {
             const int row = c / C8, k8 = c % C8;
             const int srow = a.style_per_row ? row : 0;
