@@ -430,6 +430,26 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
     else clear_wa();
     bool ok = true;
     int b = 0;
+    // Request a phase's weights (compute waves; the others clear theirs) and
+    // leave this wave's earlier stores complete: NL is the number of loads
+    // `load` issues.
+    auto prefetch_then_wait = [&](auto load, auto clear, auto NL) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DEC) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __builtin_amdgcn_sched_barrier(0);
+            if (compute) load();
+            else clear();
+        } else if (compute) {
+            load();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(NL)::value));
+        } else {
+            clear();
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
     for (int l = 0; l < a.L; ++l) {
         const uint16_t* xl = xl_ptr(l);
         uint16_t* act = a.actbuf + static_cast<int64_t>(l) * a.M * I;
@@ -506,14 +526,13 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
                 }
             }
         }
-        // this wave's stores complete (acknowledged before any weight load is
-        // queued behind them), then phase B's weights are requested: they
-        // stream in during the barrier and the staging of act
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_sched_barrier(0);
-        if (compute) load_wb(l);
-        else clear_wb();
-        __builtin_amdgcn_sched_barrier(0);
+        // phase B's weights are requested before the barrier (they stream
+        // in during it and the staging of act), and this wave's stores are
+        // complete before the arrival.  Gated-MLP chain: the loads go out
+        // right behind the stores and the wait leaves only them outstanding
+        // (vmcnt retires in order); decoder chain: the stores complete
+        // first (measured faster there)
+        prefetch_then_wait([&] { load_wb(l); }, [&] { clear_wb(); }, std::integral_constant<int, SB>{});
         ok = group_barrier(b++);
         if (!ok) break;
         // ---------------- phase B: down GEMM + residual
@@ -541,7 +560,16 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
             red_b[wave][lane] = acc2[0] + acc2[1];
         }
         lds_barrier();
-        if (wave == 0 && vb && mrow < mrows) {
+        // the tile's rows split over EPW waves (the 4 lanes of a row stay in
+        // one wave), each summing the waves' partials in wave order: the
+        // gated-MLP chain uses all compute waves, two rows each, so every
+        // wave's few stores go out ahead of its weight loads; the decoder
+        // chain's fp64 epilogue stays on wave 0 (every wave would run its
+        // whole instruction stream for a few lanes)
+        constexpr int EPW = DEC ? 1 : kCW;
+        static_assert(16 % EPW == 0 && EPW <= kCW, "whole rows per epilogue wave");
+        const bool fin_b = compute && mrow / (16 / EPW) == wave && vb && mrow < mrows;
+        if (fin_b) {
             f32x4_t pv[kCW];
 #pragma unroll
             for (int i = 0; i < kCW; ++i) pv[i] = red_b[i][lane];
@@ -606,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
                     lds_barrier();
                     if (wave == kCW) row_inv(0, INV_B);
                     lds_barrier();
-                    if (wave == 0 && vb && mrow < mrows) {
+                    if (fin_b) {
                         // this lane's residual values, stored by this wave above (complete)
                         const int64_t mhb = static_cast<int64_t>(a.M) * H * 2;
                         const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(a.x_out, 0, static_cast<int>(mhb), kRsrcWord3);
@@ -634,15 +662,10 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
             }
             break;
         }
-        // this wave's stores complete, then the next layer's phase-A weights
-        // are requested (phase B's weights are dead by now: the two phases'
-        // fragments never hold registers at once); they stream in during the
-        // barrier and the next phase's activation staging
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_sched_barrier(0);
-        if (compute) load_wa(l + 1);
-        else clear_wa();
-        __builtin_amdgcn_sched_barrier(0);
+        // the next layer's phase-A weights are requested the same way
+        // (phase B's weights are dead by now: the two phases' fragments
+        // never hold registers at once)
+        prefetch_then_wait([&] { load_wa(l + 1); }, [&] { clear_wa(); }, std::integral_constant<int, 2 * SA>{});
         ok = group_barrier(b++);
         if (!ok) break;
     }
