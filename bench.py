@@ -449,6 +449,16 @@ def secondary(vla, torch, np, synthetic, dev, quantize, up_bits, time_graph, arg
         us = ms * 1000.0 / 128
         out[f"{name}_us"] = round(us, 3)
         out[f"{name}_GBps"] = round(alg_bytes_bf16w(m, n, k) / (us * 1e-6) / 1e9, 1)
+        # the pages' 10 decoder rows, same weights and rotation (their FP8
+        # vs BF16 comparison at that size)
+        A10 = up_bits(synthetic.activations(10, k, 900 + n))
+        ws10b = vla.vla_gemm_workspace_bytes(10, n, k, 0)
+        ws10 = torch.zeros(ws10b, dtype=torch.uint8, device=dev)
+
+        def one10(i, A10=A10, qs=qs, Y=Y, ws10=ws10, ws10b=ws10b, n=n, k=k, copies=copies):
+            vla.vla_gemm_bf16(A10, qs[i % copies], None, None, Y, ws10, ws10b, 10, n, k)
+        ms = time_graph(one10, 128)
+        out[f"m10_{name}_us"] = round(ms * 1000.0 / 128, 3)
         del qs
 
     log("secondary: matrix-instruction rates")
