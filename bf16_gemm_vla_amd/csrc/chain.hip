@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
     const int pa = grp * NPA + (compute ? wave / WPA : 0);
     const int kh = compute ? wave % WPA : 0;
     const bool fin_a = compute && (wave % WPA) == 0;     // finishes pair pa
-    // phase-B: tile grp, K steps wave*SB .. +SB-1; wave 0 finishes
+    // phase-B: tile grp, K steps wave*SB .. +SB-1 (the epilogue waves: fin_b below)
     const int nb = grp * 16 + 4 * q;                     // the lane's 4 output columns in phase B
 
     u32x2_t wa[SA][2];          // gate / up weight fragments (FP8)
