@@ -675,7 +675,10 @@ __global__ __launch_bounds__(kThreads) void mlp_chain_kernel(ChainArgs a) {
         const int64_t e = static_cast<int64_t>(m0 + mrow) * H + nb;
         store_b64(a.x_out, static_cast<int64_t>(a.M) * H, e, nan2);
         if (a.xlast) store_b64(a.xlast, static_cast<int64_t>(a.M) * H, e, nan2);
-        if (DEC) store_b64(a.h_out, static_cast<int64_t>(a.M) * H, e, nan2);
+        if (DEC) {
+            store_b64(a.h_out, static_cast<int64_t>(a.M) * H, e, nan2);
+            store_b64(a.g_out, static_cast<int64_t>(a.M) * H, e, nan2);
+        }
     }
     // the last workgroup out clears the counters and the abort word for the
     // next launch

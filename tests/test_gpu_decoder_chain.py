@@ -250,8 +250,8 @@ def test_decoder_chain_layer_count_limit(L):
 
 def test_fused_decoder_chain_barrier_wait_is_bounded():
     """With the wait bound forced down to one poll the single launch's
-    barriers give up: the launch completes, x_out and h_out read NaN, the
-    status query names the cause, and the same scratch then gives the
+    barriers give up: the launch completes, x_out, h_out and gate_out read
+    NaN, the status query names the cause, and the same scratch then gives the
     correct chain again."""
     dec = Decoder(3, 50, 1024, 4096, per_row=False, seed=9)
     assert dec.fused()
@@ -262,8 +262,8 @@ def test_fused_decoder_chain_barrier_wait_is_bounded():
         torch.cuda.synchronize()
     finally:
         vla.vla_set_wait_limit(0)
-    x_out, h_out, _ = (host(o).view(np.uint16) for o in dec.d_out)
-    assert np.isnan(bf16_f64(x_out)).any() and np.isnan(bf16_f64(h_out)).any()
+    x_out, h_out, g_out = (host(o).view(np.uint16) for o in dec.d_out)
+    assert all(np.isnan(bf16_f64(o)).any() for o in (x_out, h_out, g_out))
     with pytest.raises(RuntimeError, match="fused chain phase barrier"):
         vla.vla_workspace_status(dec.scratch)
     outs, st = dec.staged()
