@@ -449,7 +449,8 @@ int vla_mlp_chain_destroy(vla_mlp_chain *chain);
  * 16-column tile's partial sum of squares of the new residual, and the next
  * layer normalizes its staged input rows from those partials (fp32 after the
  * fp64 sum; 1/rms in fp64), so the layers meet only at the chain's own
- * phase barriers.  Otherwise three kernels per layer are recorded once as a
+ * phase barriers (bounded waits: a give-up leaves NaN in x_out, h_out and
+ * gate_out and sets the scratch buffer's status word).  Otherwise three kernels per layer are recorded once as a
  * HIP graph like the gated-MLP chain's.  The residual is bit-exact on both
  * paths; h agrees with the fp64 boundary within one bf16 ulp.
  *   wgu, sgu, wd, sd  as for the gated-MLP chain.
