@@ -117,7 +117,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the GEMMs shard by output columns with no exchange; see the design notes)",
+              "(it scales by replicas, one request per GPU with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
 
