@@ -134,13 +134,15 @@ def plan(M, N, K, wfmt=vla.VLA_WFMT_E4M3_OCP, fp8_act=False):
     return info
 
 
-@pytest.mark.parametrize("K", [64, 256])
+@pytest.mark.parametrize("K", [64, 96, 160, 256, 320, 352, 448])
 @pytest.mark.parametrize("kind", ["w8a16", "fp8xfp8", "mxfp4"])
 def test_lane_map_probe_256_tiles(kind, K):
     """One-hot weights at M = 768, N = 16384 (the encoder up-projection's
     row and column counts), which the wide kernel runs on 256-column tiles:
     Y must be A's permuted columns bit for bit (FP8 x FP8: the decoded codes;
-    MXFP4: each weight a single 4.0 code in a block of scale 2^-2)."""
+    MXFP4: each weight a single 4.0 code in a block of scale 2^-2).  The K
+    values give 1 to 7 pipeline stages of 64, two with a ragged last stage,
+    so every remainder of the stage ring (and of its pairs) runs."""
     M, N = 768, 16384
     wfmt = vla.VLA_WFMT_MXFP4 if kind == "mxfp4" else vla.VLA_WFMT_E4M3_OCP
     info = plan(M, N, K, wfmt, kind == "fp8xfp8")
