@@ -528,27 +528,47 @@ void wide_gemm_kernel(KArgs a) {
         const Coherent part(a.part, a.part_bytes);
         auto off = [&](int sp, int f) { return static_cast<uint32_t>((sp * sstride + slot * per + f * C::THREADS + tid) * 16); };
         // have all splits of the tile started?  (read while the stores drain)
+        const uint32_t ks = static_cast<uint32_t>(a.ksplit);
+        const int own = split < C::MSUB ? split : -1;
         uint32_t started = 0;
         if (tid == 0) started = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        auto store_slice = [&](int ms) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ns = 0; ns < C::NSUB; ++ns)
-#pragma unroll
-            for (int ms = 0; ms < C::MSUB; ++ms)
+            for (int ns = 0; ns < C::NSUB; ++ns)
 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) {
                     const Acc& v = acc[ns][ms];
                     part.store(off(split, (ns * C::MSUB + ms) * 4 + rq), f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]});
                 }
+        };
+        // the slices other workgroups may finish; an owner keeps its own
+        // slice's partials in registers unless it hands the slice over
+#pragma unroll
+        for (int ms = 0; ms < C::MSUB; ++ms)
+            if (ms != own) store_slice(ms);
         // every wave's partial stores have completed (stores count in vmcnt),
         // then the barrier orders them before the arrival; the flag lives in
         // stage buffer 0, which every wave has finished reading
         int* const flags = reinterpret_cast<int*>(lds0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        // an owner that finds a split not yet started hands its slice over:
+        // then its partials of that slice are stored too, before the arrival
+        bool keep = false;
+        if (own >= 0) {
+            if (tid == 0) flags[0] = started == ks ? 1 : 0;
+            __syncthreads();
+            keep = flags[0] != 0;
+            if (!keep) {
+#pragma unroll
+                for (int ms = 0; ms < C::MSUB; ++ms)
+                    if (ms == own) store_slice(ms);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();
+        }
         if (tid == 0) {
-            const uint32_t ks = static_cast<uint32_t>(a.ksplit);
-            const int own = split < C::MSUB ? split : -1;
-            const bool wait_own = own >= 0 && started == ks;
+            const bool wait_own = keep;
             const uint32_t add = 1u + ((own >= 0 && !wait_own) ? (1u << (16 + own)) : 0u);
             const uint32_t prev = __hip_atomic_fetch_add(ctr + 1, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             uint32_t mine = 0;
@@ -599,7 +619,15 @@ void wide_gemm_kernel(KArgs a) {
                 for (int ns = 0; ns < C::NSUB; ++ns) acc[ns][ms] = Acc{} + __builtin_nanf("");
                 continue;
             }
-            // two splits' loads in flight at a time, summed in split order
+            // two splits' loads in flight at a time, summed in split order;
+            // this workgroup's own split of a slice it kept comes from its
+            // registers (the values it would have stored)
+            const int reg_sp = (keep && ms == own) ? split : -1;
+            auto part_or_reg = [&](int sp, int ns, int rq) __attribute__((always_inline)) {
+                const Acc& v = acc[ns][ms];
+                return sp == reg_sp ? f32x4_t{v[4 * rq], v[4 * rq + 1], v[4 * rq + 2], v[4 * rq + 3]}
+                                    : part.load(off(sp, (ns * C::MSUB + ms) * 4 + rq));
+            };
             f32x4_t sum[C::NSUB][4];
             for (int sp = 0; sp < a.ksplit; sp += 2) {
                 f32x4_t p0[C::NSUB][4], p1[C::NSUB][4];
@@ -608,9 +636,8 @@ void wide_gemm_kernel(KArgs a) {
                 for (int ns = 0; ns < C::NSUB; ++ns)
 #pragma unroll
                     for (int rq = 0; rq < 4; ++rq) {
-                        const int f = (ns * C::MSUB + ms) * 4 + rq;
-                        p0[ns][rq] = part.load(off(sp, f));
-                        p1[ns][rq] = two ? part.load(off(sp + 1, f)) : f32x4_t{};
+                        p0[ns][rq] = part_or_reg(sp, ns, rq);
+                        p1[ns][rq] = two ? part_or_reg(sp + 1, ns, rq) : f32x4_t{};
                     }
 #pragma unroll
                 for (int ns = 0; ns < C::NSUB; ++ns)
