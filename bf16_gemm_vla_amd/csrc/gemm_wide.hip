@@ -509,15 +509,18 @@ void wide_gemm_kernel(KArgs a) {
     // ---- epilogue.  acc[ns][ms] register r: row (output channel) 8*(r/4) + 4*(lane/32) + r%4
     //      of the 32-column sub-tile, activation row lane%32 of the 32-row sub-tile.
     //      The tile is finished in MSUB slices (slice ms = accumulators acc[*][ms]).
-    //      With K split over workgroups, every workgroup stores its partials;
-    //      the workgroup of split s < MSUB owns slice s and finishes it itself,
-    //      waiting for the other splits' partials, but only if every split of
-    //      the tile had started when it decided (then all of them are running
-    //      and arrive without waiting on anything, so the wait ends); otherwise
-    //      it hands the slice to whichever workgroup arrives last, which also
-    //      takes slices without an owner.  The hand-over travels in the same
-    //      atomic as the arrival, so no fence is needed.  Partials are summed
-    //      in split order, whoever finishes (bitwise repeatable).
+    //      With K split over workgroups, the workgroup of split s < MSUB owns
+    //      slice s and finishes it itself, waiting for the other splits'
+    //      partials, but only if every split of the tile had started when it
+    //      decided (then all of them are running and arrive without waiting
+    //      on anything, so the wait ends); otherwise it hands the slice to
+    //      whichever workgroup arrives last, which also takes slices without
+    //      an owner.  Every workgroup stores its partials of the slices it
+    //      does not own, and an owner that hands its slice over stores that
+    //      one too; a keeping owner adds its own partials from registers.  The
+    //      hand-over travels in the same atomic as the arrival, so no fence is
+    //      needed.  Partials are summed in split order, whoever finishes
+    //      (bitwise repeatable).
     constexpr int NACC = C::NSUB * C::MSUB * 4;
     uint32_t todo = (1u << C::MSUB) - 1;     // slices this workgroup outputs
     if (a.ksplit > 1) {
