@@ -614,27 +614,38 @@ constexpr int kActBlocks = 512;
 // Every thread keeps kActUnroll 16-byte loads in flight at a time.
 constexpr int kActUnroll = 4;
 
+// Chunks c0 .. c0 + n - 1 of an array (bytes_per_chunk each) as a buffer
+// resource: loads past the window read zero, so the absmax pass needs no
+// per-lane range branch (a branch around a load makes the compiler wait for
+// every load in flight before the code after it; branch-free, the pass's
+// loads stay in flight together: 768 x 16384 dynamic quantization 12.7 ->
+// 12.1 us on MI355X, same GPU call).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_window(const void* base, int64_t c0, int64_t n, int bytes_per_chunk) {
+    const int64_t m = n < 0 ? 0 : n;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(base)) + c0 * bytes_per_chunk, 0,
+        static_cast<int>(m * bytes_per_chunk), 0x00020000);
+}
+
 __global__ __launch_bounds__(kThreads) void act_absmax_kernel(const uint16_t* __restrict__ A,
                                                               float* __restrict__ partial,
                                                               int64_t chunks) {
     __shared__ float red[kThreads / kWave];
     float m = 0.0f;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * kActUnroll;
-    for (int64_t base = blockIdx.x * static_cast<int64_t>(kThreads) * kActUnroll + threadIdx.x; base < chunks;
-         base += stride) {
-        uint4 v[kActUnroll];
+    constexpr int64_t kSpan = static_cast<int64_t>(kThreads) * kActUnroll;   // chunks per block and step
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kSpan;
+    for (int64_t w0 = blockIdx.x * kSpan; w0 < chunks; w0 += stride) {
+        const __amdgpu_buffer_rsrc_t r = chunk_window(A, w0, chunks - w0 < kSpan ? chunks - w0 : kSpan, 16);
+        u32x4_t v[kActUnroll];
+#pragma unroll
+        for (int u = 0; u < kActUnroll; ++u)
+            v[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (u * kThreads + threadIdx.x) * 16, 0, 0));
 #pragma unroll
         for (int u = 0; u < kActUnroll; ++u) {
-            const int64_t i = base + u * kThreads;
-            v[u] = i < chunks ? *reinterpret_cast<const uint4*>(A + i * 8) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < kActUnroll; ++u) {
-            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(w[j] & 0xFFFFu))));
-                m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(w[j] >> 16))));
+                m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(v[u][j] & 0xFFFFu))));
+                m = fmaxf(m, fabsf(bf16_to_f32(static_cast<uint16_t>(v[u][j] >> 16))));
             }
         }
     }
